@@ -1,0 +1,150 @@
+/*
+ * qgemv.h -- C ABI of the MI355X (gfx950) quantized-weight GEMV library.
+ *
+ * y = W.x where W stays packed in device memory and is decoded in registers
+ * while it streams.  Every pointer argument is a DEVICE pointer owned by the
+ * caller; the library keeps no reference to any of them after the call
+ * returns and allocates no device memory.  Work is enqueued asynchronously on
+ * `stream` (a hipStream_t; NULL means the default stream); a return value of
+ * QGEMV_OK means the work was validated and launched, not that it finished.
+ *
+ * All arguments are validated on the host before any pointer is used; a
+ * refused call returns a nonzero qgemv_status, launches nothing and touches
+ * no memory.  qgemv_strerror() names the condition.  There is no silent
+ * fallback to another implementation.
+ *
+ * Activations x are f32 [S][I] row-major (S vectors of length I), outputs y
+ * are f32 [S][O] row-major and are overwritten.  S ranges over 1..8.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QGEMV_OK = 0,
+    QGEMV_E_NULL = 1,      /* a required pointer is NULL                      */
+    QGEMV_E_DIMS = 2,      /* S, I, O, E, T or K out of range                 */
+    QGEMV_E_GS = 3,        /* group size is not an even number >= 2           */
+    QGEMV_E_ALIGN = 4,     /* an f32 / int32 pointer is not 4-byte aligned    */
+    QGEMV_E_K256 = 5,      /* I is not a multiple of 256 (MQ4-v2, FWHT-256)   */
+    QGEMV_E_IDS = 6,       /* expert strides too small for one expert         */
+    QGEMV_E_WORKSPACE = 7, /* workspace NULL or smaller than required         */
+    QGEMV_E_HIP = 8        /* the HIP runtime reported an error at launch     */
+} qgemv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qgemv_strerror(int status);
+
+/* Library version, e.g. "0.1.0" (static string). */
+const char *qgemv_version(void);
+
+/* Largest S (vectors per call) the GEMV entry points accept. */
+#define QGEMV_MAX_S 8
+
+/*
+ * Grouped int4 ("fmt=4"): colibri PR #457 "metal: grouped-int4 (fmt=4) GEMV
+ * support", sections 1 and 3.
+ *   w       u8  [O][(I+1)/2]  two unsigned nibbles per byte; column 2k is the
+ *                             low nibble of byte k, column 2k+1 the high one;
+ *                             for odd I the last high nibble is ignored
+ *   scales  f32 [O][ceil(I/gs)]  weight (o,i) = (nibble - 8) * scales[o][i/gs]
+ *   x       f32 [S][I],  y f32 [S][O]
+ *   gs      even, >= 2; any I >= 1 (a last partial group is allowed)
+ * Rows whose bytes are 16-byte aligned (I % 32 == 0, w 16-byte aligned) with
+ * gs % 32 == 0 take the streaming kernel; every other valid shape takes a
+ * slower general kernel with the same result definition.
+ */
+int qgemv_i4g(const void *w, const float *scales, const float *x, float *y,
+              int S, int I, int O, int gs, void *stream);
+
+/*
+ * fp8-e4m3 with 128x128 block scales ("fmt=7"): colibri PR #528 "fmt=7:
+ * fp8-e4m3-b128 passthrough weight format", section "Design".
+ *   w          u8  [O][I]    OCP E4M3-FN codes (bias 7, subnormals, +-0;
+ *                            0x7F / 0xFF are NaN and poison their row)
+ *   scale_inv  f32 [ceil(O/128)][ceil(I/128)] row-major block order;
+ *              weight (o,i) = e4m3(w[o][i]) * scale_inv[o/128][i/128]
+ *              (a multiply, whatever the name says)
+ *   x          f32 [S][I],  y f32 [S][O]
+ */
+int qgemv_fp8b128(const void *w, const float *scale_inv, const float *x,
+                  float *y, int S, int I, int O, void *stream);
+
+/*
+ * MQ4-v2: hipfire "MQ4 V2" page, sections 2 and 4.
+ *   w      u8 [O][I/256][136]; per 256-weight group, little-endian:
+ *          bytes 0..3  dword: fp16 scale (low 16 bits), fp16 zero (high 16)
+ *                      of weights 0..127,
+ *          bytes 4..7  the same pair for weights 128..255,
+ *          bytes 8..135  128 payload bytes, weight j = nibble j (byte j/2,
+ *                      low nibble for even j);  weight = q * scale + zero
+ *   x_rot  f32 [S][I] activations already rotated into the weights' space
+ *          (qgemv_fwht256),  y f32 [S][O];  I % 256 == 0
+ */
+int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I,
+                int O, void *stream);
+
+/*
+ * FWHT-256 pre-rotation of activations for MQ4 weights (hipfire "MQ4 V2",
+ * section 1: the weights are FWHT-256 rotated with per-element signs).
+ * Per 256-element block b of each vector:
+ *     x_rot[b] = (1/16) * H256 * (signs[b] (.) x[b])
+ * with H256 the Sylvester Hadamard matrix H[i][j] = (-1)^popcount(i&j).
+ *   x f32 [S][I], signs int8 [I] (each +1 or -1), x_rot f32 [S][I];
+ *   I % 256 == 0.  x_rot may not alias x.
+ */
+int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S,
+                  int I, void *stream);
+
+/*
+ * Routed experts over grouped-int4 matrices: regolith audit "phase 0 +
+ * phase 2 m5 air validation", section 2.2 (the gates are the selection
+ * probabilities renormalised over the selected experts) and colibri PR #457,
+ * section 4 (routed experts are grouped-int4 matrices).
+ *   y[t][o] = sum_k gates[t][k] * (W_{ids[t][k]} . x[t])[o]
+ * summed over k in ascending order (deterministic; no atomics).
+ *   w        expert e's packed weights (layout as qgemv_i4g, [O x I]) start
+ *            at byte e*w_stride;  scales  expert e's f32 scales start at
+ *            element e*s_stride;  E experts
+ *   ids      int32 [T][K] device array; an id outside [0, E) makes row t of
+ *            y NaN (it is never dereferenced) and sets a flag in the
+ *            workspace (qgemv_moe_topk_error)
+ *   gates    f32 [T][K],  x f32 [T][I],  y f32 [T][O] (overwritten)
+ *   T in 1..8, K in 1..64, gs even >= 2
+ *   workspace  device scratch of at least qgemv_moe_topk_workspace(T, K, O)
+ *              bytes, 256-byte aligned; its contents are overwritten.
+ * Each distinct selected expert is streamed from memory once per call, for
+ * all tokens that selected it.  The routing never leaves the device.
+ */
+size_t qgemv_moe_topk_workspace(int T, int K, int O);
+int qgemv_moe_topk(const void *w, const float *scales, long long w_stride,
+                   long long s_stride, int E, const int32_t *ids,
+                   const float *gates, int T, int K, const float *x, float *y,
+                   int I, int O, int gs, void *workspace, size_t ws_bytes,
+                   void *stream);
+/* Copies the error flag of the last qgemv_moe_topk that used `workspace`
+ * into *flag (host int; 0 = all ids in range), synchronising `stream`. */
+int qgemv_moe_topk_error(const void *workspace, int *flag, void *stream);
+
+/*
+ * Decode-only entry points: write the decoded f32 weights W[O][I] using the
+ * same device decode code as the GEMVs (the decoded values must match the
+ * format definitions bit for bit).  Arguments as the GEMV of the same format.
+ */
+int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I,
+                      int O, int gs, void *stream);
+int qgemv_dequant_fp8b128(const void *w, const float *scale_inv, float *W,
+                          int I, int O, void *stream);
+int qgemv_dequant_mq4v2(const void *w, float *W, int I, int O, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

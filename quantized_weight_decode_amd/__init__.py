@@ -1,0 +1,262 @@
+"""MI355X (gfx950) quantized-weight GEMV: Python binding of libqgemv.so.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libqgemv.so``; there is no CPU or PyTorch fallback: if the
+library is missing or a call is refused, an exception is raised.
+
+Two layers:
+* ``qgemv_*`` -- the C ABI under the same names, taking raw device pointers
+  (ints), sizes and a stream handle, returning the status code;
+* ``i4g``, ``fp8b128``, ``mq4v2``, ``fwht256``, ``moe_topk``, ``dequant_*`` --
+  take torch tensors on the current CUDA (HIP) device, allocate the output
+  with ``torch.empty``, launch on ``torch.cuda.current_stream()`` and raise
+  ``QgemvError`` on a refusal.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemv.so")
+
+QGEMV_MAX_S = 8
+
+# every entry point declared in include/qgemv.h
+_SIGS = {
+    "qgemv_strerror": (C.c_char_p, [C.c_int]),
+    "qgemv_version": (C.c_char_p, []),
+    "qgemv_i4g": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                            C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_fp8b128": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_fwht256": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                                C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_moe_topk_workspace": (C.c_size_t, [C.c_int, C.c_int, C.c_int]),
+    "qgemv_moe_topk": (C.c_int, [C.c_void_p, C.c_void_p, C.c_longlong, C.c_longlong,
+                                 C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                 C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                 C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qgemv_moe_topk_error": (C.c_int, [C.c_void_p, C.POINTER(C.c_int), C.c_void_p]),
+    "qgemv_dequant_i4g": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_dequant_fp8b128": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_dequant_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p,
+                                      C.c_int, C.c_int, C.c_void_p]),
+}
+
+ENTRY_POINTS = tuple(_SIGS)
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """The loaded libqgemv.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built: run quantized_weight_decode_amd.build.build()")
+        L = C.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            if not hasattr(L, name):
+                continue  # reported by exported_symbols(); calling it raises
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols(path: str = LIB_PATH):
+    """Entry points of include/qgemv.h that the built library exports."""
+    L = lib(path)
+    return [n for n in ENTRY_POINTS if hasattr(L, n)]
+
+
+def strerror(status: int) -> str:
+    return lib().qgemv_strerror(status).decode()
+
+
+def version() -> str:
+    return lib().qgemv_version().decode()
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise QgemvError(name, st, strerror(st))
+    return st
+
+
+# -- raw C ABI, same names -------------------------------------------------
+def qgemv_i4g(w, scales, x, y, S, I, O, gs, stream):
+    return lib().qgemv_i4g(w, scales, x, y, S, I, O, gs, stream)
+
+
+def qgemv_fp8b128(w, scale_inv, x, y, S, I, O, stream):
+    return lib().qgemv_fp8b128(w, scale_inv, x, y, S, I, O, stream)
+
+
+def qgemv_mq4v2(w, x_rot, y, S, I, O, stream):
+    return lib().qgemv_mq4v2(w, x_rot, y, S, I, O, stream)
+
+
+def qgemv_fwht256(x, signs, x_rot, S, I, stream):
+    return lib().qgemv_fwht256(x, signs, x_rot, S, I, stream)
+
+
+def qgemv_moe_topk_workspace(T, K, O):
+    return lib().qgemv_moe_topk_workspace(T, K, O)
+
+
+def qgemv_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs,
+                   workspace, ws_bytes, stream):
+    return lib().qgemv_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
+                                I, O, gs, workspace, ws_bytes, stream)
+
+
+def qgemv_dequant_i4g(w, scales, W, I, O, gs, stream):
+    return lib().qgemv_dequant_i4g(w, scales, W, I, O, gs, stream)
+
+
+def qgemv_dequant_fp8b128(w, scale_inv, W, I, O, stream):
+    return lib().qgemv_dequant_fp8b128(w, scale_inv, W, I, O, stream)
+
+
+def qgemv_dequant_mq4v2(w, W, I, O, stream):
+    return lib().qgemv_dequant_mq4v2(w, W, I, O, stream)
+
+
+# -- torch-tensor layer ----------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _vecs(x, I, name="x"):
+    if x.dim() == 1:
+        return 1
+    if x.dim() == 2 and x.shape[1] == I:
+        return x.shape[0]
+    raise ValueError(f"{name} must be [I] or [S, I]")
+
+
+def i4g(w, scales, x, gs, out=None):
+    """y[S][O] = grouped-int4 W[O][I] . x[S][I]; w u8 [O][(I+1)//2], scales f32 [O][ng]."""
+    torch = _torch()
+    O = w.shape[0]
+    I = x.shape[-1]
+    S = _vecs(x, I)
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _call("qgemv_i4g", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
+          _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, gs, _stream())
+    return y
+
+
+def fp8b128(w, scale_inv, x, out=None):
+    torch = _torch()
+    O, I = w.shape[0], x.shape[-1]
+    S = _vecs(x, I)
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _call("qgemv_fp8b128", _dev(w, "w", torch.uint8), _dev(scale_inv, "scale_inv", torch.float32),
+          _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, _stream())
+    return y
+
+
+def mq4v2(w, x_rot, out=None):
+    torch = _torch()
+    O, I = w.shape[0], x_rot.shape[-1]
+    S = _vecs(x_rot, I, "x_rot")
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x_rot.device)
+    _call("qgemv_mq4v2", _dev(w, "w", torch.uint8), _dev(x_rot, "x_rot", torch.float32),
+          _dev(y, "y", torch.float32), S, I, O, _stream())
+    return y
+
+
+def fwht256(x, signs, out=None):
+    torch = _torch()
+    I = x.shape[-1]
+    S = _vecs(x, I)
+    y = out if out is not None else torch.empty_like(x)
+    _call("qgemv_fwht256", _dev(x, "x", torch.float32), _dev(signs, "signs", torch.int8),
+          _dev(y, "x_rot", torch.float32), S, I, _stream())
+    return y
+
+
+def moe_topk_workspace(T, K, O, device):
+    torch = _torch()
+    n = qgemv_moe_topk_workspace(T, K, O)
+    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def moe_topk(w, scales, ids, gates, x, gs, workspace=None, out=None):
+    """w u8 [E][O][rb], scales f32 [E][O][ng], ids int32 [T][K], gates f32 [T][K], x f32 [T][I]."""
+    torch = _torch()
+    E, O = w.shape[0], w.shape[1]
+    T, K = ids.shape
+    I = x.shape[-1]
+    ws = workspace if workspace is not None else moe_topk_workspace(T, K, O, x.device)
+    y = out if out is not None else torch.empty((T, O), dtype=torch.float32, device=x.device)
+    _call("qgemv_moe_topk", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
+          w[0].numel(), scales[0].numel(), E, _dev(ids, "ids", torch.int32),
+          _dev(gates, "gates", torch.float32), T, K, _dev(x, "x", torch.float32),
+          _dev(y, "y", torch.float32), I, O, gs, _dev(ws, "workspace", torch.uint8),
+          ws.numel(), _stream())
+    return y
+
+
+def moe_topk_error(workspace):
+    flag = C.c_int(0)
+    _call("qgemv_moe_topk_error", _dev(workspace, "workspace"), C.byref(flag), _stream())
+    return flag.value
+
+
+def dequant_i4g(w, scales, I, gs):
+    torch = _torch()
+    O = w.shape[0]
+    W = torch.empty((O, I), dtype=torch.float32, device=w.device)
+    _call("qgemv_dequant_i4g", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
+          _dev(W, "W"), I, O, gs, _stream())
+    return W
+
+
+def dequant_fp8b128(w, scale_inv):
+    torch = _torch()
+    O, I = w.shape
+    W = torch.empty((O, I), dtype=torch.float32, device=w.device)
+    _call("qgemv_dequant_fp8b128", _dev(w, "w", torch.uint8),
+          _dev(scale_inv, "scale_inv", torch.float32), _dev(W, "W"), I, O, _stream())
+    return W
+
+
+def dequant_mq4v2(w, I):
+    torch = _torch()
+    O = w.shape[0]
+    W = torch.empty((O, I), dtype=torch.float32, device=w.device)
+    _call("qgemv_dequant_mq4v2", _dev(w, "w", torch.uint8), _dev(W, "W"), I, O, _stream())
+    return W

@@ -1,0 +1,85 @@
+// abi.hip -- the extern "C" entry points: argument validation, then launch.
+//
+// Validation never touches a pointer's target: it looks at pointer values,
+// dimensions and sizes only, so a refused call is safe with any pointers.
+#include <mutex>
+#include <unordered_map>
+
+#include "qg_launch.h"
+
+namespace qg {
+
+hipError_t set_max_lds(const void *kernel, size_t bytes)
+{
+    static std::mutex mu;
+    static std::unordered_map<const void *, size_t> done;
+    if (bytes <= 64 * 1024) return hipSuccess;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = done.find(kernel);
+    if (it != done.end() && it->second >= bytes) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)bytes);
+    if (e == hipSuccess) done[kernel] = bytes;
+    return e;
+}
+
+}  // namespace qg
+
+namespace {
+
+constexpr int MAX_DIM = 1 << 24;
+
+bool mis4(const void *p) { return ((uintptr_t)p & 3) != 0; }
+
+int launched(hipError_t e) { return e == hipSuccess ? QGEMV_OK : QGEMV_E_HIP; }
+
+int check_gemv_dims(int S, int I, int O)
+{
+    if (S < 1 || S > QGEMV_MAX_S || I < 1 || O < 1 || I > MAX_DIM || O > MAX_DIM)
+        return QGEMV_E_DIMS;
+    return QGEMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qgemv_strerror(int status)
+{
+    switch (status) {
+    case QGEMV_OK: return "ok";
+    case QGEMV_E_NULL: return "a required pointer is NULL";
+    case QGEMV_E_DIMS: return "a dimension is out of range";
+    case QGEMV_E_GS: return "group size must be an even number >= 2";
+    case QGEMV_E_ALIGN: return "an f32/int32 pointer is not 4-byte aligned";
+    case QGEMV_E_K256: return "I must be a multiple of 256 for this format";
+    case QGEMV_E_IDS: return "expert strides are smaller than one expert";
+    case QGEMV_E_WORKSPACE: return "workspace is NULL or too small";
+    case QGEMV_E_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+    }
+}
+
+const char *qgemv_version(void) { return "0.1.0"; }
+
+int qgemv_i4g(const void *w, const float *scales, const float *x, float *y, int S, int I,
+              int O, int gs, void *stream)
+{
+    if (!w || !scales || !x || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (mis4(scales) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_i4g_gemv(w, scales, x, y, S, I, O, gs, (hipStream_t)stream));
+}
+
+int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I, int O, int gs,
+                      void *stream)
+{
+    if (!w || !scales || !W) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (mis4(scales) || mis4(W)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_i4g_dequant(w, scales, W, I, O, gs, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+// i4g.hip -- grouped-int4 ("fmt=4") GEMV and decode kernels for gfx950.
+//
+// Format (colibri PR #457 "metal: grouped-int4 (fmt=4) GEMV support",
+// sections 1 and 3): row-major u8[O][(I+1)/2], column 2k in the low nibble of
+// byte k, column 2k+1 in the high nibble; f32 scales [O][ceil(I/gs)];
+// weight = (q - 8) * scale[row][col/gs].  The scale is applied per group,
+// before the sum across groups.
+//
+// Streaming kernel (rows of 16-byte lane chunks, gs % 32 == 0):
+//   * each workgroup stages x (pre-scaled, permuted, with per-chunk sums) in
+//     LDS once;
+//   * a wave covers 64/LPR row groups of R rows; LPR lanes sweep a row in
+//     16-byte dwordx4 loads (fully coalesced), the R rows of a lane group share
+//     the activations they read from LDS, and the next chunk's loads are in
+//     flight while the current one is decoded;
+//   * per lane chunk c (32 columns, one group): P = sum q*x, then
+//     acc += s_g * (P - 8 * sum x), which is sum (q - 8) s_g x reassociated;
+//   * the row sum is a DPP reduction over the LPR lanes.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+// Tile shape of the streaming kernel for S <= 2: rows per lane group, chunk
+// sweeps in flight, waves per workgroup.
+#ifndef QG_I4G_R
+#define QG_I4G_R 4
+#endif
+#ifndef QG_I4G_PF
+#define QG_I4G_PF 1
+#endif
+#ifndef QG_I4G_WPB
+#define QG_I4G_WPB 4
+#endif
+
+// Largest S the streaming kernels are instantiated for; S up to QGEMV_MAX_S
+// goes through the general kernel.
+constexpr int I4G_FAST_MAX_S = 4;
+
+template <int S, int LPR, int R, int PF>
+__global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
+    const uint8_t *__restrict__ w, const float *__restrict__ scales,
+    const float *__restrict__ x, float *__restrict__ y, int I, int O, int ng,
+    Div20 div_cpg, int ntiles)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int NU = I / 32;                       // lane chunks per row
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NU]
+    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * NU);  // [S][NU]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane / LPR;
+    const int sl = lane % LPR;
+    const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+    const int row0 = tile * ROWS_PER_WAVE + sub * R;
+    const size_t rb = (size_t)I / 2;
+    const int nit = (NU + LPR - 1) / LPR;
+
+    const uint8_t *wr[R];
+    const float *sr[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int row = min(row0 + r, O - 1);   // rows past O re-read row O-1, never stored
+        wr[r] = w + (size_t)row * rb;
+        sr[r] = scales + (size_t)row * ng;
+    }
+
+    // 1. activations are requested first (coalesced float4s, L2-resident), so
+    //    waiting for them never waits for the weight stream issued after them
+    XStage<S> xst;
+    xst.load(x, I, NU);
+
+    // 2. the first PF chunk-sweeps of weights and scales go out
+    u32x4 wb[PF][R];
+    float sb[PF][R];
+#pragma unroll
+    for (int j = 0; j < PF; j++) {
+        if (j < nit) {
+            const int u = min(j * LPR + sl, NU - 1);
+            const uint32_t g = div_cpg((uint32_t)u);
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16);
+                sb[j][r] = sr[r][g];
+            }
+        }
+    }
+
+    // 3. activations into LDS (pre-scaled, permuted, chunk sums)
+    xst.store(x, I, NU, xl, xs);
+    __syncthreads();
+    if (tile >= ntiles) return;
+
+    float acc[S][R];
+#pragma unroll
+    for (int t = 0; t < S; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+
+    // 4. sweep: consume ring slot j, refill it with the sweep PF ahead
+    for (int c0 = 0; c0 < nit; c0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            const int c = c0 + j;
+            if (c < nit) {
+                const int u = c * LPR + sl;
+                const bool valid = u < NU;
+                const int uu = valid ? u : 0;
+#pragma unroll
+                for (int t = 0; t < S; t++) {
+                    const f32x4 *xt = xl + (size_t)t * 8 * NU;
+                    const float xsum = xs[(size_t)t * NU + uu];
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                        const float tv = __builtin_fmaf(-8.0f, xsum, p);
+                        acc[t][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[t][r]);
+                    }
+                }
+                if (c + PF < nit) {
+                    const int un = min(u + PF * LPR, NU - 1);
+                    const uint32_t g = div_cpg((uint32_t)un);
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)un * 16);
+                        sb[j][r] = sr[r][g];
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < S; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const float v = sub_reduce<LPR>(acc[t][r]);
+            if (sl == LPR - 1 && row0 + r < O) y[(size_t)t * O + row0 + r] = v;
+        }
+}
+
+// General kernel: any I >= 1, any even gs, S <= QGEMV_MAX_S, any alignment of
+// w.  One wave per row; each lane takes bytes lane, lane+64, ...; each weight
+// is decoded to f32 as (q - 8) * s (one rounding) and multiplied in f32.
+__global__ __launch_bounds__(256) void i4g_gemv_general(
+    const uint8_t *__restrict__ w, const float *__restrict__ scales,
+    const float *__restrict__ x, float *__restrict__ y, int S, int I, int O, int gs)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (row >= O) return;
+    const int rb = (I + 1) / 2;
+    const int ng = (I + gs - 1) / gs;
+    const uint8_t *wr = w + (size_t)row * rb;
+    const float *sr = scales + (size_t)row * ng;
+    float acc[QGEMV_MAX_S];
+#pragma unroll
+    for (int t = 0; t < QGEMV_MAX_S; t++) acc[t] = 0.0f;
+    for (int k = lane; k < rb; k += WAVE) {
+        float e[4], o[4];
+        nib8((uint32_t)wr[k], e, o);
+        const int c0 = 2 * k, c1 = 2 * k + 1;
+        const float w0 = (e[0] * NIB_XSCALE - 8.0f) * sr[c0 / gs];
+        const float w1 = c1 < I ? (o[0] * NIB_XSCALE - 8.0f) * sr[c1 / gs] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < QGEMV_MAX_S; t++) {
+            if (t < S) {
+                const float *xt = x + (size_t)t * I;
+                acc[t] = __builtin_fmaf(w0, xt[c0], acc[t]);
+                if (c1 < I) acc[t] = __builtin_fmaf(w1, xt[c1], acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < QGEMV_MAX_S; t++) {
+        if (t < S) {
+            const float v = sub_reduce<64>(acc[t]);
+            if (lane == 63) y[(size_t)t * O + row] = v;
+        }
+    }
+}
+
+// Decode-only: W[o][i] = (q - 8) * s as f32, with the GEMVs' nibble decoder.
+__global__ __launch_bounds__(256) void i4g_dequant(
+    const uint8_t *__restrict__ w, const float *__restrict__ scales, float *__restrict__ W,
+    int I, int O, int gs)
+{
+    const int rb = (I + 1) / 2;
+    const int ng = (I + gs - 1) / gs;
+    const size_t n = (size_t)O * rb;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const size_t o = idx / rb;
+        const int k = (int)(idx - o * rb);
+        float e[4], od[4];
+        nib8((uint32_t)w[idx], e, od);
+        const int c0 = 2 * k, c1 = 2 * k + 1;
+        W[o * I + c0] = (e[0] * NIB_XSCALE - 8.0f) * scales[o * ng + c0 / gs];
+        if (c1 < I) W[o * I + c1] = (od[0] * NIB_XSCALE - 8.0f) * scales[o * ng + c1 / gs];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+// lanes per row: the widest of 64/32/16/8/4 whose last sweep is not mostly idle
+int pick_lpr(int nchunks)
+{
+    const int opts[] = {64, 32, 16, 8, 4};
+    int best = 4;
+    double best_eff = -1.0;
+    for (int lpr : opts) {
+        const int it = (nchunks + lpr - 1) / lpr;
+        const double eff = (double)nchunks / ((double)it * lpr);
+        if (eff > best_eff + 1e-9) { best_eff = eff; best = lpr; }
+    }
+    return best;
+}
+
+template <int S, int LPR, int R, int PF>
+hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, float *y,
+                           int I, int O, int gs, hipStream_t st)
+{
+    const int NU = I / 32;
+    const int ng = (I + gs - 1) / gs;
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    const int waves_per_block = QG_I4G_WPB;
+    const int blocks = (ntiles + waves_per_block - 1) / waves_per_block;
+    const size_t lds = i4g_stream_lds_bytes(S, I);
+    auto kern = i4g_gemv_stream<S, LPR, R, PF>;
+    hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves_per_block), lds, st, w, s, x, y,
+                       I, O, ng, Div20::make((uint32_t)(gs / 32)), ntiles);
+    return hipGetLastError();
+}
+
+template <int S>
+hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, float *y,
+                           int I, int O, int gs, hipStream_t st)
+{
+    // R rows share each activation read; PF sweeps of R dwordx4 loads are in
+    // flight per lane (12 loads for S <= 2)
+    constexpr int R = S <= 2 ? QG_I4G_R : 2;
+    constexpr int PF = S <= 2 ? QG_I4G_PF : 4;
+    switch (pick_lpr(I / 32)) {
+    case 64: return launch_stream_t<S, 64, R, PF>(w, s, x, y, I, O, gs, st);
+    case 32: return launch_stream_t<S, 32, R, PF>(w, s, x, y, I, O, gs, st);
+    case 16: return launch_stream_t<S, 16, R, PF>(w, s, x, y, I, O, gs, st);
+    case 8: return launch_stream_t<S, 8, R, PF>(w, s, x, y, I, O, gs, st);
+    default: return launch_stream_t<S, 4, R, PF>(w, s, x, y, I, O, gs, st);
+    }
+}
+
+}  // namespace
+
+size_t i4g_stream_lds_bytes(int S, int I)
+{
+    return (size_t)S * (I / 32) * (8 * sizeof(f32x4) + sizeof(float));
+}
+
+bool i4g_stream_ok(const void *w, const float *x, int S, int I, int gs)
+{
+    if (S > I4G_FAST_MAX_S || I % 32 != 0 || gs % 32 != 0 || ((uintptr_t)w & 15) != 0 ||
+        ((uintptr_t)x & 15) != 0)
+        return false;
+    return i4g_stream_lds_bytes(S, I) <= LDS_BUDGET;
+}
+
+hipError_t launch_i4g_gemv(const void *w, const float *scales, const float *x, float *y,
+                           int S, int I, int O, int gs, hipStream_t st)
+{
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    if (i4g_stream_ok(w, x, S, I, gs)) {
+        switch (S) {
+        case 1: return launch_stream_s<1>(wb, scales, x, y, I, O, gs, st);
+        case 2: return launch_stream_s<2>(wb, scales, x, y, I, O, gs, st);
+        case 3: return launch_stream_s<3>(wb, scales, x, y, I, O, gs, st);
+        default: return launch_stream_s<4>(wb, scales, x, y, I, O, gs, st);
+        }
+    }
+    const int wpb = 4;
+    hipLaunchKernelGGL(i4g_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
+                       scales, x, y, S, I, O, gs);
+    return hipGetLastError();
+}
+
+hipError_t launch_i4g_dequant(const void *w, const float *scales, float *W, int I, int O,
+                              int gs, hipStream_t st)
+{
+    const size_t n = (size_t)O * ((I + 1) / 2);
+    const int threads = 256;
+    const size_t want = (n + threads - 1) / threads;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(i4g_dequant, dim3(blocks), dim3(threads), 0, st,
+                       static_cast<const uint8_t *>(w), scales, W, I, O, gs);
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,201 @@
+// qg_device.h -- device helpers shared by the gfx950 GEMV kernels.
+//
+// Wave64 only.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------
+// Nibble decode.
+//
+// A byte whose top four bits are clear, read as an OCP E4M3 code, has value
+// q * 2^-9 for q = 0..15: q < 8 is the subnormal q * 2^-9, q >= 8 is exponent
+// 1 with mantissa q - 8, i.e. (8 + (q-8)) * 2^-9.  So masking the nibbles of a
+// packed dword into separate bytes and feeding them to the hardware
+// fp8->f32 pair converter decodes two nibbles per instruction, exactly.
+// Activations are staged pre-multiplied by 2^9 so products come out as q*x.
+// ---------------------------------------------------------------------------
+constexpr float NIB_XSCALE = 512.0f;  // 2^9
+
+// Decodes the 8 nibbles of one little-endian packed dword.
+//   e[0..3] = nibbles of bytes 0..3 low halves  (columns 0, 2, 4, 6)
+//   o[0..3] = nibbles of bytes 0..3 high halves (columns 1, 3, 5, 7)
+// each as q * 2^-9.
+__device__ __forceinline__ void nib8(uint32_t w, float e[4], float o[4])
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu;
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    e[0] = a.x; e[1] = a.y; e[2] = b.x; e[3] = b.y;
+    o[0] = c.x; o[1] = c.y; o[2] = d.x; o[3] = d.y;
+}
+
+// Four E4M3 codes of a dword (byte k = column k) as floats, exactly.
+__device__ __forceinline__ void e4m3x4(uint32_t w, float v[4])
+{
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+}
+
+// IEEE binary16 bits -> f32 (exact).
+__device__ __forceinline__ float f16_to_f32(uint32_t h16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// 8-lane sum (lanes 8m..8m+7); lane 8m+7 holds it.  Defined before use.
+__device__ __forceinline__ float sub_reduce8(float v);
+
+// ---------------------------------------------------------------------------
+// Activation staging for the 4-bit formats.
+//
+// A "lane chunk" is 16 packed bytes = 32 columns.  For chunk u and segment
+// k = 0..7 the LDS holds one float4:
+//    k = 2d   : x[32u + 8d + {0,2,4,6}] * 2^9   (matches low nibbles of dword d)
+//    k = 2d+1 : x[32u + 8d + {1,3,5,7}] * 2^9   (matches high nibbles)
+// stored at float4 index (k * NU + u), NU = chunks per vector, so that lanes
+// reading consecutive chunks touch consecutive 16-byte LDS words (no bank
+// conflicts).  xs[u] = plain f32 sum of the chunk's 32 activations, used to
+// fold per-chunk affine offsets out of the inner loop.
+// ---------------------------------------------------------------------------
+// Stages S activation vectors of I columns into the LDS layout above.
+// Loads are coalesced: thread f of the workgroup reads float4 number f of x
+// (so each load instruction of a wave covers 1 KB of consecutive bytes); the
+// eight float4s of one lane chunk sit in eight consecutive lanes, whose sum is
+// formed with an 8-lane DPP reduction.  load() issues the first NPRE float4s
+// per thread into registers (call it before issuing the weight stream, so the
+// in-order wait for them never waits for weights); store() writes them and
+// stages any remainder.  blockDim.x must be a multiple of 64.
+template <int S>
+struct XStage {
+    static constexpr int NPRE = 8;
+    f32x4 v[NPRE];
+
+    __device__ __forceinline__ void load(const float *__restrict__ x, int I, int NU)
+    {
+        const int total = S * NU * 8;
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const int f = threadIdx.x + j * blockDim.x;
+            if (f < total) v[j] = x4[f];
+        }
+        (void)I;
+    }
+
+    __device__ __forceinline__ static void put(f32x4 a, int f, int NU, f32x4 *__restrict__ xl,
+                                               float *__restrict__ xs)
+    {
+        const int cpv = NU * 8;                  // float4s per vector
+        const int t = f / cpv;
+        const int rem = f - t * cpv;
+        const int u = rem >> 3, k = rem & 7;
+        const int d = k >> 1, h = k & 1;
+        float *base = reinterpret_cast<float *>(xl + (size_t)t * 8 * NU);
+        f32x2 ev = {a.x * NIB_XSCALE, a.z * NIB_XSCALE};
+        f32x2 od = {a.y * NIB_XSCALE, a.w * NIB_XSCALE};
+        *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d) * NU + u) * 4 + 2 * h) = ev;
+        *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d + 1) * NU + u) * 4 + 2 * h) = od;
+        const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
+        if (k == 7) xs[(size_t)t * NU + u] = cs;
+    }
+
+    __device__ __forceinline__ void store(const float *__restrict__ x, int I, int NU,
+                                          f32x4 *__restrict__ xl, float *__restrict__ xs)
+    {
+        const int total = S * NU * 8;
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const int f = threadIdx.x + j * blockDim.x;
+            if (f < total) put(v[j], f, NU, xl, xs);
+        }
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+        for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x)
+            put(x4[f], f, NU, xl, xs);
+        (void)I;
+    }
+};
+
+// sum over the 32 columns of one lane chunk of q*x (x pre-scaled in LDS).
+__device__ __forceinline__ float nib_chunk_dot(const u32x4 wv, const f32x4 *__restrict__ xl,
+                                               int NU, int u)
+{
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        float e[4], o[4];
+        nib8(wv[d], e, o);
+        const f32x4 xe = xl[(2 * d) * NU + u];
+        const f32x4 xo = xl[(2 * d + 1) * NU + u];
+        p0 = __builtin_fmaf(e[0], xe.x, p0);
+        p1 = __builtin_fmaf(o[0], xo.x, p1);
+        p0 = __builtin_fmaf(e[1], xe.y, p0);
+        p1 = __builtin_fmaf(o[1], xo.y, p1);
+        p0 = __builtin_fmaf(e[2], xe.z, p0);
+        p1 = __builtin_fmaf(o[2], xo.z, p1);
+        p0 = __builtin_fmaf(e[3], xe.w, p0);
+        p1 = __builtin_fmaf(o[3], xo.w, p1);
+    }
+    return p0 + p1;
+}
+
+// ---------------------------------------------------------------------------
+// Sub-wave sum over LPR consecutive lanes (LPR in 4..64) with DPP.  The full
+// sum lands in the last lane of each LPR-lane group.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float sub_reduce(float v)
+{
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "LPR");
+    v += dpp<0xB1>(v);                       // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4E>(v);                       // quad_perm [2,3,0,1]: lane ^ 2
+    if (LPR >= 8) v += dpp<0x141>(v);        // row_half_mirror: 8-lane sums
+    if (LPR >= 16) v += dpp<0x140>(v);       // row_mirror: 16-lane sums
+    if (LPR >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    if (LPR >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ float sub_reduce8(float v) { return sub_reduce<8>(v); }
+
+// ---------------------------------------------------------------------------
+// floor(u / d) via a 64-bit reciprocal multiply, exact whenever u * d < 2^40
+// (here u < 2^20 and d < 2^20): with m = ceil(2^40 / d), u*m / 2^40 exceeds
+// u/d by less than u / 2^40 < 1/d, which cannot reach the next integer.
+// ---------------------------------------------------------------------------
+struct Div20 {
+    uint64_t m;
+    __host__ __device__ static Div20 make(uint32_t d)
+    {
+        Div20 r;
+        r.m = ((1ull << 40) + d - 1) / d;
+        return r;
+    }
+    __device__ __forceinline__ uint32_t operator()(uint32_t u) const
+    {
+        return (uint32_t)(((uint64_t)u * m) >> 40);
+    }
+};
+
+}  // namespace qg

@@ -1,0 +1,55 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+that include/qgemv.h declares, and refuses bad arguments by name before it
+touches any pointer (0xdeadbeef pointers are never dereferenced)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BAD = 0xDEADBEEF0  # 16-byte aligned, never mapped
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantized_weight_decode_amd as q
+    try:
+        q.lib()
+    except ImportError as e:
+        pytest.skip(str(e))
+    return q
+
+
+def declared_entry_points():
+    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemv_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree(q):
+    assert sorted(q.ENTRY_POINTS) == declared_entry_points()
+
+
+def test_library_exports_every_declared_symbol(q):
+    assert sorted(q.exported_symbols()) == declared_entry_points()
+
+
+def test_strerror_names_every_status(q):
+    for st in range(0, 9):
+        assert q.strerror(st) and q.strerror(st) != "unknown status"
+    assert q.strerror(99) == "unknown status"
+
+
+def test_i4g_refusals(q):
+    f = q.qgemv_i4g
+    assert f(0, BAD, BAD, BAD, 1, 64, 8, 64, 0) == 1            # NULL
+    assert f(BAD, BAD, BAD, BAD, 0, 64, 8, 64, 0) == 2          # S = 0
+    assert f(BAD, BAD, BAD, BAD, 9, 64, 8, 64, 0) == 2          # S > 8
+    assert f(BAD, BAD, BAD, BAD, 1, 0, 8, 64, 0) == 2           # I = 0
+    assert f(BAD, BAD, BAD, BAD, 1, 64, -1, 64, 0) == 2         # O < 0
+    assert f(BAD, BAD, BAD, BAD, 1, 64, 8, 63, 0) == 3          # odd gs
+    assert f(BAD, BAD, BAD, BAD, 1, 64, 8, 0, 0) == 3           # gs = 0
+    assert f(BAD, BAD + 2, BAD, BAD, 1, 64, 8, 64, 0) == 4      # misaligned scales
+    assert f(BAD, BAD, BAD, BAD + 1, 1, 64, 8, 64, 0) == 4      # misaligned y
+    assert q.qgemv_dequant_i4g(BAD, BAD, 0, 64, 8, 64, 0) == 1
+    assert q.qgemv_dequant_i4g(BAD, BAD, BAD, 64, 8, 5, 0) == 3

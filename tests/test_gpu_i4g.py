@@ -1,0 +1,99 @@
+"""Grouped-int4 GEMV on the GPU against the CPU oracle.
+
+Shapes follow colibri PR #457, section 5 (I a multiple of gs, I = 200 / 201,
+I <= gs, S = 1..4, an activation forced to 50.0 in group 0) plus the
+workload shapes O=256 x I=512 and O=12288 x I=6144 at gs = 64 and 128.
+Decoded weights must match bit for bit; y to relative L2 <= 1e-5.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_bits_equal, assert_y_close, dev, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    torch_cuda()
+    import quantized_weight_decode_amd as q
+    return q
+
+
+@pytest.mark.parametrize("O,I,gs", [(256, 512, 64), (37, 201, 64), (64, 6144, 128), (5, 40, 64),
+                                    (130, 300, 16), (1, 1, 2)])
+def test_dequant_bit_exact(q, qref, O, I, gs):
+    d = W.gen_i4g(O, I, gs, seed=O + I)
+    got = host(q.dequant_i4g(dev(d["w"]), dev(d["scales"]), I, gs))
+    assert_bits_equal(got, qref.i4g_dequant(d["w"], d["scales"], O, I, gs))
+
+
+@pytest.mark.parametrize("O,I,gs,S", [
+    (256, 512, 64, 1),        # small workload
+    (12288, 6144, 64, 1),     # resident-projection workload, gs 64
+    (12288, 6144, 128, 1),    # same shape, gs 128
+    (2048, 6144, 64, 4), (6144, 2048, 64, 1), (333, 2048, 64, 3),
+    (77, 200, 64, 2), (77, 201, 64, 1), (9, 64, 64, 1), (9, 40, 64, 4),
+    (50, 512, 64, 8), (100, 1024, 96, 2), (31, 4096, 256, 1), (3, 96, 32, 1),
+    (1, 32, 32, 1), (1, 1, 2, 1),
+])
+def test_gemv_matches_oracle(q, qref, O, I, gs, S):
+    d = W.gen_i4g(O, I, gs, S=S, seed=7 * O + I)
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), gs))
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
+
+
+@pytest.mark.parametrize("I", [512, 201])
+def test_outlier_activation(q, qref, I):
+    d = W.gen_i4g(64, I, 64, seed=3)
+    d["x"][0, 5] = 50.0
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], 64, I, 64))
+
+
+def test_magnitude_relative_error(q, qref):
+    # per-element |dy| / sum_i |w_i x_i| <= 1e-4 (colibri PR #457, section 5)
+    O, I, gs = 512, 2048, 64
+    d = W.gen_i4g(O, I, gs, seed=21)
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), gs))[0]
+    ref = qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs)[0]
+    mag = np.abs(qref.i4g_dequant(d["w"], d["scales"], O, I, gs).astype(np.float64)) @ \
+        np.abs(d["x"][0].astype(np.float64))
+    assert np.max(np.abs(y - ref) / mag) <= 1e-4
+
+
+def test_nan_activation_poisons_all_rows(q):
+    d = W.gen_i4g(40, 256, 64, seed=4)
+    d["x"][0, 100] = np.nan
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
+    assert np.isnan(y).all()
+
+
+def test_misaligned_weights_take_general_path(q, qref):
+    import torch
+    O, I, gs = 20, 512, 64
+    d = W.gen_i4g(O, I, gs, seed=5)
+    buf = torch.zeros(d["w"].size + 8, dtype=torch.uint8, device="cuda")
+    buf[8:] = dev(d["w"].reshape(-1))
+    w_off = buf[8:]  # 8-byte offset: not 16-byte aligned
+    y = torch.empty((1, O), dtype=torch.float32, device="cuda")
+    x = dev(d["x"])
+    s = dev(d["scales"])
+    st = q.qgemv_i4g(w_off.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), 1, I, O, gs,
+                     torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert_y_close(host(y), qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
+
+
+def test_output_rows_outside_o_untouched(q):
+    import torch
+    d = W.gen_i4g(37, 512, 64, S=2, seed=6)
+    y = torch.full((2, 37 + 64), 7.0, device="cuda")
+    yv = y[:, :37]
+    # write through the raw ABI into a wider buffer: rows >= O must stay 7.0
+    st = q.qgemv_i4g(dev(d["w"]).data_ptr(), dev(d["scales"]).data_ptr(), dev(d["x"]).data_ptr(),
+                     y.data_ptr(), 2, 512, 37, 64, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    flat = host(y).reshape(-1)
+    assert np.all(flat[2 * 37:] == 7.0)
