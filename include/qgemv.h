@@ -97,7 +97,8 @@ int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I,
  *     x_rot[b] = (1/16) * H256 * (signs[b] (.) x[b])
  * with H256 the Sylvester Hadamard matrix H[i][j] = (-1)^popcount(i&j).
  *   x f32 [S][I], signs int8 [I] (each +1 or -1), x_rot f32 [S][I];
- *   I % 256 == 0.  x_rot may not alias x.
+ *   I % 256 == 0; x and x_rot must be 16-byte aligned and may be the same
+ *   buffer (in-place rotation).
  */
 int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S,
                   int I, void *stream);
@@ -118,7 +119,7 @@ int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S,
  *   gates    f32 [T][K],  x f32 [T][I],  y f32 [T][O] (overwritten)
  *   T in 1..8, K in 1..64, gs even >= 2
  *   workspace  device scratch of at least qgemv_moe_topk_workspace(T, K, O)
- *              bytes, 256-byte aligned; its contents are overwritten.
+ *              bytes, 4-byte aligned; its contents are overwritten.
  * Each distinct selected expert is streamed from memory once per call, for
  * all tokens that selected it.  The routing never leaves the device.
  */

@@ -82,4 +82,86 @@ int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I, int O
     return launched(qg::launch_i4g_dequant(w, scales, W, I, O, gs, (hipStream_t)stream));
 }
 
+int qgemv_fp8b128(const void *w, const float *scale_inv, const float *x, float *y, int S,
+                  int I, int O, void *stream)
+{
+    if (!w || !scale_inv || !x || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (mis4(scale_inv) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_fp8b128_gemv(w, scale_inv, x, y, S, I, O, (hipStream_t)stream));
+}
+
+int qgemv_dequant_fp8b128(const void *w, const float *scale_inv, float *W, int I, int O,
+                          void *stream)
+{
+    if (!w || !scale_inv || !W) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (mis4(scale_inv) || mis4(W)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_fp8b128_dequant(w, scale_inv, W, I, O, (hipStream_t)stream));
+}
+
+int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I, int O, void *stream)
+{
+    if (!w || !x_rot || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(x_rot) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4v2_gemv(w, x_rot, y, S, I, O, (hipStream_t)stream));
+}
+
+int qgemv_dequant_mq4v2(const void *w, float *W, int I, int O, void *stream)
+{
+    if (!w || !W) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(W)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4v2_dequant(w, W, I, O, (hipStream_t)stream));
+}
+
+int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S, int I, void *stream)
+{
+    if (!x || !signs || !x_rot) return QGEMV_E_NULL;
+    if (S < 1 || S > QGEMV_MAX_S || I < 1 || I > MAX_DIM) return QGEMV_E_DIMS;
+    if (I % 256) return QGEMV_E_K256;
+    // x and x_rot are read and written as float4
+    if (((uintptr_t)x | (uintptr_t)x_rot) & 15) return QGEMV_E_ALIGN;
+    return launched(qg::launch_fwht256(x, signs, x_rot, S, I, (hipStream_t)stream));
+}
+
+size_t qgemv_moe_topk_workspace(int T, int K, int O)
+{
+    (void)T; (void)K; (void)O;
+    return qg::MOE_WORKSPACE_BYTES;
+}
+
+int qgemv_moe_topk(const void *w, const float *scales, long long w_stride, long long s_stride,
+                   int E, const int32_t *ids, const float *gates, int T, int K, const float *x,
+                   float *y, int I, int O, int gs, void *workspace, size_t ws_bytes,
+                   void *stream)
+{
+    if (!w || !scales || !ids || !gates || !x || !y) return QGEMV_E_NULL;
+    if (T < 1 || T > QGEMV_MAX_S || K < 1 || K > 64 || E < 1 || I < 1 || O < 1 ||
+        I > MAX_DIM || O > MAX_DIM)
+        return QGEMV_E_DIMS;
+    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (mis4(scales) || mis4(ids) || mis4(gates) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
+    const long long rb = (I + 1) / 2, ng = (I + gs - 1) / gs;
+    if (w_stride < (long long)O * rb || s_stride < (long long)O * ng) return QGEMV_E_IDS;
+    if (!workspace || ws_bytes < qgemv_moe_topk_workspace(T, K, O) || mis4(workspace))
+        return QGEMV_E_WORKSPACE;
+    return launched(qg::launch_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
+                                        I, O, gs, static_cast<int *>(workspace),
+                                        (hipStream_t)stream));
+}
+
+int qgemv_moe_topk_error(const void *workspace, int *flag, void *stream)
+{
+    if (!workspace || !flag) return QGEMV_E_NULL;
+    if (mis4(workspace)) return QGEMV_E_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (hipMemcpyAsync(flag, workspace, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return QGEMV_E_HIP;
+    return hipStreamSynchronize(st) == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+}
+
 }  // extern "C"

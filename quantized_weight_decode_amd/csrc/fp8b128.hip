@@ -1,0 +1,300 @@
+// fp8b128.hip -- fp8-e4m3 GEMV with 128x128 block scales ("fmt=7") for gfx950.
+//
+// Format ("fmt=7: fp8-e4m3-b128 passthrough weight format", section
+// "Design"): row-major u8[O][I] OCP E4M3-FN codes; f32 scale per 128x128
+// block in row-major block order; weight = e4m3(code) * scale (a multiply).
+//
+// Streaming kernel (I % 16 == 0, 16-byte aligned rows):
+//   * x is staged once per workgroup in LDS as float4 segments k = 0..3 of
+//     each 16-column lane chunk u, stored at float4 index k * NU + u (lanes on
+//     consecutive chunks read consecutive LDS words);
+//   * a lane group of LPR lanes sweeps R consecutive rows with dwordx4 loads;
+//     the R rows share one 128-row band, so one block scale per chunk serves
+//     all of them; E4M3 pairs go through the hardware pair converter (exact,
+//     OCP semantics: NaN only for 0x7F/0xFF, subnormals, -0);
+//   * acc += scale_block * sum_16(w * x); the row sum is a DPP reduction.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+#ifndef QG_FP8_R
+#define QG_FP8_R 4
+#endif
+#ifndef QG_FP8_PF
+#define QG_FP8_PF 2
+#endif
+#ifndef QG_FP8_WPB
+#define QG_FP8_WPB 4
+#endif
+
+namespace qg {
+
+constexpr int FP8_FAST_MAX_S = 4;
+
+// Stages S vectors into the fp8 LDS layout with coalesced float4 loads.
+template <int S>
+struct XStageF8 {
+    static constexpr int NPRE = 8;
+    f32x4 v[NPRE];
+
+    __device__ __forceinline__ void load(const float *__restrict__ x, int NU)
+    {
+        const int total = S * NU * 4;
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const int f = threadIdx.x + j * blockDim.x;
+            if (f < total) v[j] = x4[f];
+        }
+    }
+
+    __device__ __forceinline__ static void put(f32x4 a, int f, int NU, f32x4 *__restrict__ xl)
+    {
+        const int t = f / (NU * 4);
+        const int rem = f - t * NU * 4;
+        xl[(size_t)t * 4 * NU + (size_t)(rem & 3) * NU + (rem >> 2)] = a;
+    }
+
+    __device__ __forceinline__ void store(const float *__restrict__ x, int NU,
+                                          f32x4 *__restrict__ xl)
+    {
+        const int total = S * NU * 4;
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const int f = threadIdx.x + j * blockDim.x;
+            if (f < total) put(v[j], f, NU, xl);
+        }
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+        for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x)
+            put(x4[f], f, NU, xl);
+    }
+};
+
+// sum over the 16 columns of one lane chunk of e4m3(w) * x
+__device__ __forceinline__ float fp8_chunk_dot(const u32x4 wv, const f32x4 *__restrict__ xl,
+                                               int NU, int u)
+{
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        float v[4];
+        e4m3x4(wv[d], v);
+        const f32x4 xv = xl[(size_t)d * NU + u];
+        p0 = __builtin_fmaf(v[0], xv.x, p0);
+        p1 = __builtin_fmaf(v[1], xv.y, p1);
+        p0 = __builtin_fmaf(v[2], xv.z, p0);
+        p1 = __builtin_fmaf(v[3], xv.w, p1);
+    }
+    return p0 + p1;
+}
+
+template <int S, int LPR, int R, int PF>
+__global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
+    const uint8_t *__restrict__ w, const float *__restrict__ sc, const float *__restrict__ x,
+    float *__restrict__ y, int I, int O, int nbi, int ntiles)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    static_assert(128 % R == 0, "a lane group's rows must share one 128-row band");
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int NU = I / 16;
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);   // [S][4][NU]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane / LPR;
+    const int sl = lane % LPR;
+    const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+    const int row0 = tile * ROWS_PER_WAVE + sub * R;
+    const int nit = (NU + LPR - 1) / LPR;
+    const float *scrow = sc + (size_t)(min(row0, O - 1) / 128) * nbi;
+
+    const uint8_t *wr[R];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        wr[r] = w + (size_t)min(row0 + r, O - 1) * I;
+
+    XStageF8<S> xst;
+    xst.load(x, NU);
+
+    u32x4 wb[PF][R];
+    float sb[PF];
+#pragma unroll
+    for (int j = 0; j < PF; j++) {
+        if (j < nit) {
+            const int u = min(j * LPR + sl, NU - 1);
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16);
+            sb[j] = scrow[u >> 3];
+        }
+    }
+
+    xst.store(x, NU, xl);
+    __syncthreads();
+    if (tile >= ntiles) return;
+
+    float acc[S][R];
+#pragma unroll
+    for (int t = 0; t < S; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+
+    for (int c0 = 0; c0 < nit; c0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            const int c = c0 + j;
+            if (c < nit) {
+                const int u = c * LPR + sl;
+                const bool valid = u < NU;
+                const int uu = valid ? u : 0;
+                const float s = sb[j];
+#pragma unroll
+                for (int t = 0; t < S; t++) {
+                    const f32x4 *xt = xl + (size_t)t * 4 * NU;
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        const float p = fp8_chunk_dot(wb[j][r], xt, NU, uu);
+                        // lanes past the row end add nothing (not even a NaN)
+                        acc[t][r] = valid ? __builtin_fmaf(s, p, acc[t][r]) : acc[t][r];
+                    }
+                }
+                if (c + PF < nit) {
+                    const int un = min(u + PF * LPR, NU - 1);
+#pragma unroll
+                    for (int r = 0; r < R; r++)
+                        wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)un * 16);
+                    sb[j] = scrow[un >> 3];
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < S; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const float v = sub_reduce<LPR>(acc[t][r]);
+            if (sl == LPR - 1 && row0 + r < O) y[(size_t)t * O + row0 + r] = v;
+        }
+}
+
+// General kernel: any I >= 1, any alignment, S <= QGEMV_MAX_S.  One wave per
+// row; each weight decoded to f32 and multiplied by its block scale (one
+// rounding), then multiplied into x in f32.
+__global__ __launch_bounds__(256) void fp8_gemv_general(
+    const uint8_t *__restrict__ w, const float *__restrict__ sc, const float *__restrict__ x,
+    float *__restrict__ y, int S, int I, int O)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (row >= O) return;
+    const int nbi = (I + 127) / 128;
+    const uint8_t *wr = w + (size_t)row * I;
+    const float *scr = sc + (size_t)(row / 128) * nbi;
+    float acc[QGEMV_MAX_S];
+#pragma unroll
+    for (int t = 0; t < QGEMV_MAX_S; t++) acc[t] = 0.0f;
+    for (int i = lane; i < I; i += WAVE) {
+        float v[4];
+        e4m3x4((uint32_t)wr[i], v);
+        const float wv = v[0] * scr[i / 128];
+#pragma unroll
+        for (int t = 0; t < QGEMV_MAX_S; t++)
+            if (t < S) acc[t] = __builtin_fmaf(wv, x[(size_t)t * I + i], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < QGEMV_MAX_S; t++) {
+        if (t < S) {
+            const float v = sub_reduce<64>(acc[t]);
+            if (lane == 63) y[(size_t)t * O + row] = v;
+        }
+    }
+}
+
+// Decode-only: W[o][i] = e4m3(w[o][i]) * scale[o/128][i/128] as f32.
+__global__ __launch_bounds__(256) void fp8_dequant(const uint8_t *__restrict__ w,
+                                                   const float *__restrict__ sc,
+                                                   float *__restrict__ W, int I, int O)
+{
+    const int nbi = (I + 127) / 128;
+    const size_t n = (size_t)O * I;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const size_t o = idx / I;
+        const int i = (int)(idx - o * I);
+        float v[4];
+        e4m3x4((uint32_t)w[idx], v);
+        W[idx] = v[0] * sc[(o / 128) * nbi + i / 128];
+    }
+}
+
+namespace {
+
+// 16 columns per lane chunk = 4 float4 segments
+size_t fp8_lds_bytes(int S, int I) { return (size_t)S * (I / 16) * 4 * sizeof(f32x4); }
+
+template <int S, int LPR, int R, int PF>
+hipError_t launch_t(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
+                    hipStream_t st)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    const int wpb = QG_FP8_WPB;
+    const int blocks = (ntiles + wpb - 1) / wpb;
+    const size_t lds = fp8_lds_bytes(S, I);
+    auto kern = fp8_gemv_stream<S, LPR, R, PF>;
+    hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * wpb), lds, st, w, sc, x, y, I, O,
+                       (I + 127) / 128, ntiles);
+    return hipGetLastError();
+}
+
+template <int S>
+hipError_t launch_s(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
+                    hipStream_t st)
+{
+    constexpr int R = S <= 2 ? QG_FP8_R : 2;
+    constexpr int PF = QG_FP8_PF;
+    switch (pick_lpr(I / 16)) {
+    case 64: return launch_t<S, 64, R, PF>(w, sc, x, y, I, O, st);
+    case 32: return launch_t<S, 32, R, PF>(w, sc, x, y, I, O, st);
+    case 16: return launch_t<S, 16, R, PF>(w, sc, x, y, I, O, st);
+    case 8: return launch_t<S, 8, R, PF>(w, sc, x, y, I, O, st);
+    default: return launch_t<S, 4, R, PF>(w, sc, x, y, I, O, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const float *x, float *y,
+                               int S, int I, int O, hipStream_t st)
+{
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const bool fast = S <= FP8_FAST_MAX_S && I % 16 == 0 && ((uintptr_t)w & 15) == 0 &&
+                      ((uintptr_t)x & 15) == 0 && fp8_lds_bytes(S, I) <= LDS_BUDGET;
+    if (fast) {
+        switch (S) {
+        case 1: return launch_s<1>(wb, scale_inv, x, y, I, O, st);
+        case 2: return launch_s<2>(wb, scale_inv, x, y, I, O, st);
+        case 3: return launch_s<3>(wb, scale_inv, x, y, I, O, st);
+        default: return launch_s<4>(wb, scale_inv, x, y, I, O, st);
+        }
+    }
+    const int wpb = 4;
+    hipLaunchKernelGGL(fp8_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
+                       scale_inv, x, y, S, I, O);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8b128_dequant(const void *w, const float *scale_inv, float *W, int I, int O,
+                                  hipStream_t st)
+{
+    const size_t n = (size_t)O * I;
+    const size_t want = (n + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(fp8_dequant, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(w), scale_inv, W, I, O);
+    return hipGetLastError();
+}
+
+}  // namespace qg

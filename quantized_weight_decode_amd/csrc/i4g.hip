@@ -207,20 +207,6 @@ __global__ __launch_bounds__(256) void i4g_dequant(
 // ---------------------------------------------------------------------------
 namespace {
 
-// lanes per row: the widest of 64/32/16/8/4 whose last sweep is not mostly idle
-int pick_lpr(int nchunks)
-{
-    const int opts[] = {64, 32, 16, 8, 4};
-    int best = 4;
-    double best_eff = -1.0;
-    for (int lpr : opts) {
-        const int it = (nchunks + lpr - 1) / lpr;
-        const double eff = (double)nchunks / ((double)it * lpr);
-        if (eff > best_eff + 1e-9) { best_eff = eff; best = lpr; }
-    }
-    return best;
-}
-
 template <int S, int LPR, int R, int PF>
 hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, float *y,
                            int I, int O, int gs, hipStream_t st)

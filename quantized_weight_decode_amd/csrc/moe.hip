@@ -1,0 +1,378 @@
+// moe.hip -- routed-expert GEMV over grouped-int4 experts for gfx950.
+//
+//   y[t][o] = sum_k gates[t][k] * (W_{ids[t][k]} . x[t])[o],  k ascending
+//
+// (regolith audit "phase 0 + phase 2 m5 air validation", section 2.2: the
+// gates are the selection probabilities renormalised over the selected
+// experts; colibri PR #457, section 4: routed experts are grouped-int4.)
+//
+// One launch, no host round trip, no atomics:
+//   * a workgroup owns RT consecutive output rows for every token;
+//   * each wave reads the T*K ids (T*K <= 64) into its lanes and derives with
+//     ballots the distinct valid experts (first-occurrence order) and, for
+//     each, the set of tokens that chose it -- the routing never leaves the
+//     device;
+//   * work units are (distinct expert, sub-tile of rows), dealt round-robin
+//     to the waves; a unit streams its rows of that expert once (dwordx4,
+//     scale gather) and forms the dot products of every token that chose it,
+//     with x of all tokens staged in LDS as for the dense grouped-int4 GEMV;
+//     the next unit's first loads are issued while the current one finishes;
+//   * a unit's row sums go to an LDS partial array [T][K][RT] for every slot
+//     (t, k) that selected the expert; after a barrier the workgroup forms
+//     y = sum_k gates * partial in ascending k (deterministic).
+// An id outside [0, E) is never dereferenced: its token's row of y is NaN and
+// the workspace error flag is set.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+#ifndef QG_MOE_R
+#define QG_MOE_R 2
+#endif
+#ifndef QG_MOE_WPB
+#define QG_MOE_WPB 16
+#endif
+
+namespace qg {
+
+constexpr int MOE_MAX_T = 8;
+constexpr int MOE_FAST_MAX_TK = 64;
+
+struct Routing {
+    int e;            // this lane's id (lane < T*K), or -1
+    uint64_t first;   // lanes holding the first occurrence of a valid id
+    uint32_t mask;    // on a first-occurrence lane: tokens that chose the id
+    uint32_t bad;     // tokens with an out-of-range id
+    int nu;           // distinct valid experts
+};
+
+// Every lane of the wave calls this (wave-uniform results except e / mask).
+__device__ __forceinline__ Routing route(const int32_t *__restrict__ ids, int T, int K, int E)
+{
+    const int lane = threadIdx.x & 63;
+    const int TK = T * K;
+    Routing rt;
+    rt.e = lane < TK ? ids[lane] : -1;
+    const bool in = lane < TK;
+    const bool valid = in && rt.e >= 0 && rt.e < E;
+    bool first = valid;
+    uint32_t mask = 0;
+    for (int q = 0; q < TK; q++) {
+        const int eq = __builtin_amdgcn_readlane(rt.e, q);
+        if (eq == rt.e) {
+            if (q < lane) first = false;
+            mask |= 1u << (q / K);
+        }
+    }
+    rt.first = __ballot(first);
+    rt.mask = mask;
+    const uint64_t badl = __ballot(in && !valid);
+    uint32_t bad = 0;
+    for (int t = 0; t < T; t++)
+        if ((badl >> (t * K)) & ((K == 64) ? ~0ull : ((1ull << K) - 1))) bad |= 1u << t;
+    rt.bad = bad;
+    rt.nu = __popcll(rt.first);
+    return rt;
+}
+
+// Lane holding the ui-th distinct expert.
+__device__ __forceinline__ int unique_lane(const Routing &rt, int ui)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = lane ? (rt.first & ((1ull << lane) - 1)) : 0ull;
+    const int idx = __popcll(below);
+    const uint64_t sel = __ballot(((rt.first >> lane) & 1) && idx == ui);
+    return __ffsll((long long)sel) - 1;
+}
+
+template <int LPR, int R>
+__global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
+    const uint8_t *__restrict__ w, const float *__restrict__ scales, long long w_stride,
+    long long s_stride, int E, const int32_t *__restrict__ ids, const float *__restrict__ gates,
+    int T, int K, const float *__restrict__ x, float *__restrict__ y, int I, int O, int ng,
+    Div20 div_cpg, int RT, int *__restrict__ err_flag)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int NU = I / 32;
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [T][8][NU]
+    float *xs = reinterpret_cast<float *>(xl + (size_t)T * 8 * NU);  // [T][NU]
+    float *part = xs + (size_t)T * NU;                               // [T][K][RT]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int sub = lane / LPR;
+    const int sl = lane % LPR;
+    const int o0 = blockIdx.x * RT;
+    const size_t rb = (size_t)I / 2;
+    const int nit = (NU + LPR - 1) / LPR;
+    const int nsub = RT / ROWS_PER_WAVE;
+
+    const Routing rt = route(ids, T, K, E);
+    if (blockIdx.x == 0 && threadIdx.x == 0) err_flag[0] = rt.bad ? 1 : 0;
+
+    // activations of all tokens are requested before any weight
+    const int total4 = T * NU * 8;
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+    constexpr int NPRE = 8;
+    f32x4 xv[NPRE];
+#pragma unroll
+    for (int j = 0; j < NPRE; j++) {
+        const int f = threadIdx.x + j * blockDim.x;
+        if (f < total4) xv[j] = x4[f];
+    }
+
+    // this wave's units: i = wave, wave + nwaves, ...; step s = (unit, sweep)
+    const int nunits = rt.nu * nsub;
+    const int my_units = wave < nunits ? (nunits - wave + nwaves - 1) / nwaves : 0;
+    const int nsteps = my_units * nit;
+
+    // per-unit state (wave-uniform)
+    int cur_e = 0;
+    uint32_t cur_mask = 0;
+    int cur_row0 = 0;     // first row of this lane group for the current unit
+    const uint8_t *wr[R];
+    const float *sr[R];
+    const uint8_t *nwr[R];
+    const float *nsr[R];
+
+    auto unit_setup = [&](int k, int &e, uint32_t &m, int &lrow0, const uint8_t **pw,
+                          const float **ps) {
+        const int i = wave + k * nwaves;
+        const int ui = i / nsub, st = i - ui * nsub;
+        const int ql = unique_lane(rt, ui);
+        e = __builtin_amdgcn_readlane(rt.e, ql);
+        m = (uint32_t)__builtin_amdgcn_readlane((int)rt.mask, ql);
+        lrow0 = o0 + st * ROWS_PER_WAVE + sub * R;
+        const uint8_t *we = w + (size_t)e * (size_t)w_stride;
+        const float *se = scales + (size_t)e * (size_t)s_stride;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int row = min(lrow0 + r, O - 1);
+            pw[r] = we + (size_t)row * rb;
+            ps[r] = se + (size_t)row * ng;
+        }
+    };
+
+    u32x4 wc[R], wn[R];
+    float scur[R], sn[R];
+    if (nsteps > 0) {
+        unit_setup(0, cur_e, cur_mask, cur_row0, wr, sr);
+        const int u = min(sl, NU - 1);
+        const uint32_t g = div_cpg((uint32_t)u);
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            wc[r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16);
+            scur[r] = sr[r][g];
+        }
+    }
+
+    // stage activations
+#pragma unroll
+    for (int j = 0; j < NPRE; j++) {
+        const int f = threadIdx.x + j * blockDim.x;
+        if (f < total4) XStagePut(xv[j], f, NU, xl, xs);
+    }
+    for (int f = threadIdx.x + NPRE * blockDim.x; f < total4; f += blockDim.x)
+        XStagePut(x4[f], f, NU, xl, xs);
+    __syncthreads();
+
+    float acc[MOE_MAX_T][R];
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_T; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+
+    int nxt_e = 0, nxt_row0 = 0;
+    uint32_t nxt_mask = 0;
+    for (int s = 0; s < nsteps; s++) {
+        const int k = s / nit;
+        const int c = s - k * nit;
+        // prefetch step s+1 (possibly the next unit's first sweep)
+        const bool have_next = s + 1 < nsteps;
+        const bool next_new_unit = c + 1 == nit;
+        if (have_next) {
+            int un;
+            if (next_new_unit) {
+                unit_setup(k + 1, nxt_e, nxt_mask, nxt_row0, nwr, nsr);
+                un = min(sl, NU - 1);
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; r++) { nwr[r] = wr[r]; nsr[r] = sr[r]; }
+                un = min((c + 1) * LPR + sl, NU - 1);
+            }
+            const uint32_t g = div_cpg((uint32_t)un);
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                wn[r] = *reinterpret_cast<const u32x4 *>(nwr[r] + (size_t)un * 16);
+                sn[r] = nsr[r][g];
+            }
+        }
+
+        const int u = c * LPR + sl;
+        const bool valid = u < NU;
+        const int uu = valid ? u : 0;
+#pragma unroll
+        for (int t = 0; t < MOE_MAX_T; t++) {
+            if (t < T && ((cur_mask >> t) & 1)) {
+                const f32x4 *xt = xl + (size_t)t * 8 * NU;
+                const float xsum = xs[(size_t)t * NU + uu];
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const float p = nib_chunk_dot(wc[r], xt, NU, uu);
+                    const float tv = __builtin_fmaf(-8.0f, xsum, p);
+                    acc[t][r] = valid ? __builtin_fmaf(scur[r], tv, acc[t][r]) : acc[t][r];
+                }
+            }
+        }
+
+        if (c + 1 == nit) {
+            // unit done: row sums -> partials of every slot that chose cur_e
+#pragma unroll
+            for (int t = 0; t < MOE_MAX_T; t++) {
+                if (t < T && ((cur_mask >> t) & 1)) {
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        const float v = sub_reduce<LPR>(acc[t][r]);
+                        const int lr = cur_row0 + r - o0;
+                        if (sl == LPR - 1 && cur_row0 + r < O) {
+                            for (int kk = 0; kk < K; kk++)
+                                if (ids[t * K + kk] == cur_e) part[((size_t)t * K + kk) * RT + lr] = v;
+                        }
+                        acc[t][r] = 0.0f;
+                    }
+                }
+            }
+            if (have_next) {
+                cur_e = nxt_e;
+                cur_mask = nxt_mask;
+                cur_row0 = nxt_row0;
+#pragma unroll
+                for (int r = 0; r < R; r++) { wr[r] = nwr[r]; sr[r] = nsr[r]; }
+            }
+        }
+        if (have_next) {
+#pragma unroll
+            for (int r = 0; r < R; r++) { wc[r] = wn[r]; scur[r] = sn[r]; }
+        }
+    }
+    __syncthreads();
+
+    // combine in ascending k
+    for (int idx = threadIdx.x; idx < T * RT; idx += blockDim.x) {
+        const int t = idx / RT, i = idx - t * RT;
+        const int row = o0 + i;
+        if (row >= O) continue;
+        float v;
+        if ((rt.bad >> t) & 1) {
+            v = __builtin_nanf("");
+        } else {
+            v = 0.0f;
+            for (int kk = 0; kk < K; kk++)
+                v = __builtin_fmaf(gates[t * K + kk], part[((size_t)t * K + kk) * RT + i], v);
+        }
+        y[(size_t)t * O + row] = v;
+    }
+}
+
+// General kernel: any shape the streaming kernel does not take (T*K > 64,
+// unaligned rows or strides, LDS too small).  One wave per output row; each
+// (t, k) dot product is formed from per-weight f32 decodes, combined in
+// ascending k.  Also sets the error flag (block 0).
+__global__ __launch_bounds__(256) void moe_i4g_general(
+    const uint8_t *__restrict__ w, const float *__restrict__ scales, long long w_stride,
+    long long s_stride, int E, const int32_t *__restrict__ ids, const float *__restrict__ gates,
+    int T, int K, const float *__restrict__ x, float *__restrict__ y, int I, int O, int gs,
+    int *__restrict__ err_flag)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        int bad = 0;
+        for (int p = 0; p < T * K; p++) bad |= (ids[p] < 0 || ids[p] >= E);
+        err_flag[0] = bad;
+    }
+    if (row >= O) return;
+    const int rb = (I + 1) / 2;
+    const int ng = (I + gs - 1) / gs;
+    for (int t = 0; t < T; t++) {
+        float yt = 0.0f;
+        bool bad = false;
+        for (int kk = 0; kk < K; kk++) {
+            const int e = ids[t * K + kk];
+            if (e < 0 || e >= E) { bad = true; continue; }
+            const uint8_t *wr = w + (size_t)e * (size_t)w_stride + (size_t)row * rb;
+            const float *sr = scales + (size_t)e * (size_t)s_stride + (size_t)row * ng;
+            const float *xt = x + (size_t)t * I;
+            float acc = 0.0f;
+            for (int b = lane; b < rb; b += WAVE) {
+                float ev[4], od[4];
+                nib8((uint32_t)wr[b], ev, od);
+                const int c0 = 2 * b, c1 = 2 * b + 1;
+                acc = __builtin_fmaf((ev[0] * NIB_XSCALE - 8.0f) * sr[c0 / gs], xt[c0], acc);
+                if (c1 < I)
+                    acc = __builtin_fmaf((od[0] * NIB_XSCALE - 8.0f) * sr[c1 / gs], xt[c1], acc);
+            }
+            const float dot = sub_reduce<64>(acc);
+            yt = __builtin_fmaf(gates[t * K + kk], dot, yt);
+        }
+        if (lane == 63) y[(size_t)t * O + row] = bad ? __builtin_nanf("") : yt;
+    }
+}
+
+namespace {
+
+size_t moe_lds_bytes(int T, int K, int I, int RT)
+{
+    return (size_t)T * (I / 32) * (8 * sizeof(f32x4) + 4) + (size_t)T * K * RT * 4;
+}
+
+template <int LPR, int R>
+hipError_t launch_t(const uint8_t *w, const float *s, long long ws, long long ss, int E,
+                    const int32_t *ids, const float *gates, int T, int K, const float *x,
+                    float *y, int I, int O, int gs, int RT, int *err, hipStream_t st)
+{
+    const size_t lds = moe_lds_bytes(T, K, I, RT);
+    auto kern = moe_i4g_stream<LPR, R>;
+    hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
+    const int blocks = (O + RT - 1) / RT;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * QG_MOE_WPB), lds, st, w, s, ws, ss, E, ids,
+                       gates, T, K, x, y, I, O, (I + gs - 1) / gs,
+                       Div20::make((uint32_t)(gs / 32)), RT, err);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moe_topk(const void *w, const float *scales, long long w_stride,
+                           long long s_stride, int E, const int32_t *ids, const float *gates,
+                           int T, int K, const float *x, float *y, int I, int O, int gs,
+                           int *err_flag, hipStream_t st)
+{
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const int lpr = pick_lpr(I / 32 > 0 ? I / 32 : 1);
+    const int R = QG_MOE_R;
+    const int rpw = (WAVE / lpr) * R;
+    // rows per workgroup: a multiple of the wave tile, about one workgroup per CU
+    const int per_cu = (O + 255) / 256;
+    const int RT = ((per_cu + rpw - 1) / rpw) * rpw;
+    const bool fast = T * K <= MOE_FAST_MAX_TK && I % 32 == 0 && gs % 32 == 0 &&
+                      ((uintptr_t)w & 15) == 0 && (w_stride & 15) == 0 &&
+                      ((uintptr_t)x & 15) == 0 && moe_lds_bytes(T, K, I, RT) <= LDS_BUDGET;
+    if (fast) {
+        switch (lpr) {
+        case 64: return launch_t<64, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
+        case 32: return launch_t<32, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
+        case 16: return launch_t<16, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
+        case 8: return launch_t<8, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
+        default: return launch_t<4, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
+        }
+    }
+    const int wpb = 4;
+    hipLaunchKernelGGL(moe_i4g_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
+                       scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, err_flag);
+    return hipGetLastError();
+}
+
+}  // namespace qg

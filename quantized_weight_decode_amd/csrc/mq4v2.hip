@@ -1,0 +1,334 @@
+// mq4v2.hip -- MQ4-v2 GEMV, decode and the FWHT-256 pre-rotation for gfx950.
+//
+// Format (hipfire "MQ4 V2", sections 2 and 4): per row, I/256 groups of 136
+// bytes, little-endian.  Dword 0 = {fp16 scale, fp16 zero} of weights 0..127,
+// dword 1 = the pair of weights 128..255, bytes 8..135 = 128 payload bytes
+// with weight j in nibble j (low nibble first).  weight = q * scale + zero,
+// the half chosen from the weight's index (j >= 128), never from a lane id.
+//
+// Streaming kernel: the lane chunk is 16 payload bytes (32 weights), chunk
+// u = 8 g + p covers payload bytes 16p..16p+15 of group g, so half = (p >= 4)
+// follows from the chunk's own byte offset.  The chunk is fetched with one
+// 16-byte load at an 8-byte-aligned address (136 g + 8 + 16 p); the lane's
+// header dword (+0 or +4) is a separate 4-byte load that hits the same lines.
+// With x staged exactly as for grouped int4 (pre-scaled by 2^9, per-chunk
+// sums), acc += scale * sum(q x) + zero * sum(x): weight = q*scale + zero
+// reassociated.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+#ifndef QG_MQ4_R
+#define QG_MQ4_R 4
+#endif
+#ifndef QG_MQ4_PF
+#define QG_MQ4_PF 1
+#endif
+#ifndef QG_MQ4_WPB
+#define QG_MQ4_WPB 4
+#endif
+
+namespace qg {
+
+constexpr int MQ4_FAST_MAX_S = 4;
+constexpr int MQ4_GROUP_BYTES = 136;
+
+// 16 bytes at an 8-byte-aligned address.
+typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
+
+__device__ __forceinline__ u32x4 load16_a8(const uint8_t *p)
+{
+    const u32x4_a8 v = *reinterpret_cast<const u32x4_a8 *>(p);
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+
+template <int S, int LPR, int R, int PF>
+__global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
+    const uint8_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int I,
+    int O, int ntiles)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int NU = I / 32;
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NU]
+    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * NU);  // [S][NU]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane / LPR;
+    const int sl = lane % LPR;
+    const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+    const int row0 = tile * ROWS_PER_WAVE + sub * R;
+    const size_t rowbytes = (size_t)(I / 256) * MQ4_GROUP_BYTES;
+    const int nit = (NU + LPR - 1) / LPR;
+
+    const uint8_t *wr[R];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
+
+    XStage<S> xst;
+    xst.load(x, I, NU);
+
+    u32x4 wb[PF][R];
+    uint32_t hb[PF][R];
+#pragma unroll
+    for (int j = 0; j < PF; j++) {
+        if (j < nit) {
+            const int u = min(j * LPR + sl, NU - 1);
+            const int g = u >> 3, p = u & 7;
+            const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                wb[j][r] = load16_a8(wr[r] + goff + 8 + 16 * p);
+                hb[j][r] = *reinterpret_cast<const uint32_t *>(wr[r] + goff + (p >= 4 ? 4 : 0));
+            }
+        }
+    }
+
+    xst.store(x, I, NU, xl, xs);
+    __syncthreads();
+    if (tile >= ntiles) return;
+
+    float acc[S][R];
+#pragma unroll
+    for (int t = 0; t < S; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+
+    for (int c0 = 0; c0 < nit; c0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            const int c = c0 + j;
+            if (c < nit) {
+                const int u = c * LPR + sl;
+                const bool valid = u < NU;
+                const int uu = valid ? u : 0;
+                float scl[R], zro[R];
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    scl[r] = f16_to_f32(hb[j][r] & 0xFFFFu);
+                    zro[r] = f16_to_f32(hb[j][r] >> 16);
+                }
+#pragma unroll
+                for (int t = 0; t < S; t++) {
+                    const f32x4 *xt = xl + (size_t)t * 8 * NU;
+                    const float xsum = xs[(size_t)t * NU + uu];
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                        const float v = __builtin_fmaf(scl[r], p, zro[r] * xsum);
+                        acc[t][r] = valid ? acc[t][r] + v : acc[t][r];
+                    }
+                }
+                if (c + PF < nit) {
+                    const int un = min(u + PF * LPR, NU - 1);
+                    const int g = un >> 3, p = un & 7;
+                    const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        wb[j][r] = load16_a8(wr[r] + goff + 8 + 16 * p);
+                        hb[j][r] =
+                            *reinterpret_cast<const uint32_t *>(wr[r] + goff + (p >= 4 ? 4 : 0));
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < S; t++)
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const float v = sub_reduce<LPR>(acc[t][r]);
+            if (sl == LPR - 1 && row0 + r < O) y[(size_t)t * O + row0 + r] = v;
+        }
+}
+
+// General kernel: any alignment of w, S <= QGEMV_MAX_S.  One wave per row;
+// lane takes payload bytes; each weight decoded to f32 as fma(q, scale, zero).
+__global__ __launch_bounds__(256) void mq4v2_gemv_general(const uint8_t *__restrict__ w,
+                                                          const float *__restrict__ x,
+                                                          float *__restrict__ y, int S, int I,
+                                                          int O)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (row >= O) return;
+    const int G = I / 256;
+    const uint8_t *wr = w + (size_t)row * G * MQ4_GROUP_BYTES;
+    float acc[QGEMV_MAX_S];
+#pragma unroll
+    for (int t = 0; t < QGEMV_MAX_S; t++) acc[t] = 0.0f;
+    for (int k = lane; k < G * 128; k += WAVE) {     // payload byte k of the row
+        const int g = k >> 7, b = k & 127;
+        const uint8_t *gp = wr + (size_t)g * MQ4_GROUP_BYTES;
+        const int h = b >= 64 ? 4 : 0;
+        const uint32_t hd = (uint32_t)gp[h] | ((uint32_t)gp[h + 1] << 8) |
+                            ((uint32_t)gp[h + 2] << 16) | ((uint32_t)gp[h + 3] << 24);
+        const float scl = f16_to_f32(hd & 0xFFFFu), zro = f16_to_f32(hd >> 16);
+        float e[4], o[4];
+        nib8((uint32_t)gp[8 + b], e, o);
+        const float w0 = __builtin_fmaf(e[0] * NIB_XSCALE, scl, zro);
+        const float w1 = __builtin_fmaf(o[0] * NIB_XSCALE, scl, zro);
+        const int c0 = g * 256 + 2 * b;
+#pragma unroll
+        for (int t = 0; t < QGEMV_MAX_S; t++) {
+            if (t < S) {
+                const float *xt = x + (size_t)t * I;
+                acc[t] = __builtin_fmaf(w1, xt[c0 + 1], __builtin_fmaf(w0, xt[c0], acc[t]));
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < QGEMV_MAX_S; t++) {
+        if (t < S) {
+            const float v = sub_reduce<64>(acc[t]);
+            if (lane == 63) y[(size_t)t * O + row] = v;
+        }
+    }
+}
+
+// Decode-only: W[o][i] = fma(q, scale, zero) (exact q*scale, one rounding).
+__global__ __launch_bounds__(256) void mq4v2_dequant(const uint8_t *__restrict__ w,
+                                                     float *__restrict__ W, int I, int O)
+{
+    const int G = I / 256;
+    const size_t n = (size_t)O * G * 128;     // payload bytes
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const size_t og = idx >> 7;             // row * G + g
+        const int b = (int)(idx & 127);
+        const uint8_t *gp = w + og * MQ4_GROUP_BYTES;
+        const int h = b >= 64 ? 4 : 0;
+        const uint32_t hd = (uint32_t)gp[h] | ((uint32_t)gp[h + 1] << 8) |
+                            ((uint32_t)gp[h + 2] << 16) | ((uint32_t)gp[h + 3] << 24);
+        const float scl = f16_to_f32(hd & 0xFFFFu), zro = f16_to_f32(hd >> 16);
+        float e[4], o[4];
+        nib8((uint32_t)gp[8 + b], e, o);
+        const size_t o_row = og / G;
+        const int g = (int)(og - o_row * G);
+        float *dst = W + o_row * I + (size_t)g * 256 + 2 * b;
+        dst[0] = __builtin_fmaf(e[0] * NIB_XSCALE, scl, zro);
+        dst[1] = __builtin_fmaf(o[0] * NIB_XSCALE, scl, zro);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FWHT-256 pre-rotation: x_rot = (1/16) H256 (signs . x) per 256-element block,
+// H256 the Sylvester Hadamard matrix.  One wave per block; lane l holds
+// elements 4l..4l+3.  Radix-2 butterflies (a, b) -> (a + b, a - b) for
+// strides 1, 2, 4, ..., 128 in f32: strides 1 and 2 inside a lane, strides
+// 4..128 between lanes l and l ^ (stride/4).  The 1/16 is exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor_lane(float v, int m)
+{
+    return __shfl_xor(v, m, WAVE);
+}
+
+__global__ __launch_bounds__(256) void fwht256_kernel(const float *__restrict__ x,
+                                                      const int8_t *__restrict__ signs,
+                                                      float *__restrict__ xr, int I, int nblk)
+{
+    const int lane = threadIdx.x & 63;
+    const int blk = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (blk >= nblk) return;
+    const int nb = I / 256;
+    const int t = blk / nb, b = blk - t * nb;
+    const size_t off = (size_t)t * I + (size_t)b * 256 + 4 * lane;
+    const f32x4 xv = *reinterpret_cast<const f32x4 *>(x + off);
+    const int8_t *sg = signs + (size_t)b * 256 + 4 * lane;
+    float v[4] = {xv.x * (float)sg[0], xv.y * (float)sg[1], xv.z * (float)sg[2],
+                  xv.w * (float)sg[3]};
+    // stride 1
+    float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+    // stride 2
+    v[0] = a0 + a2; v[2] = a0 - a2; v[1] = a1 + a3; v[3] = a1 - a3;
+    // strides 4..128: partner lane l ^ m; the lane whose bit m is clear holds a
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float o = xor_lane(v[k], m);
+            v[k] = upper ? o - v[k] : v[k] + o;
+        }
+    }
+    f32x4 out = {v[0] * 0.0625f, v[1] * 0.0625f, v[2] * 0.0625f, v[3] * 0.0625f};
+    *reinterpret_cast<f32x4 *>(xr + off) = out;
+}
+
+namespace {
+
+size_t mq4_lds_bytes(int S, int I) { return (size_t)S * (I / 32) * (8 * sizeof(f32x4) + 4); }
+
+template <int S, int LPR, int R, int PF>
+hipError_t launch_t(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    const int wpb = QG_MQ4_WPB;
+    const int blocks = (ntiles + wpb - 1) / wpb;
+    const size_t lds = mq4_lds_bytes(S, I);
+    auto kern = mq4v2_gemv_stream<S, LPR, R, PF>;
+    hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * wpb), lds, st, w, x, y, I, O, ntiles);
+    return hipGetLastError();
+}
+
+template <int S>
+hipError_t launch_s(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
+{
+    constexpr int R = S <= 2 ? QG_MQ4_R : 2;
+    constexpr int PF = S <= 2 ? QG_MQ4_PF : 2;
+    switch (pick_lpr(I / 32)) {
+    case 64: return launch_t<S, 64, R, PF>(w, x, y, I, O, st);
+    case 32: return launch_t<S, 32, R, PF>(w, x, y, I, O, st);
+    case 16: return launch_t<S, 16, R, PF>(w, x, y, I, O, st);
+    default: return launch_t<S, 8, R, PF>(w, x, y, I, O, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int I, int O,
+                             hipStream_t st)
+{
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const bool fast = S <= MQ4_FAST_MAX_S && ((uintptr_t)w & 7) == 0 &&
+                      ((uintptr_t)x & 15) == 0 && mq4_lds_bytes(S, I) <= LDS_BUDGET;
+    if (fast) {
+        switch (S) {
+        case 1: return launch_s<1>(wb, x, y, I, O, st);
+        case 2: return launch_s<2>(wb, x, y, I, O, st);
+        case 3: return launch_s<3>(wb, x, y, I, O, st);
+        default: return launch_s<4>(wb, x, y, I, O, st);
+        }
+    }
+    const int wpb = 4;
+    hipLaunchKernelGGL(mq4v2_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
+                       x, y, S, I, O);
+    return hipGetLastError();
+}
+
+hipError_t launch_mq4v2_dequant(const void *w, float *W, int I, int O, hipStream_t st)
+{
+    const size_t n = (size_t)O * (I / 256) * 128;
+    const size_t want = (n + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(mq4v2_dequant, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(w), W, I, O);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwht256(const float *x, const int8_t *signs, float *xr, int S, int I,
+                          hipStream_t st)
+{
+    const int nblk = S * (I / 256);
+    const int wpb = 4;
+    hipLaunchKernelGGL(fwht256_kernel, dim3((nblk + wpb - 1) / wpb), dim3(64 * wpb), 0, st, x,
+                       signs, xr, I, nblk);
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -27,6 +27,16 @@ constexpr int WAVE = 64;
 // ---------------------------------------------------------------------------
 constexpr float NIB_XSCALE = 512.0f;  // 2^9
 
+// fp8 (OCP E4M3) pair conversion of bytes 0-1 / bytes 2-3 of a dword.
+__device__ __forceinline__ f32x2 fp8pair_lo(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+__device__ __forceinline__ f32x2 fp8pair_hi(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+}
+
 // Decodes the 8 nibbles of one little-endian packed dword.
 //   e[0..3] = nibbles of bytes 0..3 low halves  (columns 0, 2, 4, 6)
 //   o[0..3] = nibbles of bytes 0..3 high halves (columns 1, 3, 5, 7)
@@ -35,10 +45,10 @@ __device__ __forceinline__ void nib8(uint32_t w, float e[4], float o[4])
 {
     const uint32_t lo = w & 0x0F0F0F0Fu;
     const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    const f32x2 a = fp8pair_lo(lo);
+    const f32x2 b = fp8pair_hi(lo);
+    const f32x2 c = fp8pair_lo(hi);
+    const f32x2 d = fp8pair_hi(hi);
     e[0] = a.x; e[1] = a.y; e[2] = b.x; e[3] = b.y;
     o[0] = c.x; o[1] = c.y; o[2] = d.x; o[3] = d.y;
 }
@@ -46,8 +56,8 @@ __device__ __forceinline__ void nib8(uint32_t w, float e[4], float o[4])
 // Four E4M3 codes of a dword (byte k = column k) as floats, exactly.
 __device__ __forceinline__ void e4m3x4(uint32_t w, float v[4])
 {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    const f32x2 a = fp8pair_lo(w);
+    const f32x2 b = fp8pair_hi(w);
     v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
 }
 
@@ -80,6 +90,26 @@ __device__ __forceinline__ float sub_reduce8(float v);
 // per thread into registers (call it before issuing the weight stream, so the
 // in-order wait for them never waits for weights); store() writes them and
 // stages any remainder.  blockDim.x must be a multiple of 64.
+// Places float4 number f of the activations (vector t = f / (8 NU)) into the
+// LDS layout and adds its part of the chunk sum (8 consecutive lanes hold one
+// chunk; all 8 must be active).
+__device__ __forceinline__ void XStagePut(f32x4 a, int f, int NU, f32x4 *__restrict__ xl,
+                                          float *__restrict__ xs)
+{
+    const int cpv = NU * 8;                  // float4s per vector
+    const int t = f / cpv;
+    const int rem = f - t * cpv;
+    const int u = rem >> 3, k = rem & 7;
+    const int d = k >> 1, h = k & 1;
+    float *base = reinterpret_cast<float *>(xl + (size_t)t * 8 * NU);
+    f32x2 ev = {a.x * NIB_XSCALE, a.z * NIB_XSCALE};
+    f32x2 od = {a.y * NIB_XSCALE, a.w * NIB_XSCALE};
+    *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d) * NU + u) * 4 + 2 * h) = ev;
+    *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d + 1) * NU + u) * 4 + 2 * h) = od;
+    const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
+    if (k == 7) xs[(size_t)t * NU + u] = cs;
+}
+
 template <int S>
 struct XStage {
     static constexpr int NPRE = 8;
@@ -100,18 +130,7 @@ struct XStage {
     __device__ __forceinline__ static void put(f32x4 a, int f, int NU, f32x4 *__restrict__ xl,
                                                float *__restrict__ xs)
     {
-        const int cpv = NU * 8;                  // float4s per vector
-        const int t = f / cpv;
-        const int rem = f - t * cpv;
-        const int u = rem >> 3, k = rem & 7;
-        const int d = k >> 1, h = k & 1;
-        float *base = reinterpret_cast<float *>(xl + (size_t)t * 8 * NU);
-        f32x2 ev = {a.x * NIB_XSCALE, a.z * NIB_XSCALE};
-        f32x2 od = {a.y * NIB_XSCALE, a.w * NIB_XSCALE};
-        *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d) * NU + u) * 4 + 2 * h) = ev;
-        *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d + 1) * NU + u) * 4 + 2 * h) = od;
-        const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
-        if (k == 7) xs[(size_t)t * NU + u] = cs;
+        XStagePut(a, f, NU, xl, xs);
     }
 
     __device__ __forceinline__ void store(const float *__restrict__ x, int I, int NU,

@@ -12,6 +12,21 @@ namespace qg {
 // LDS a workgroup may ask for on gfx950 (160 KiB per CU).
 constexpr size_t LDS_BUDGET = 160 * 1024;
 
+// Lanes per row for a row of `nchunks` 16-byte lane chunks: the widest of
+// 64/32/16/8/4 lanes whose sweeps leave the fewest lanes idle.
+inline int pick_lpr(int nchunks)
+{
+    const int opts[] = {64, 32, 16, 8, 4};
+    int best = 4;
+    double best_eff = -1.0;
+    for (int lpr : opts) {
+        const int it = (nchunks + lpr - 1) / lpr;
+        const double eff = (double)nchunks / ((double)it * lpr);
+        if (eff > best_eff + 1e-9) { best_eff = eff; best = lpr; }
+    }
+    return best;
+}
+
 // Raises a kernel's dynamic-LDS limit to `bytes` once (cached per kernel).
 hipError_t set_max_lds(const void *kernel, size_t bytes);
 
@@ -22,5 +37,25 @@ hipError_t launch_i4g_gemv(const void *w, const float *scales, const float *x, f
                            int S, int I, int O, int gs, hipStream_t st);
 hipError_t launch_i4g_dequant(const void *w, const float *scales, float *W, int I, int O,
                               int gs, hipStream_t st);
+
+// fp8-e4m3, 128x128 block scales
+hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const float *x, float *y,
+                               int S, int I, int O, hipStream_t st);
+hipError_t launch_fp8b128_dequant(const void *w, const float *scale_inv, float *W, int I, int O,
+                                  hipStream_t st);
+
+// MQ4-v2 and the FWHT-256 rotation
+hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int I, int O,
+                             hipStream_t st);
+hipError_t launch_mq4v2_dequant(const void *w, float *W, int I, int O, hipStream_t st);
+hipError_t launch_fwht256(const float *x, const int8_t *signs, float *xr, int S, int I,
+                          hipStream_t st);
+
+// routed experts
+constexpr size_t MOE_WORKSPACE_BYTES = 256;
+hipError_t launch_moe_topk(const void *w, const float *scales, long long w_stride,
+                           long long s_stride, int E, const int32_t *ids, const float *gates,
+                           int T, int K, const float *x, float *y, int I, int O, int gs,
+                           int *err_flag, hipStream_t st);
 
 }  // namespace qg

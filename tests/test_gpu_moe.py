@@ -1,0 +1,79 @@
+"""Routed-expert GEMV on the GPU against the CPU oracle.
+
+y[t] = sum_k gates[t][k] * W_{ids[t][k]} x[t] over grouped-int4 experts
+(regolith audit, section 2.2; colibri PR #457, section 4).  Includes the
+workload shape (256 experts of 2048x7168, gs 64, 4 tokens, top-8) checked on
+sampled rows, duplicate ids, an out-of-range id (NaN row plus the error
+flag) and the general kernel (T*K > 64, odd I).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_y_close, dev, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    torch_cuda()
+    import quantized_weight_decode_amd as q
+    return q
+
+
+def run(q, d):
+    ws = q.moe_topk_workspace(d["T"], d["K"], d["O"], "cuda")
+    y = q.moe_topk(dev(d["w"]), dev(d["scales"]), dev(d["ids"]), dev(d["gates"]), dev(d["x"]),
+                   d["gs"], workspace=ws)
+    return host(y), q.moe_topk_error(ws)
+
+
+def oracle_y(qref, d, rows=None):
+    return qref.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], d["E"], d["O"],
+                        d["I"], d["gs"], rows=rows)
+
+
+@pytest.mark.parametrize("E,O,I,gs,T,K", [
+    (16, 256, 512, 64, 4, 8), (32, 300, 1024, 64, 2, 4), (8, 77, 7168, 64, 4, 2),
+    (12, 40, 256, 128, 1, 1), (64, 512, 2048, 32, 8, 8), (6, 100, 2048, 64, 3, 6),
+])
+def test_matches_oracle(q, qref, E, O, I, gs, T, K):
+    d = W.gen_moe(E, O, I, gs, T, K, seed=E + O)
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))
+
+
+def test_workload_shape_sampled_rows(q, qref):
+    d = W.gen_moe(256, 2048, 7168, 64, 4, 8, seed=0)
+    y, err = run(q, d)
+    assert err == 0
+    rows = np.random.default_rng(0).choice(2048, 96, replace=False)
+    rows = np.concatenate([rows, [0, 1, 2047]])
+    assert_y_close(y[:, rows], oracle_y(qref, d, rows=rows))
+
+
+def test_duplicate_ids_count_per_occurrence(q, qref):
+    d = W.gen_moe(10, 64, 512, 64, 3, 4, seed=9)
+    d["ids"][1] = [5, 5, 2, 5]
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))
+
+
+def test_out_of_range_id(q, qref):
+    d = W.gen_moe(10, 64, 512, 64, 3, 4, seed=10)
+    d["ids"][2, 1] = 10
+    y, err = run(q, d)
+    assert err == 1
+    assert np.isnan(y[2]).all() and np.isfinite(y[:2]).all()
+    assert_y_close(y[:2], oracle_y(qref, d)[:2])
+
+
+@pytest.mark.parametrize("E,O,I,gs,T,K", [(50, 50, 201, 64, 2, 40), (5, 30, 300, 16, 2, 3)])
+def test_general_kernel(q, qref, E, O, I, gs, T, K):
+    d = W.gen_moe(E, O, I, gs, T, K, seed=O)
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))

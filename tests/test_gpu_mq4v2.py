@@ -1,0 +1,94 @@
+"""MQ4-v2 GEMV and the FWHT-256 rotation on the GPU against the CPU oracle.
+
+hipfire "MQ4 V2" page: sections 2 and 4 (layout, w = q*scale + zero, the half
+chosen by weight index) and section 1e (a discriminating fixture).  The
+rotation is the orthonormal Sylvester FWHT-256 with signs applied first
+(the reading stated in the oracle); the GPU does radix-2 butterflies in f32,
+so x_rot is compared with a tolerance: relative L2 <= 1e-6 per call (eight
+rounding stages of 2^-24).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_bits_equal, assert_y_close, dev, host, rel_l2, torch_cuda
+from test_oracle_mq4v2 import handbuilt_fixture
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    torch_cuda()
+    import quantized_weight_decode_amd as q
+    return q
+
+
+def test_handbuilt_fixture_decodes_exactly(q, qref):
+    w, checks = handbuilt_fixture()
+    got = host(q.dequant_mq4v2(dev(w.reshape(1, -1)), 512))[0]
+    assert_bits_equal(got, qref.mq4v2_dequant(w, 1, 512)[0])
+    for i, v in checks:
+        assert got[i] == v
+
+
+@pytest.mark.parametrize("O,I", [(9, 768), (64, 8192), (3, 256)])
+def test_dequant_bit_exact(q, qref, O, I):
+    d = W.gen_mq4v2(O, I, seed=O)
+    got = host(q.dequant_mq4v2(dev(d["w"].reshape(O, -1)), I))
+    assert_bits_equal(got, qref.mq4v2_dequant(d["w"], O, I))
+
+
+@pytest.mark.parametrize("O,I,S", [
+    (8192, 8192, 1),          # workload shape (GEMV on the rotated x)
+    (256, 512, 1), (300, 1024, 2), (77, 256, 3), (1000, 4096, 4), (33, 2304, 1),
+    (5, 768, 8), (1, 256, 1),
+])
+def test_gemv_matches_oracle(q, qref, O, I, S):
+    d = W.gen_mq4v2(O, I, S=S, seed=O + 7)
+    y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), dev(d["x"])))
+    assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I))
+
+
+def test_unaligned_rows_take_general_path(q, qref):
+    import torch
+    O, I = 12, 512
+    d = W.gen_mq4v2(O, I, seed=2)
+    buf = torch.zeros(d["w"].size + 4, dtype=torch.uint8, device="cuda")
+    buf[4:] = dev(d["w"].reshape(-1))
+    x = dev(d["x"])
+    y = torch.empty((1, O), device="cuda")
+    st = q.qgemv_mq4v2(buf[4:].data_ptr(), x.data_ptr(), y.data_ptr(), 1, I, O,
+                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert_y_close(host(y), qref.mq4v2_gemv(d["w"], d["x"], O, I))
+
+
+@pytest.mark.parametrize("S,I", [(1, 8192), (3, 512), (8, 256)])
+def test_fwht_matches_oracle(q, qref, S, I):
+    rng = np.random.default_rng(S + I)
+    x = rng.standard_normal((S, I)).astype(np.float32)
+    sg = W.gen_fwht_signs(I)
+    got = host(q.fwht256(dev(x), dev(sg)))
+    ref = qref.fwht256(x, sg, I)
+    assert rel_l2(got, ref) <= 1e-6
+    assert np.max(np.abs(got - ref)) <= 1e-6 * np.abs(ref).max()
+
+
+def test_fwht_in_place(q, qref):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 512)).astype(np.float32)
+    sg = W.gen_fwht_signs(512)
+    xd = dev(x)
+    q.fwht256(xd, dev(sg), out=xd)
+    assert rel_l2(host(xd), qref.fwht256(x, sg, 512)) <= 1e-6
+
+
+def test_rotate_then_gemv_end_to_end(q, qref):
+    """The MQ4 workload path: x -> FWHT-256 rotation -> MQ4-v2 GEMV."""
+    O, I = 2048, 8192
+    d = W.gen_mq4v2(O, I, seed=0)
+    xr = q.fwht256(dev(d["x"]), dev(d["signs"]))
+    y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), xr))
+    ref = qref.mq4v2_gemv(d["w"], qref.fwht256(d["x"], d["signs"], I), O, I)
+    assert_y_close(y, ref)
