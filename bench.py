@@ -1,18 +1,27 @@
 #!/usr/bin/env python3
 """Batch-1 quantized-weight GEMV benchmark on one MI355X.
 
-A step is one pass of the hot path over one batch: for the grouped-int4
-resident projection (O=12288, I=6144, gs=64, one activation vector) one
-qgemv_i4g call.  Steps rotate through distinct weight copies totalling over
-1 GiB so that every call streams its weights from HBM, not from the 256 MB
-last-level cache.  Inputs are resident in HBM before timing starts.
+A step is one pass of the hot path over one batch of synthetic input:
 
-Prints one JSON line:
-  value            algorithmic bytes moved per second (GB/s) over the timed
-                   region (K steps between two events on the launch stream)
-  roofline         the GEMV kernel's algorithmic bytes / its average launch
-                   duration against the 8 TB/s HBM peak
-  cpu_baseline     the CPU oracle on a bounded sample of the same workload
+  i4g_O12288_I6144_gs64 (default), i4g_O12288_I6144_gs128:
+      one qgemv_i4g call (grouped int4, one activation vector)
+  fp8b128_O7168_I16384:
+      one qgemv_fp8b128 call
+  mq4v2_O8192_I8192:
+      qgemv_fwht256 (rotate x) then qgemv_mq4v2
+  moe_E256_O2048_I7168_gs64_T4_K8:
+      one qgemv_moe_topk call (4 tokens, top-8 of 256 experts)
+
+Dense steps rotate through distinct weight copies totalling over 1 GiB, and
+the routed-expert step cycles through 16 seeded routings over one resident
+2.1 GB expert stack, so calls stream their weights from HBM rather than the
+256 MB last-level cache.  All inputs are resident in HBM before timing.
+
+Prints one JSON line.  `value` is the algorithmic bytes of K steps divided by
+the time between two HIP events bracketing them on the launch stream;
+`roofline.achieved` is the same for the dominant (GEMV) kernel timed alone.
+`--copy-calibrate` instead runs a plain device-to-device copy of known size
+(used to scale the HBM traffic counters).
 """
 from __future__ import annotations
 
@@ -29,62 +38,298 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DENSE_27B = 27e9   # weights of the dense decode fixture the tok/s figure is scaled to
+ROTATE_BYTES = 1 << 30
+METRIC = "achieved HBM GB/s (% of MI355X peak) + equiv decode tok/s, batch-1 qGEMV"
 
 
-def i4g_case(O, I, gs):
-    rb = (I + 1) // 2
-    ng = (I + gs - 1) // gs
-    wbytes = O * rb + O * ng * 4          # packed nibbles + f32 scales
-    total = wbytes + I * 4 + O * 4        # + x + y
-    return {"workload": f"i4g_O{O}_I{I}_gs{gs}", "fmt": "i4g", "O": O, "I": I, "gs": gs,
-            "weight_bytes": wbytes, "alg_bytes": total,
-            "bytes_per_weight": wbytes / (O * I)}
+def n_copies(bytes_per_copy):
+    return max(2, int(np.ceil(ROTATE_BYTES / bytes_per_copy)))
 
 
-CASES = {
-    "i4g_O12288_I6144_gs64": lambda: i4g_case(12288, 6144, 64),
-    "i4g_O12288_I6144_gs128": lambda: i4g_case(12288, 6144, 128),
-}
+class Case:
+    """A workload: builds device inputs, runs one step, checks parity."""
+    name = ""
+    kernel = ""            # name fragment of the dominant kernel
+    fmt_desc = ""
+
+    def step(self, i):
+        raise NotImplementedError
+
+    def gemv_only(self, i):
+        self.step(i)
 
 
-def make_copies(case, n_copies, torch, dev):
-    """Copy 0 from the seeded generator (checked against the oracle); the rest
-    are distinct seeded draws made on the device, same distributions."""
-    import workloads as W
-    O, I, gs = case["O"], case["I"], case["gs"]
-    d = W.gen_i4g(O, I, gs, seed=0)
-    ws = [torch.from_numpy(d["w"]).to(dev)]
-    ss = [torch.from_numpy(d["scales"]).to(dev)]
-    g = torch.Generator(device=dev)
-    g.manual_seed(1)
-    for _ in range(1, n_copies):
-        ws.append(torch.randint(0, 256, d["w"].shape, dtype=torch.uint8, device=dev, generator=g))
-        ss.append((0.002 + 0.018 * torch.rand(d["scales"].shape, device=dev, generator=g)).float())
-    x = torch.from_numpy(d["x"]).to(dev)
-    return d, ws, ss, x
+def _check(rel, what):
+    if not rel <= 1e-5:
+        raise SystemExit(f"bench: {what}: GPU result disagrees with the oracle (rel L2 {rel:.3e})")
 
 
-def cpu_baseline(case, d, budget_s=12.0):
-    """The oracle as it stands, on all host cores (OpenMP over rows)."""
+def _rel(got, ref):
+    return float(np.linalg.norm(got.astype(np.float64) - ref) / np.linalg.norm(ref))
+
+
+class I4G(Case):
+    kernel = "i4g_gemv_stream"
+
+    def __init__(self, O, I, gs, torch, q, o):
+        import workloads as W
+        self.name = f"i4g_O{O}_I{I}_gs{gs}"
+        self.fmt_desc = "grouped int4, f32 scale per group"
+        self.O, self.I, self.gs = O, I, gs
+        rb, ng = (I + 1) // 2, (I + gs - 1) // gs
+        self.weight_bytes = O * rb + O * ng * 4
+        self.alg_bytes = self.weight_bytes + I * 4 + O * 4
+        self.bytes_per_weight = self.weight_bytes / (O * I)
+        dev = torch.device("cuda:0")
+        d = W.gen_i4g(O, I, gs, seed=0)
+        self.n = n_copies(self.weight_bytes)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        self.ws = [torch.from_numpy(d["w"]).to(dev)]
+        self.ss = [torch.from_numpy(d["scales"]).to(dev)]
+        for _ in range(1, self.n):
+            self.ws.append(torch.randint(0, 256, d["w"].shape, dtype=torch.uint8, device=dev,
+                                         generator=g))
+            self.ss.append(0.002 + 0.018 * torch.rand(d["scales"].shape, device=dev, generator=g))
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        self.y = torch.empty((1, O), dtype=torch.float32, device=dev)
+        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
+        self.step(0)
+        self.rel = _rel(self.y.cpu().numpy(), o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
+        _check(self.rel, self.name)
+        self.cpu = lambda: o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs)
+
+    def step(self, i):
+        wp, spp = self.ptrs[i % self.n]
+        st = self.q.qgemv_i4g(wp, spp, self.x.data_ptr(), self.y.data_ptr(), 1, self.I, self.O,
+                              self.gs, self.sp)
+        if st:
+            raise SystemExit(f"qgemv_i4g: {self.q.strerror(st)}")
+
+
+class FP8(Case):
+    kernel = "fp8_gemv_stream"
+
+    def __init__(self, O, I, torch, q, o):
+        import workloads as W
+        self.name = f"fp8b128_O{O}_I{I}"
+        self.fmt_desc = "fp8 e4m3, f32 scale per 128x128 block"
+        self.O, self.I = O, I
+        nbo, nbi = W.fp8_nblocks(O, I)
+        self.weight_bytes = O * I + nbo * nbi * 4
+        self.alg_bytes = self.weight_bytes + I * 4 + O * 4
+        self.bytes_per_weight = self.weight_bytes / (O * I)
+        dev = torch.device("cuda:0")
+        d = W.gen_fp8b128(O, I, seed=0)
+        self.n = n_copies(self.weight_bytes)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        self.ws = [torch.from_numpy(d["w"]).to(dev)]
+        self.ss = [torch.from_numpy(d["scale_inv"]).to(dev)]
+        for _ in range(1, self.n):
+            # uniform over the 254 non-NaN codes: v in 0..253 -> v + (v >= 0x7F)
+            v = torch.randint(0, 254, (O, I), dtype=torch.uint8, device=dev, generator=g)
+            self.ws.append(v + (v >= 0x7F).to(torch.uint8))
+            self.ss.append(torch.exp(np.log(1e-4) + (np.log(1e-2) - np.log(1e-4)) *
+                                     torch.rand((nbo, nbi), device=dev, generator=g)))
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        self.y = torch.empty((1, O), dtype=torch.float32, device=dev)
+        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
+        self.step(0)
+        self.rel = _rel(self.y.cpu().numpy(), o.fp8b128_gemv(d["w"], d["scale_inv"], d["x"], O, I))
+        _check(self.rel, self.name)
+        self.cpu = lambda: o.fp8b128_gemv(d["w"], d["scale_inv"], d["x"], O, I)
+
+    def step(self, i):
+        wp, spp = self.ptrs[i % self.n]
+        st = self.q.qgemv_fp8b128(wp, spp, self.x.data_ptr(), self.y.data_ptr(), 1, self.I,
+                                  self.O, self.sp)
+        if st:
+            raise SystemExit(f"qgemv_fp8b128: {self.q.strerror(st)}")
+
+
+class MQ4(Case):
+    kernel = "mq4v2_gemv_stream"
+
+    def __init__(self, O, I, torch, q, o):
+        import workloads as W
+        self.name = f"mq4v2_O{O}_I{I}"
+        self.fmt_desc = "MQ4-v2 136 B / 256 weights, FWHT-256 rotated activations"
+        self.O, self.I = O, I
+        self.weight_bytes = O * (I // 256) * 136
+        # step: FWHT (x, signs in; x_rot out) + GEMV (weights, x_rot in; y out)
+        self.gemv_bytes = self.weight_bytes + I * 4 + O * 4
+        self.alg_bytes = self.gemv_bytes + I * 4 + I + I * 4
+        self.bytes_per_weight = self.weight_bytes / (O * I)
+        dev = torch.device("cuda:0")
+        d = W.gen_mq4v2(O, I, seed=0)
+        self.n = n_copies(self.weight_bytes)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        w0 = torch.from_numpy(d["w"].reshape(O, -1)).to(dev)
+        self.ws = [w0]
+        for _ in range(1, self.n):
+            # another draw: fresh payload, headers from copy 0 with their
+            # scale/zero halves re-paired at random (same value ranges)
+            w = w0.clone()
+            pay = torch.randint(0, 256, (O, I // 256, 128), dtype=torch.uint8, device=dev,
+                                generator=g)
+            w.view(O, I // 256, 136)[:, :, 8:] = pay
+            perm = torch.randperm(O, device=dev, generator=g)
+            w.view(O, I // 256, 136)[:, :, :8] = w0.view(O, I // 256, 136)[perm, :, :8]
+            self.ws.append(w)
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        self.signs = torch.from_numpy(d["signs"]).to(dev)
+        self.xr = torch.empty_like(self.x)
+        self.y = torch.empty((1, O), dtype=torch.float32, device=dev)
+        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.ptrs = [w.data_ptr() for w in self.ws]
+        self.step(0)
+        ref = o.mq4v2_gemv(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
+        self.rel = _rel(self.y.cpu().numpy(), ref)
+        _check(self.rel, self.name)
+        self.cpu = lambda: o.mq4v2_gemv(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
+
+    def step(self, i):
+        q = self.q
+        st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(), 1,
+                             self.I, self.sp)
+        st = st or q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), 1,
+                                 self.I, self.O, self.sp)
+        if st:
+            raise SystemExit(f"mq4v2 step: {q.strerror(st)}")
+
+    def gemv_only(self, i):
+        st = self.q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), 1,
+                                self.I, self.O, self.sp)
+        if st:
+            raise SystemExit(f"qgemv_mq4v2: {self.q.strerror(st)}")
+
+
+class MoE(Case):
+    kernel = "moe_i4g_stream"
+    N_ROUTINGS = 16
+
+    def __init__(self, E, O, I, gs, T, K, torch, q, o):
+        import workloads as W
+        self.name = f"moe_E{E}_O{O}_I{I}_gs{gs}_T{T}_K{K}"
+        self.fmt_desc = "routed grouped-int4 experts, gate-weighted top-k sum"
+        self.E, self.O, self.I, self.gs, self.T, self.K = E, O, I, gs, T, K
+        rb, ng = (I + 1) // 2, (I + gs - 1) // gs
+        self.expert_bytes = O * rb + O * ng * 4
+        self.bytes_per_weight = self.expert_bytes / (O * I)
+        dev = torch.device("cuda:0")
+        d = W.gen_moe(E, O, I, gs, T, K, seed=0)
+        self.w = torch.from_numpy(d["w"]).to(dev)
+        self.s = torch.from_numpy(d["scales"]).to(dev)
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        self.y = torch.empty((T, O), dtype=torch.float32, device=dev)
+        self.ws_buf = q.moe_topk_workspace(T, K, O, dev)
+        self.routings = []
+        uniq = []
+        for r in range(self.N_ROUTINGS):
+            ids, gates = (d["ids"], d["gates"]) if r == 0 else W.gen_moe_routing(E, T, K, 1000 + r)
+            self.routings.append((torch.from_numpy(ids).to(dev), torch.from_numpy(gates).to(dev)))
+            uniq.append(len(np.unique(ids)))
+        self.uniq = uniq
+        small = T * I * 4 + T * O * 4 + T * K * 8
+        self.alg_bytes_per_routing = [u * self.expert_bytes + small for u in uniq]
+        self.alg_bytes = float(np.mean(self.alg_bytes_per_routing))
+        self.weight_bytes = float(np.mean(uniq)) * self.expert_bytes
+        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.step(0)
+        rows = np.random.default_rng(0).choice(O, 64, replace=False)
+        ref = o.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], E, O, I, gs, rows=rows)
+        self.rel = _rel(self.y.cpu().numpy()[:, rows], ref)
+        _check(self.rel, self.name)
+        self.cpu_rows = rows
+        self.cpu = lambda: o.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], E, O, I,
+                                     gs, rows=rows)
+
+    def step(self, i):
+        ids, gates = self.routings[i % self.N_ROUTINGS]
+        st = self.q.qgemv_moe_topk(self.w.data_ptr(), self.s.data_ptr(), self.w[0].numel(),
+                                   self.s[0].numel(), self.E, ids.data_ptr(), gates.data_ptr(),
+                                   self.T, self.K, self.x.data_ptr(), self.y.data_ptr(), self.I,
+                                   self.O, self.gs, self.ws_buf.data_ptr(), self.ws_buf.numel(),
+                                   self.sp)
+        if st:
+            raise SystemExit(f"qgemv_moe_topk: {self.q.strerror(st)}")
+
+    def bytes_for(self, first, k):
+        n = self.N_ROUTINGS
+        return sum(self.alg_bytes_per_routing[(first + i) % n] for i in range(k))
+
+
+def build_case(name, torch, q, o):
+    table = {
+        "i4g_O12288_I6144_gs64": lambda: I4G(12288, 6144, 64, torch, q, o),
+        "i4g_O12288_I6144_gs128": lambda: I4G(12288, 6144, 128, torch, q, o),
+        "fp8b128_O7168_I16384": lambda: FP8(7168, 16384, torch, q, o),
+        "mq4v2_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o),
+        "moe_E256_O2048_I7168_gs64_T4_K8": lambda: MoE(256, 2048, 7168, 64, 4, 8, torch, q, o),
+        "i4g_O256_I512_gs64": lambda: I4G(256, 512, 64, torch, q, o),
+    }
+    return table[name]()
+
+
+CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_I16384",
+              "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64"]
+
+
+def timed(torch, fn, first, k):
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(k):
+        fn(first + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)  # ms
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The oracle as it stands, on the host's cores (OpenMP over rows)."""
     import oracle
     o = oracle.load()
     cores = min(os.cpu_count() or 1, 16)
     o.set_threads(cores)
-    O, I, gs = case["O"], case["I"], case["gs"]
-    o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs)  # warm-up
+    case.cpu()  # warm-up
     n = 0
     t0 = time.perf_counter()
     while True:
-        o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs)
+        case.cpu()
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     o.set_threads(1)
-    return {"value": case["alg_bytes"] * n / el / 1e9, "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{n} full GEMVs of {case['workload']} in {el:.1f} s "
-                      f"({el / n * 1e3:.1f} ms each, f64 accumulate)"}
+    if isinstance(case, MoE):
+        frac = len(case.cpu_rows) / case.O
+        per_call = case.alg_bytes_per_routing[0] * frac
+        sample = (f"{n} routed-expert calls restricted to {len(case.cpu_rows)} of {case.O} output "
+                  f"rows (routing seed 0) in {el:.1f} s")
+    else:
+        per_call = case.alg_bytes
+        sample = f"{n} full GEMVs of {case.name} in {el:.1f} s ({el / n * 1e3:.1f} ms each)"
+    return {"value": round(per_call * n / el / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "sample": sample + ", f64 accumulate"}
+
+
+def copy_calibrate(torch, nbytes, steps):
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    ms = timed(torch, lambda i: b.copy_(a), 0, steps)
+    print(json.dumps({"copy_calibrate_bytes": nbytes, "steps": steps,
+                      "ms_per_copy": ms / steps,
+                      "GBs_read_plus_write": 2 * nbytes / (ms / steps * 1e-3) / 1e9}), flush=True)
 
 
 def main():
@@ -92,79 +337,66 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--case", default="i4g_O12288_I6144_gs64", choices=sorted(CASES))
-    ap.add_argument("--copies-gib", type=float, default=1.0,
-                    help="total size of the rotated weight copies")
+    ap.add_argument("--case", default="i4g_O12288_I6144_gs64", choices=CASE_NAMES)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only time a plain device copy of BYTES bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the row-sharded multi-GPU layout is described in DESIGN.md)", file=sys.stderr)
+              f"(how the path would shard across GPUs is described in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
     import torch
-    import quantized_weight_decode_amd as q
+    if args.copy_calibrate:
+        copy_calibrate(torch, args.copy_calibrate, args.steps)
+        return
+
     import oracle
+    import quantized_weight_decode_amd as q
 
-    dev = torch.device("cuda:0")
-    case = CASES[args.case]()
-    per_copy = case["weight_bytes"]
-    n_copies = max(2, int(np.ceil(args.copies_gib * (1 << 30) / per_copy)))
-    d, ws, ss, x = make_copies(case, n_copies, torch, dev)
-    O, I, gs = case["O"], case["I"], case["gs"]
-    y = torch.empty((1, O), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-
-    # correctness of the timed configuration: copy 0 against the oracle
-    q.i4g(ws[0], ss[0], x, gs, out=y)
-    ref = oracle.load().i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs)
-    got = y.cpu().numpy()
-    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    if not rel <= 1e-5:
-        raise SystemExit(f"bench: GPU result disagrees with the oracle (rel L2 {rel:.3e})")
-
-    ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(ws, ss)]
-    xp, yp = x.data_ptr(), y.data_ptr()
-
-    def step(i):
-        wp, spp = ptrs[i % n_copies]
-        st = q.qgemv_i4g(wp, spp, xp, yp, 1, I, O, gs, sp)
-        if st:
-            raise SystemExit(f"qgemv_i4g failed: {q.strerror(st)}")
-
+    case = build_case(args.case, torch, q, oracle.load())
     for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+        case.step(i)
+    ms = timed(torch, case.step, args.warmup, args.steps)
+    ms_step = ms / args.steps
+    if isinstance(case, MoE):
+        step_bytes = case.bytes_for(args.warmup, args.steps) / args.steps
+    else:
+        step_bytes = case.alg_bytes
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
 
-    gbs = case["alg_bytes"] / (ms * 1e-3) / 1e9
-    wgbs = case["weight_bytes"] / (ms * 1e-3) / 1e9
+    # dominant kernel alone (identical to the step for single-kernel steps)
+    if isinstance(case, MQ4):
+        kms = timed(torch, case.gemv_only, 0, args.steps) / args.steps
+        kbytes = case.gemv_bytes
+    else:
+        kms, kbytes = ms_step, step_bytes
+    kgbs = kbytes / (kms * 1e-3) / 1e9
+    wgbs = case.weight_bytes / (kms * 1e-3) / 1e9
+
     out = {
-        "metric": "achieved HBM GB/s (% of MI355X peak) + equiv decode tok/s, batch-1 qGEMV",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": case["workload"], "batch": 1, "format": "grouped int4, f32 scales",
-                   "rotated_copies": n_copies, "alg_bytes_per_step": case["alg_bytes"]},
+        "config": {"workload": case.name, "batch": 1, "format": case.fmt_desc,
+                   "alg_bytes_per_step": round(step_bytes)},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "weights_gbs": round(wgbs, 1),
-        "equiv_decode_tok_s": round(wgbs * 1e9 / (DENSE_27B * case["bytes_per_weight"]), 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-        "parity_rel_l2": rel,
+        "equiv_decode_tok_s": round(wgbs * 1e9 / (DENSE_27B * case.bytes_per_weight), 1),
+        "roofline": {"bound": "hbm", "kernel": case.kernel, "achieved": round(kgbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "us_per_launch": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes),
+                     "traffic": None},
+        "parity_rel_l2": case.rel,
     }
+    if isinstance(case, MoE):
+        out["config"]["distinct_experts_per_routing"] = case.uniq
+        out["tokens_per_s"] = round(case.T / (ms_step * 1e-3), 1)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(case, d)
+        out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)
 
 

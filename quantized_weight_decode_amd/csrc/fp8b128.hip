@@ -17,55 +17,53 @@
 #include "qg_launch.h"
 
 #ifndef QG_FP8_R
-#define QG_FP8_R 4
+#define QG_FP8_R 1
 #endif
 #ifndef QG_FP8_PF
-#define QG_FP8_PF 2
+#define QG_FP8_PF 4
 #endif
 #ifndef QG_FP8_WPB
-#define QG_FP8_WPB 4
+#define QG_FP8_WPB 8
 #endif
 
 namespace qg {
 
 constexpr int FP8_FAST_MAX_S = 4;
 
-// Stages S vectors into the fp8 LDS layout with coalesced float4 loads.
-template <int S>
+// Stages up to 8 vectors into the fp8 LDS layout with coalesced float4 loads;
+// as XStageN, the first NPRE float4s per thread are loaded unconditionally
+// (indices clamped) so later waits count exactly.
+template <int NPRE>
 struct XStageF8 {
-    static constexpr int NPRE = 8;
     f32x4 v[NPRE];
 
-    __device__ __forceinline__ void load(const float *__restrict__ x, int NU)
+    __device__ __forceinline__ void load(const float *__restrict__ x, int total)
     {
-        const int total = S * NU * 4;
-        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
 #pragma unroll
-        for (int j = 0; j < NPRE; j++) {
-            const int f = threadIdx.x + j * blockDim.x;
-            if (f < total) v[j] = x4[f];
-        }
+        for (int j = 0; j < NPRE; j++)
+            v[j] = ldx4(x, (uint32_t)min((int)(threadIdx.x + j * blockDim.x), total - 1));
     }
 
-    __device__ __forceinline__ static void put(f32x4 a, int f, int NU, f32x4 *__restrict__ xl)
+    // Out-of-range f writes the spare float4 after the staged vectors, so the
+    // store (and the load feeding it) is unconditional.
+    __device__ __forceinline__ static void put(f32x4 a, int f, int total, int NU,
+                                               f32x4 *__restrict__ xl)
     {
-        const int t = f / (NU * 4);
-        const int rem = f - t * NU * 4;
-        xl[(size_t)t * 4 * NU + (size_t)(rem & 3) * NU + (rem >> 2)] = a;
+        int t, rem;
+        split_f<8>(min(f, total - 1), NU * 4, t, rem);
+        const size_t idx = f < total ? (size_t)t * 4 * NU + (size_t)(rem & 3) * NU + (rem >> 2)
+                                     : (size_t)total;
+        xl[idx] = a;
     }
 
-    __device__ __forceinline__ void store(const float *__restrict__ x, int NU,
+    __device__ __forceinline__ void store(const float *__restrict__ x, int total, int NU,
                                           f32x4 *__restrict__ xl)
     {
-        const int total = S * NU * 4;
 #pragma unroll
-        for (int j = 0; j < NPRE; j++) {
-            const int f = threadIdx.x + j * blockDim.x;
-            if (f < total) put(v[j], f, NU, xl);
-        }
+        for (int j = 0; j < NPRE; j++) put(v[j], threadIdx.x + j * blockDim.x, total, NU, xl);
         const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
         for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x)
-            put(x4[f], f, NU, xl);
+            put(x4[f], f, total, NU, xl);
     }
 };
 
@@ -96,15 +94,16 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     static_assert(128 % R == 0, "a lane group's rows must share one 128-row band");
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 16;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);   // [S][4][NU]
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);   // [S][4][NU] + 1 spare
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
     const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const int nit = (NU + LPR - 1) / LPR;
+    const int nit_pad = (nit + PF - 1) / PF * PF;
     const float *scrow = sc + (size_t)(min(row0, O - 1) / 128) * nbi;
 
     const uint8_t *wr[R];
@@ -112,23 +111,30 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * I;
 
-    XStageF8<S> xst;
-    xst.load(x, NU);
+    // activations first, then the first PF sweeps; every load unconditional
+    XStageF8<8> xst;
+    const int total4 = S * NU * 4;
+    xst.load(x, total4);
+    // every wave of the workgroup has issued its activation loads before any
+    // wave issues weight loads: the per-CU memory queue is in order, so the
+    // staging never waits behind the weight stream (raw barrier: no drain)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 
     u32x4 wb[PF][R];
     float sb[PF];
 #pragma unroll
     for (int j = 0; j < PF; j++) {
-        if (j < nit) {
-            const int u = min(j * LPR + sl, NU - 1);
+        const int u = min(j * LPR + sl, NU - 1);
 #pragma unroll
-            for (int r = 0; r < R; r++)
-                wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16);
-            sb[j] = scrow[u >> 3];
-        }
+        for (int r = 0; r < R; r++)
+            wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
+        sb[j] = ld_stream(&scrow[u >> 3]);
     }
 
-    xst.store(x, NU, xl);
+    __builtin_amdgcn_sched_barrier(0);
+    xst.store(x, total4, NU, xl);
     __syncthreads();
     if (tile >= ntiles) return;
 
@@ -138,35 +144,39 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
 
-    for (int c0 = 0; c0 < nit; c0 += PF) {
+    auto consume = [&](int c, int j) {
+        const int u = c * LPR + sl;
+        const bool valid = u < NU;
+        const int uu = valid ? u : 0;
+        const float s = valid ? sb[j] : 0.0f;
 #pragma unroll
-        for (int j = 0; j < PF; j++) {
-            const int c = c0 + j;
-            if (c < nit) {
-                const int u = c * LPR + sl;
-                const bool valid = u < NU;
-                const int uu = valid ? u : 0;
-                const float s = sb[j];
+        for (int t = 0; t < S; t++) {
+            const f32x4 *xt = xl + (size_t)t * 4 * NU;
 #pragma unroll
-                for (int t = 0; t < S; t++) {
-                    const f32x4 *xt = xl + (size_t)t * 4 * NU;
-#pragma unroll
-                    for (int r = 0; r < R; r++) {
-                        const float p = fp8_chunk_dot(wb[j][r], xt, NU, uu);
-                        // lanes past the row end add nothing (not even a NaN)
-                        acc[t][r] = valid ? __builtin_fmaf(s, p, acc[t][r]) : acc[t][r];
-                    }
-                }
-                if (c + PF < nit) {
-                    const int un = min(u + PF * LPR, NU - 1);
-#pragma unroll
-                    for (int r = 0; r < R; r++)
-                        wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)un * 16);
-                    sb[j] = scrow[un >> 3];
-                }
+            for (int r = 0; r < R; r++) {
+                const float p = fp8_chunk_dot(wb[j][r], xt, NU, uu);
+                // lanes past the row end add nothing (not even a NaN)
+                acc[t][r] = valid ? __builtin_fmaf(s, p, acc[t][r]) : acc[t][r];
             }
         }
+    };
+    // rounds of PF sweeps; refills unconditional and pinned; last round none
+    const int nrounds = nit_pad / PF;
+    for (int rd = 0; rd + 1 < nrounds; rd++) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            const int c = rd * PF + j;
+            consume(c, j);
+            const int un = min((c + PF) * LPR + sl, NU - 1);
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (uint32_t)un * 16u));
+            sb[j] = ld_stream(&scrow[un >> 3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+#pragma unroll
+    for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
 
 #pragma unroll
     for (int t = 0; t < S; t++)
@@ -229,8 +239,8 @@ __global__ __launch_bounds__(256) void fp8_dequant(const uint8_t *__restrict__ w
 
 namespace {
 
-// 16 columns per lane chunk = 4 float4 segments
-size_t fp8_lds_bytes(int S, int I) { return (size_t)S * (I / 16) * 4 * sizeof(f32x4); }
+// 16 columns per lane chunk = 4 float4 segments, plus one spare float4
+size_t fp8_lds_bytes(int S, int I) { return ((size_t)S * (I / 16) * 4 + 1) * sizeof(f32x4); }
 
 template <int S, int LPR, int R, int PF>
 hipError_t launch_t(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
@@ -254,7 +264,7 @@ hipError_t launch_s(const uint8_t *w, const float *sc, const float *x, float *y,
                     hipStream_t st)
 {
     constexpr int R = S <= 2 ? QG_FP8_R : 2;
-    constexpr int PF = QG_FP8_PF;
+    constexpr int PF = S <= 2 ? QG_FP8_PF : 2;
     switch (pick_lpr(I / 16)) {
     case 64: return launch_t<S, 64, R, PF>(w, sc, x, y, I, O, st);
     case 32: return launch_t<S, 32, R, PF>(w, sc, x, y, I, O, st);

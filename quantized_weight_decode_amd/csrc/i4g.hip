@@ -7,8 +7,7 @@
 // before the sum across groups.
 //
 // Streaming kernel (rows of 16-byte lane chunks, gs % 32 == 0):
-//   * each workgroup stages x (pre-scaled, permuted, with per-chunk sums) in
-//     LDS once;
+//   * each workgroup stages x (permuted, with per-chunk sums) in LDS once;
 //   * a wave covers 64/LPR row groups of R rows; LPR lanes sweep a row in
 //     16-byte dwordx4 loads (fully coalesced), the R rows of a lane group share
 //     the activations they read from LDS, and the next chunk's loads are in
@@ -21,13 +20,10 @@
 
 namespace qg {
 
-// Tile shape of the streaming kernel for S <= 2: rows per lane group, chunk
-// sweeps in flight, waves per workgroup.
+// Tile shape of the streaming kernel for S <= 2: rows per lane group and
+// waves per workgroup.
 #ifndef QG_I4G_R
 #define QG_I4G_R 4
-#endif
-#ifndef QG_I4G_PF
-#define QG_I4G_PF 1
 #endif
 #ifndef QG_I4G_WPB
 #define QG_I4G_WPB 4
@@ -50,13 +46,14 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * NU);  // [S][NU]
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
     const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const size_t rb = (size_t)I / 2;
     const int nit = (NU + LPR - 1) / LPR;
+    const int nit_pad = (nit + PF - 1) / PF * PF;
 
     const uint8_t *wr[R];
     const float *sr[R];
@@ -67,29 +64,37 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
         sr[r] = scales + (size_t)row * ng;
     }
 
-    // 1. activations are requested first (coalesced float4s, L2-resident), so
-    //    waiting for them never waits for the weight stream issued after them
-    XStage<S> xst;
-    xst.load(x, I, NU);
+    // Every global load below is unconditional (indices clamped into range),
+    // so the compiler can wait for exactly the load a value comes from
+    // instead of draining all outstanding loads.
+    // 1. activations first (L2-resident)
+    XStageN<S, 8> xst;
+    const int total4 = S * NU * 8;
+    xst.load(x, total4);
+    // every wave of the workgroup has issued its activation loads before any
+    // wave issues weight loads: the per-CU memory queue is in order, so the
+    // staging never waits behind the weight stream (raw barrier: no drain)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the first PF chunk-sweeps of weights and scales go out
+    // 2. the first PF chunk-sweeps of weights and scales
     u32x4 wb[PF][R];
     float sb[PF][R];
 #pragma unroll
     for (int j = 0; j < PF; j++) {
-        if (j < nit) {
-            const int u = min(j * LPR + sl, NU - 1);
-            const uint32_t g = div_cpg((uint32_t)u);
+        const int u = min(j * LPR + sl, NU - 1);
+        const uint32_t g = div_cpg((uint32_t)u);
 #pragma unroll
-            for (int r = 0; r < R; r++) {
-                wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16);
-                sb[j][r] = sr[r][g];
-            }
+        for (int r = 0; r < R; r++) {
+            wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
+            sb[j][r] = ld_stream(&sr[r][g]);
         }
     }
 
-    // 3. activations into LDS (pre-scaled, permuted, chunk sums)
-    xst.store(x, I, NU, xl, xs);
+    // 3. activations into LDS (permuted, chunk sums)
+    __builtin_amdgcn_sched_barrier(0);
+    xst.store(x, total4, NU, xl, xs);
     __syncthreads();
     if (tile >= ntiles) return;
 
@@ -99,38 +104,46 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
 
-    // 4. sweep: consume ring slot j, refill it with the sweep PF ahead
-    for (int c0 = 0; c0 < nit; c0 += PF) {
+    // 4. sweep in rounds of PF chunk-sweeps: consume ring slot j, then refill
+    //    it with the sweep one round ahead.  All refills are unconditional
+    //    (clamped) and pinned in place, so every wait is for exactly the slot
+    //    about to be used; the last round issues no refills.  Padding sweeps
+    //    past the row end add zero.
+    auto consume = [&](int c, int j) {
+        const int u = c * LPR + sl;
+        const bool valid = u < NU;
+        const int uu = valid ? u : 0;
 #pragma unroll
-        for (int j = 0; j < PF; j++) {
-            const int c = c0 + j;
-            if (c < nit) {
-                const int u = c * LPR + sl;
-                const bool valid = u < NU;
-                const int uu = valid ? u : 0;
+        for (int t = 0; t < S; t++) {
+            const f32x4 *xt = xl + (size_t)t * 8 * NU;
+            const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
 #pragma unroll
-                for (int t = 0; t < S; t++) {
-                    const f32x4 *xt = xl + (size_t)t * 8 * NU;
-                    const float xsum = xs[(size_t)t * NU + uu];
-#pragma unroll
-                    for (int r = 0; r < R; r++) {
-                        const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
-                        const float tv = __builtin_fmaf(-8.0f, xsum, p);
-                        acc[t][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[t][r]);
-                    }
-                }
-                if (c + PF < nit) {
-                    const int un = min(u + PF * LPR, NU - 1);
-                    const uint32_t g = div_cpg((uint32_t)un);
-#pragma unroll
-                    for (int r = 0; r < R; r++) {
-                        wb[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)un * 16);
-                        sb[j][r] = sr[r][g];
-                    }
-                }
+            for (int r = 0; r < R; r++) {
+                // s * (sum q x - 8 sum x); the chunk dot comes out as 2^-9 sum q x
+                const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
+                acc[t][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[t][r]);
             }
         }
+    };
+    const int nrounds = nit_pad / PF;
+    for (int rd = 0; rd + 1 < nrounds; rd++) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            const int c = rd * PF + j;
+            consume(c, j);
+            const int un = min((c + PF) * LPR + sl, NU - 1);
+            const uint32_t g = div_cpg((uint32_t)un);
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (uint32_t)un * 16u));
+                sb[j][r] = ld_stream(&sr[r][g]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+#pragma unroll
+    for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
 
 #pragma unroll
     for (int t = 0; t < S; t++)
@@ -226,20 +239,41 @@ hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, flo
     return hipGetLastError();
 }
 
+// chunk sweeps in flight per lane: the depth in {2, 3, 4} that leaves the
+// fewest padded sweeps (ties go to the deeper ring)
+inline int pick_pf(int nit)
+{
+    int best = 4, best_pad = 1 << 30;
+    for (int pf : {4, 3, 2}) {
+        const int pad = (nit + pf - 1) / pf * pf - nit;
+        if (pad < best_pad) { best_pad = pad; best = pf; }
+    }
+    return best;
+}
+
+template <int S, int LPR, int R>
+hipError_t launch_stream_pf(const uint8_t *w, const float *s, const float *x, float *y, int I,
+                            int O, int gs, hipStream_t st)
+{
+    switch (pick_pf((I / 32 + LPR - 1) / LPR)) {
+    case 2: return launch_stream_t<S, LPR, R, 2>(w, s, x, y, I, O, gs, st);
+    case 3: return launch_stream_t<S, LPR, R, 3>(w, s, x, y, I, O, gs, st);
+    default: return launch_stream_t<S, LPR, R, 4>(w, s, x, y, I, O, gs, st);
+    }
+}
+
 template <int S>
 hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, float *y,
                            int I, int O, int gs, hipStream_t st)
 {
-    // R rows share each activation read; PF sweeps of R dwordx4 loads are in
-    // flight per lane (12 loads for S <= 2)
+    // R rows of a lane group share each activation read from LDS
     constexpr int R = S <= 2 ? QG_I4G_R : 2;
-    constexpr int PF = S <= 2 ? QG_I4G_PF : 4;
     switch (pick_lpr(I / 32)) {
-    case 64: return launch_stream_t<S, 64, R, PF>(w, s, x, y, I, O, gs, st);
-    case 32: return launch_stream_t<S, 32, R, PF>(w, s, x, y, I, O, gs, st);
-    case 16: return launch_stream_t<S, 16, R, PF>(w, s, x, y, I, O, gs, st);
-    case 8: return launch_stream_t<S, 8, R, PF>(w, s, x, y, I, O, gs, st);
-    default: return launch_stream_t<S, 4, R, PF>(w, s, x, y, I, O, gs, st);
+    case 64: return launch_stream_pf<S, 64, R>(w, s, x, y, I, O, gs, st);
+    case 32: return launch_stream_pf<S, 32, R>(w, s, x, y, I, O, gs, st);
+    case 16: return launch_stream_pf<S, 16, R>(w, s, x, y, I, O, gs, st);
+    case 8: return launch_stream_pf<S, 8, R>(w, s, x, y, I, O, gs, st);
+    default: return launch_stream_pf<S, 4, R>(w, s, x, y, I, O, gs, st);
     }
 }
 

@@ -117,10 +117,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     constexpr int NPRE = 8;
     f32x4 xv[NPRE];
 #pragma unroll
-    for (int j = 0; j < NPRE; j++) {
-        const int f = threadIdx.x + j * blockDim.x;
-        if (f < total4) xv[j] = x4[f];
-    }
+    for (int j = 0; j < NPRE; j++) xv[j] = x4[min((int)(threadIdx.x + j * blockDim.x), total4 - 1)];
 
     // this wave's units: i = wave, wave + nwaves, ...; step s = (unit, sweep)
     const int nunits = rt.nu * nsub;
@@ -162,19 +159,27 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         const uint32_t g = div_cpg((uint32_t)u);
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            wc[r] = *reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16);
-            scur[r] = sr[r][g];
+            wc[r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
+            scur[r] = ld_stream(&sr[r][g]);
         }
     }
 
     // stage activations
+    const int cpv = NU * 8;
 #pragma unroll
     for (int j = 0; j < NPRE; j++) {
         const int f = threadIdx.x + j * blockDim.x;
-        if (f < total4) XStagePut(xv[j], f, NU, xl, xs);
+        int t, rem;
+        split_f<MOE_MAX_T>(min(f, total4 - 1), cpv, t, rem);
+        XStagePut(xv[j], f < total4, t, rem, NU, xl, xs);
     }
-    for (int f = threadIdx.x + NPRE * blockDim.x; f < total4; f += blockDim.x)
-        XStagePut(x4[f], f, NU, xl, xs);
+    const int nrest = (total4 - NPRE * (int)blockDim.x + (int)blockDim.x - 1) / (int)blockDim.x;
+    for (int it = 0; it < nrest; it++) {
+        const int f = threadIdx.x + (NPRE + it) * blockDim.x;
+        int t, rem;
+        split_f<MOE_MAX_T>(min(f, total4 - 1), cpv, t, rem);
+        XStagePut(x4[min(f, total4 - 1)], f < total4, t, rem, NU, xl, xs);
+    }
     __syncthreads();
 
     float acc[MOE_MAX_T][R];
@@ -204,8 +209,8 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
             const uint32_t g = div_cpg((uint32_t)un);
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                wn[r] = *reinterpret_cast<const u32x4 *>(nwr[r] + (size_t)un * 16);
-                sn[r] = nsr[r][g];
+                wn[r] = ld_stream(reinterpret_cast<const u32x4 *>(nwr[r] + (size_t)un * 16));
+                sn[r] = ld_stream(&nsr[r][g]);
             }
         }
 
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
                 for (int r = 0; r < R; r++) {
                     const float p = nib_chunk_dot(wc[r], xt, NU, uu);
-                    const float tv = __builtin_fmaf(-8.0f, xsum, p);
+                    const float tv = __builtin_fmaf(p, NIB_XSCALE, -8.0f * xsum);
                     acc[t][r] = valid ? __builtin_fmaf(scur[r], tv, acc[t][r]) : acc[t][r];
                 }
             }

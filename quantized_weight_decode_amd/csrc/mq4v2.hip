@@ -11,8 +11,8 @@
 // follows from the chunk's own byte offset.  The chunk is fetched with one
 // 16-byte load at an 8-byte-aligned address (136 g + 8 + 16 p); the lane's
 // header dword (+0 or +4) is a separate 4-byte load that hits the same lines.
-// With x staged exactly as for grouped int4 (pre-scaled by 2^9, per-chunk
-// sums), acc += scale * sum(q x) + zero * sum(x): weight = q*scale + zero
+// With x staged exactly as for grouped int4 (permuted, per-chunk sums),
+// acc += scale * sum(q x) + zero * sum(x): weight = q*scale + zero
 // reassociated.
 #include "qg_device.h"
 #include "qg_launch.h"
@@ -21,7 +21,7 @@
 #define QG_MQ4_R 4
 #endif
 #ifndef QG_MQ4_PF
-#define QG_MQ4_PF 1
+#define QG_MQ4_PF 2
 #endif
 #ifndef QG_MQ4_WPB
 #define QG_MQ4_WPB 4
@@ -37,7 +37,7 @@ typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 
 __device__ __forceinline__ u32x4 load16_a8(const uint8_t *p)
 {
-    const u32x4_a8 v = *reinterpret_cast<const u32x4_a8 *>(p);
+    const u32x4_a8 v = ld_stream(reinterpret_cast<const u32x4_a8 *>(p));
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
@@ -53,39 +53,48 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * NU);  // [S][NU]
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
     const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const size_t rowbytes = (size_t)(I / 256) * MQ4_GROUP_BYTES;
     const int nit = (NU + LPR - 1) / LPR;
+    const int nit_pad = (nit + PF - 1) / PF * PF;
 
     const uint8_t *wr[R];
 #pragma unroll
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
 
-    XStage<S> xst;
-    xst.load(x, I, NU);
+    XStageN<S, 8> xst;
+    const int total4 = S * NU * 8;
+    xst.load(x, total4);
+    // every wave of the workgroup has issued its activation loads before any
+    // wave issues weight loads: the per-CU memory queue is in order, so the
+    // staging never waits behind the weight stream (raw barrier: no drain)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // payload chunk u: group u/8, bytes 8 + 16 (u%8); header dword +0 / +4
+    auto fetch = [&](int u, u32x4 *wv, uint32_t *hv) {
+        const int g = u >> 3, p = u & 7;
+        const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            wv[r] = load16_a8(wr[r] + goff + 8 + 16 * p);
+            hv[r] = ld_stream(reinterpret_cast<const uint32_t *>(wr[r] + goff + (p >= 4 ? 4 : 0)));
+        }
+    };
 
     u32x4 wb[PF][R];
     uint32_t hb[PF][R];
 #pragma unroll
-    for (int j = 0; j < PF; j++) {
-        if (j < nit) {
-            const int u = min(j * LPR + sl, NU - 1);
-            const int g = u >> 3, p = u & 7;
-            const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
-#pragma unroll
-            for (int r = 0; r < R; r++) {
-                wb[j][r] = load16_a8(wr[r] + goff + 8 + 16 * p);
-                hb[j][r] = *reinterpret_cast<const uint32_t *>(wr[r] + goff + (p >= 4 ? 4 : 0));
-            }
-        }
-    }
+    for (int j = 0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
 
-    xst.store(x, I, NU, xl, xs);
+    __builtin_amdgcn_sched_barrier(0);
+    xst.store(x, total4, NU, xl, xs);
     __syncthreads();
     if (tile >= ntiles) return;
 
@@ -95,45 +104,41 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
 
-    for (int c0 = 0; c0 < nit; c0 += PF) {
+    auto consume = [&](int c, int j) {
+        const int u = c * LPR + sl;
+        const bool valid = u < NU;
+        const int uu = valid ? u : 0;
+        float scl[R], zro[R];
 #pragma unroll
-        for (int j = 0; j < PF; j++) {
-            const int c = c0 + j;
-            if (c < nit) {
-                const int u = c * LPR + sl;
-                const bool valid = u < NU;
-                const int uu = valid ? u : 0;
-                float scl[R], zro[R];
+        for (int r = 0; r < R; r++) {
+            scl[r] = f16_to_f32(hb[j][r] & 0xFFFFu);
+            zro[r] = f16_to_f32(hb[j][r] >> 16);
+        }
 #pragma unroll
-                for (int r = 0; r < R; r++) {
-                    scl[r] = f16_to_f32(hb[j][r] & 0xFFFFu);
-                    zro[r] = f16_to_f32(hb[j][r] >> 16);
-                }
+        for (int t = 0; t < S; t++) {
+            const f32x4 *xt = xl + (size_t)t * 8 * NU;
+            const float xsum = xs[(size_t)t * NU + uu];
 #pragma unroll
-                for (int t = 0; t < S; t++) {
-                    const f32x4 *xt = xl + (size_t)t * 8 * NU;
-                    const float xsum = xs[(size_t)t * NU + uu];
-#pragma unroll
-                    for (int r = 0; r < R; r++) {
-                        const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
-                        const float v = __builtin_fmaf(scl[r], p, zro[r] * xsum);
-                        acc[t][r] = valid ? acc[t][r] + v : acc[t][r];
-                    }
-                }
-                if (c + PF < nit) {
-                    const int un = min(u + PF * LPR, NU - 1);
-                    const int g = un >> 3, p = un & 7;
-                    const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
-#pragma unroll
-                    for (int r = 0; r < R; r++) {
-                        wb[j][r] = load16_a8(wr[r] + goff + 8 + 16 * p);
-                        hb[j][r] =
-                            *reinterpret_cast<const uint32_t *>(wr[r] + goff + (p >= 4 ? 4 : 0));
-                    }
-                }
+            for (int r = 0; r < R; r++) {
+                // scale * sum q x + zero * sum x; the chunk dot is 2^-9 sum q x
+                const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                const float v = __builtin_fmaf(scl[r] * NIB_XSCALE, p, zro[r] * xsum);
+                acc[t][r] = valid ? acc[t][r] + v : acc[t][r];
             }
         }
+    };
+    const int nrounds = nit_pad / PF;
+    for (int rd = 0; rd + 1 < nrounds; rd++) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            const int c = rd * PF + j;
+            consume(c, j);
+            fetch(min((c + PF) * LPR + sl, NU - 1), wb[j], hb[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+#pragma unroll
+    for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
 
 #pragma unroll
     for (int t = 0; t < S; t++)
@@ -280,7 +285,7 @@ template <int S>
 hipError_t launch_s(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
 {
     constexpr int R = S <= 2 ? QG_MQ4_R : 2;
-    constexpr int PF = S <= 2 ? QG_MQ4_PF : 2;
+    constexpr int PF = QG_MQ4_PF;
     switch (pick_lpr(I / 32)) {
     case 64: return launch_t<S, 64, R, PF>(w, x, y, I, O, st);
     case 32: return launch_t<S, 32, R, PF>(w, x, y, I, O, st);

@@ -15,6 +15,22 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
+// Weight streams are read with the non-temporal hint: each byte is used once
+// per call, and keeping it out of the caches leaves the activations (read by
+// every workgroup) resident in L2 across calls.
+#ifndef QG_NT
+#define QG_NT 1
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p)
+{
+#if QG_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Nibble decode.
 //
@@ -75,81 +91,96 @@ __device__ __forceinline__ float sub_reduce8(float v);
 //
 // A "lane chunk" is 16 packed bytes = 32 columns.  For chunk u and segment
 // k = 0..7 the LDS holds one float4:
-//    k = 2d   : x[32u + 8d + {0,2,4,6}] * 2^9   (matches low nibbles of dword d)
-//    k = 2d+1 : x[32u + 8d + {1,3,5,7}] * 2^9   (matches high nibbles)
+//    k = 2d   : x[32u + 8d + {0,2,4,6}]   (matches low nibbles of dword d)
+//    k = 2d+1 : x[32u + 8d + {1,3,5,7}]   (matches high nibbles)
 // stored at float4 index (k * NU + u), NU = chunks per vector, so that lanes
 // reading consecutive chunks touch consecutive 16-byte LDS words (no bank
 // conflicts).  xs[u] = plain f32 sum of the chunk's 32 activations, used to
-// fold per-chunk affine offsets out of the inner loop.
+// fold per-chunk affine offsets out of the inner loop.  The nibble decoder
+// returns q * 2^-9, so a chunk's dot product comes out as 2^-9 sum(q x) and
+// the fold multiplies it back by 2^9 (exact).
 // ---------------------------------------------------------------------------
-// Stages S activation vectors of I columns into the LDS layout above.
-// Loads are coalesced: thread f of the workgroup reads float4 number f of x
-// (so each load instruction of a wave covers 1 KB of consecutive bytes); the
-// eight float4s of one lane chunk sit in eight consecutive lanes, whose sum is
-// formed with an 8-lane DPP reduction.  load() issues the first NPRE float4s
-// per thread into registers (call it before issuing the weight stream, so the
-// in-order wait for them never waits for weights); store() writes them and
-// stages any remainder.  blockDim.x must be a multiple of 64.
-// Places float4 number f of the activations (vector t = f / (8 NU)) into the
-// LDS layout and adds its part of the chunk sum (8 consecutive lanes hold one
-// chunk; all 8 must be active).
-__device__ __forceinline__ void XStagePut(f32x4 a, int f, int NU, f32x4 *__restrict__ xl,
-                                          float *__restrict__ xs)
+// float4 number i of an array (32-bit offset from a wave-uniform base)
+__device__ __forceinline__ f32x4 ldx4(const float *__restrict__ base, uint32_t i)
 {
-    const int cpv = NU * 8;                  // float4s per vector
-    const int t = f / cpv;
-    const int rem = f - t * cpv;
-    const int u = rem >> 3, k = rem & 7;
-    const int d = k >> 1, h = k & 1;
-    float *base = reinterpret_cast<float *>(xl + (size_t)t * 8 * NU);
-    f32x2 ev = {a.x * NIB_XSCALE, a.z * NIB_XSCALE};
-    f32x2 od = {a.y * NIB_XSCALE, a.w * NIB_XSCALE};
-    *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d) * NU + u) * 4 + 2 * h) = ev;
-    *reinterpret_cast<f32x2 *>(base + ((size_t)(2 * d + 1) * NU + u) * 4 + 2 * h) = od;
-    const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
-    if (k == 7) xs[(size_t)t * NU + u] = cs;
+    return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(base) + i * 16u);
 }
 
-template <int S>
-struct XStage {
-    static constexpr int NPRE = 8;
+// Places float4 number f of vector t into the LDS layout and adds its part of
+// the chunk sum.  rem = f - t * 8 NU is the float4's index inside its vector.
+// Every lane of the wave must call this (the chunk sum is an 8-lane DPP
+// reduction over consecutive lanes); lanes with ok == false compute but store
+// nothing (their 8-lane group is entirely out of range).
+__device__ __forceinline__ void XStagePut(f32x4 a, bool ok, int t, int rem, int NU,
+                                          f32x4 *__restrict__ xl, float *__restrict__ xs)
+{
+    const uint32_t u = (uint32_t)rem >> 3, k = (uint32_t)rem & 7;
+    const uint32_t d = k >> 1, h = k & 1;
+    float *base = reinterpret_cast<float *>(xl) + (uint32_t)t * 32u * (uint32_t)NU;
+    const uint32_t oe = ((2 * d) * (uint32_t)NU + u) * 4 + 2 * h;
+    const uint32_t oo = oe + 4u * (uint32_t)NU;
+    f32x2 ev = {a.x, a.z};
+    f32x2 od = {a.y, a.w};
+    const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
+    if (ok) {
+        *reinterpret_cast<f32x2 *>(base + oe) = ev;
+        *reinterpret_cast<f32x2 *>(base + oo) = od;
+        if (k == 7) xs[(uint32_t)t * (uint32_t)NU + u] = cs;
+    }
+}
+
+// vector index t (< TMAX) and in-vector index of float4 number f; cpv = 8 NU
+template <int TMAX>
+__device__ __forceinline__ void split_f(int f, int cpv, int &t, int &rem)
+{
+    t = 0;
+#pragma unroll
+    for (int k = 1; k < TMAX; k++) t += f >= k * cpv;
+    rem = f - t * cpv;
+}
+
+// Stages S (<= 8) activation vectors of I columns into the LDS layout above.
+// Loads are coalesced: thread f of the workgroup reads float4 number f of x
+// (each load instruction of a wave covers 1 KB of consecutive bytes); the
+// eight float4s of one lane chunk sit in eight consecutive lanes, whose sum is
+// formed with an 8-lane DPP reduction.  load() issues NPRE float4s per thread
+// unconditionally (indices clamped into range) and store() consumes them
+// unconditionally, so a caller that issues the weight stream in between
+// waits for exactly these loads.  blockDim.x must be a multiple of 64.
+template <int S, int NPRE>
+struct XStageN {
     f32x4 v[NPRE];
 
-    __device__ __forceinline__ void load(const float *__restrict__ x, int I, int NU)
+    __device__ __forceinline__ void load(const float *__restrict__ x, int total)
     {
-        const int total = S * NU * 8;
-        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
 #pragma unroll
-        for (int j = 0; j < NPRE; j++) {
-            const int f = threadIdx.x + j * blockDim.x;
-            if (f < total) v[j] = x4[f];
-        }
-        (void)I;
+        for (int j = 0; j < NPRE; j++)
+            v[j] = ldx4(x, (uint32_t)min((int)(threadIdx.x + j * blockDim.x), total - 1));
     }
 
-    __device__ __forceinline__ static void put(f32x4 a, int f, int NU, f32x4 *__restrict__ xl,
-                                               float *__restrict__ xs)
-    {
-        XStagePut(a, f, NU, xl, xs);
-    }
-
-    __device__ __forceinline__ void store(const float *__restrict__ x, int I, int NU,
+    __device__ __forceinline__ void store(const float *__restrict__ x, int total, int NU,
                                           f32x4 *__restrict__ xl, float *__restrict__ xs)
     {
-        const int total = S * NU * 8;
+        const int cpv = NU * 8;
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
             const int f = threadIdx.x + j * blockDim.x;
-            if (f < total) put(v[j], f, NU, xl, xs);
+            int t, rem;
+            split_f<S>(min(f, total - 1), cpv, t, rem);
+            XStagePut(v[j], f < total, t, rem, NU, xl, xs);
         }
-        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
-        for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x)
-            put(x4[f], f, NU, xl, xs);
-        (void)I;
+        // remainder (shapes with more than NPRE float4s per thread)
+        const int nrest = (total - NPRE * (int)blockDim.x + (int)blockDim.x - 1) / (int)blockDim.x;
+        for (int it = 0; it < nrest; it++) {
+            const int f = threadIdx.x + (NPRE + it) * blockDim.x;
+            int t, rem;
+            split_f<S>(min(f, total - 1), cpv, t, rem);
+            XStagePut(ldx4(x, (uint32_t)min(f, total - 1)), f < total, t, rem, NU, xl, xs);
+        }
     }
 };
 
-// sum over the 32 columns of one lane chunk of q*x (x pre-scaled in LDS).
+// 2^-9 * sum over the 32 columns of one lane chunk of q*x.
 __device__ __forceinline__ float nib_chunk_dot(const u32x4 wv, const f32x4 *__restrict__ xl,
                                                int NU, int u)
 {
