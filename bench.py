@@ -279,6 +279,43 @@ CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_
               "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64"]
 
 
+KERNEL_SOURCES = {
+    "i4g_gemv_stream": "i4g.hip",
+    "fp8_gemv_stream": "fp8b128.hip",
+    "mq4v2_gemv_stream": "mq4v2.hip",
+    "moe_i4g_stream": "moe.hip",
+}
+
+
+def kernel_digest(kernel):
+    """sha256 over the sources that define `kernel` (its file and the shared headers)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "quantized_weight_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "qg_device.h", "qg_launch.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary of this kernel on this
+    workload, or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest = traffic = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("source digest: sha256:"):
+                digest = line.split(":", 2)[2].strip()
+            elif line.startswith("traffic per dispatch"):
+                traffic = int(line.rsplit(":", 1)[1].split()[0])
+    if digest != kernel_digest(kernel):
+        return None
+    return traffic
+
+
 def timed(torch, fn, first, k):
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -389,7 +426,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": case.kernel, "achieved": round(kgbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "us_per_launch": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes),
-                     "traffic": None},
+                     "traffic": profiled_traffic(case.kernel, case.name)},
         "parity_rel_l2": case.rel,
     }
     if isinstance(case, MoE):

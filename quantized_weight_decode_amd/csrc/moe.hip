@@ -16,7 +16,8 @@
 //     to the waves; a unit streams its rows of that expert once (dwordx4,
 //     scale gather) and forms the dot products of every token that chose it,
 //     with x of all tokens staged in LDS as for the dense grouped-int4 GEMV;
-//     the next unit's first loads are issued while the current one finishes;
+//     a wave's (unit, sweep) steps form one stream with PF sweeps of loads in
+//     flight, crossing unit boundaries;
 //   * a unit's row sums go to an LDS partial array [T][K][RT] for every slot
 //     (t, k) that selected the expert; after a barrier the workgroup forms
 //     y = sum_k gates * partial in ascending k (deterministic).
@@ -30,6 +31,9 @@
 #endif
 #ifndef QG_MOE_WPB
 #define QG_MOE_WPB 16
+#endif
+#ifndef QG_MOE_PF
+#define QG_MOE_PF 2
 #endif
 
 namespace qg {
@@ -45,13 +49,22 @@ struct Routing {
     int nu;           // distinct valid experts
 };
 
-// Every lane of the wave calls this (wave-uniform results except e / mask).
-__device__ __forceinline__ Routing route(const int32_t *__restrict__ ids, int T, int K, int E)
+// The id of this lane's (token, slot), loaded unconditionally (clamped) so
+// that the load can be issued ahead of others and waited for on its own.
+__device__ __forceinline__ int load_id(const int32_t *__restrict__ ids, int T, int K)
+{
+    const int lane = threadIdx.x & 63;
+    return ids[min(lane, T * K - 1)];
+}
+
+// Every lane of the wave calls this with its load_id() value (wave-uniform
+// results except e / mask).
+__device__ __forceinline__ Routing route_ids(int id, int T, int K, int E)
 {
     const int lane = threadIdx.x & 63;
     const int TK = T * K;
     Routing rt;
-    rt.e = lane < TK ? ids[lane] : -1;
+    rt.e = lane < TK ? id : -1;
     const bool in = lane < TK;
     const bool valid = in && rt.e >= 0 && rt.e < E;
     bool first = valid;
@@ -74,6 +87,11 @@ __device__ __forceinline__ Routing route(const int32_t *__restrict__ ids, int T,
     return rt;
 }
 
+__device__ __forceinline__ Routing route(const int32_t *__restrict__ ids, int T, int K, int E)
+{
+    return route_ids(load_id(ids, T, K), T, K, E);
+}
+
 // Lane holding the ui-th distinct expert.
 __device__ __forceinline__ int unique_lane(const Routing &rt, int ui)
 {
@@ -84,7 +102,7 @@ __device__ __forceinline__ int unique_lane(const Routing &rt, int ui)
     return __ffsll((long long)sel) - 1;
 }
 
-template <int LPR, int R>
+template <int LPR, int R, int PF>
 __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ scales, long long w_stride,
     long long s_stride, int E, const int32_t *__restrict__ ids, const float *__restrict__ gates,
@@ -99,7 +117,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     float *part = xs + (size_t)T * NU;                               // [T][K][RT]
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = blockDim.x >> 6;
     const int sub = lane / LPR;
     const int sl = lane % LPR;
@@ -108,61 +126,76 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const int nit = (NU + LPR - 1) / LPR;
     const int nsub = RT / ROWS_PER_WAVE;
 
-    const Routing rt = route(ids, T, K, E);
-    if (blockIdx.x == 0 && threadIdx.x == 0) err_flag[0] = rt.bad ? 1 : 0;
-
-    // activations of all tokens are requested before any weight
+    // activations of all tokens are requested before any weight; every wave
+    // has issued them before any wave issues a weight load
+    const int id = load_id(ids, T, K);
     const int total4 = T * NU * 8;
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
     constexpr int NPRE = 8;
     f32x4 xv[NPRE];
 #pragma unroll
-    for (int j = 0; j < NPRE; j++) xv[j] = x4[min((int)(threadIdx.x + j * blockDim.x), total4 - 1)];
+    for (int j = 0; j < NPRE; j++)
+        xv[j] = ldx4(x, (uint32_t)min((int)(threadIdx.x + j * blockDim.x), total4 - 1));
+    __builtin_amdgcn_sched_barrier(0);
 
-    // this wave's units: i = wave, wave + nwaves, ...; step s = (unit, sweep)
+    const Routing rt = route_ids(id, T, K, E);
+    if (blockIdx.x == 0 && threadIdx.x == 0) err_flag[0] = rt.bad ? 1 : 0;
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // this wave's units: i = wave + k * nwaves (k < my_units); a unit is
+    // (distinct expert ui, row sub-tile st); steps s = k * nit + c
     const int nunits = rt.nu * nsub;
     const int my_units = wave < nunits ? (nunits - wave + nwaves - 1) / nwaves : 0;
     const int nsteps = my_units * nit;
+    const int nsteps_pad = (nsteps + PF - 1) / PF * PF;
 
-    // per-unit state (wave-uniform)
-    int cur_e = 0;
-    uint32_t cur_mask = 0;
-    int cur_row0 = 0;     // first row of this lane group for the current unit
-    const uint8_t *wr[R];
-    const float *sr[R];
-    const uint8_t *nwr[R];
-    const float *nsr[R];
-
-    auto unit_setup = [&](int k, int &e, uint32_t &m, int &lrow0, const uint8_t **pw,
-                          const float **ps) {
+    struct Unit {
+        int e, row0;
+        uint32_t mask;
+    };
+    auto unit_of = [&](int k) {
         const int i = wave + k * nwaves;
         const int ui = i / nsub, st = i - ui * nsub;
         const int ql = unique_lane(rt, ui);
-        e = __builtin_amdgcn_readlane(rt.e, ql);
-        m = (uint32_t)__builtin_amdgcn_readlane((int)rt.mask, ql);
-        lrow0 = o0 + st * ROWS_PER_WAVE + sub * R;
-        const uint8_t *we = w + (size_t)e * (size_t)w_stride;
-        const float *se = scales + (size_t)e * (size_t)s_stride;
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-            const int row = min(lrow0 + r, O - 1);
-            pw[r] = we + (size_t)row * rb;
-            ps[r] = se + (size_t)row * ng;
-        }
+        Unit u;
+        // a wave without units still issues its (clamped) prefetch: expert 0
+        u.e = ql >= 0 ? __builtin_amdgcn_readlane(rt.e, ql) : 0;
+        u.mask = ql >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)rt.mask, ql) : 0u;
+        u.row0 = o0 + st * ROWS_PER_WAVE + sub * R;
+        return u;
     };
 
-    u32x4 wc[R], wn[R];
-    float scur[R], sn[R];
-    if (nsteps > 0) {
-        unit_setup(0, cur_e, cur_mask, cur_row0, wr, sr);
-        const int u = min(sl, NU - 1);
+    u32x4 wb[PF][R];
+    float sb[PF][R];
+    // fetch cursor (unit fk, sweep fc): the step whose loads are issued next.
+    // It stops on the wave's last step, so the padded tail of the stream
+    // re-issues that step's loads instead of branching around them.
+    const Unit u0 = unit_of(0);
+    int fk = 0, fc = 0;
+    Unit fu = u0;
+    auto fetch = [&](int j) {
+        const uint8_t *we = w + (size_t)fu.e * (size_t)w_stride;
+        const float *se = scales + (size_t)fu.e * (size_t)s_stride;
+        const int u = min(fc * LPR + sl, NU - 1);
         const uint32_t g = div_cpg((uint32_t)u);
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            wc[r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
-            scur[r] = ld_stream(&sr[r][g]);
+            const int row = min(fu.row0 + r, O - 1);
+            wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(we + (size_t)row * rb +
+                                                                 (uint32_t)u * 16u));
+            sb[j][r] = ld_stream(se + (size_t)row * ng + g);
         }
-    }
+        if (fc + 1 < nit) {
+            ++fc;
+        } else if (fk + 1 < my_units) {
+            fc = 0;
+            fu = unit_of(++fk);
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < PF; j++) fetch(j);
+    __builtin_amdgcn_sched_barrier(0);
 
     // stage activations
     const int cpv = NU * 8;
@@ -178,7 +211,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         const int f = threadIdx.x + (NPRE + it) * blockDim.x;
         int t, rem;
         split_f<MOE_MAX_T>(min(f, total4 - 1), cpv, t, rem);
-        XStagePut(x4[min(f, total4 - 1)], f < total4, t, rem, NU, xl, xs);
+        XStagePut(ldx4(x, (uint32_t)min(f, total4 - 1)), f < total4, t, rem, NU, xl, xs);
     }
     __syncthreads();
 
@@ -188,78 +221,65 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
 
-    int nxt_e = 0, nxt_row0 = 0;
-    uint32_t nxt_mask = 0;
-    for (int s = 0; s < nsteps; s++) {
-        const int k = s / nit;
-        const int c = s - k * nit;
-        // prefetch step s+1 (possibly the next unit's first sweep)
-        const bool have_next = s + 1 < nsteps;
-        const bool next_new_unit = c + 1 == nit;
-        if (have_next) {
-            int un;
-            if (next_new_unit) {
-                unit_setup(k + 1, nxt_e, nxt_mask, nxt_row0, nwr, nsr);
-                un = min(sl, NU - 1);
-            } else {
-#pragma unroll
-                for (int r = 0; r < R; r++) { nwr[r] = wr[r]; nsr[r] = sr[r]; }
-                un = min((c + 1) * LPR + sl, NU - 1);
-            }
-            const uint32_t g = div_cpg((uint32_t)un);
-#pragma unroll
-            for (int r = 0; r < R; r++) {
-                wn[r] = ld_stream(reinterpret_cast<const u32x4 *>(nwr[r] + (size_t)un * 16));
-                sn[r] = ld_stream(&nsr[r][g]);
-            }
-        }
-
-        const int u = c * LPR + sl;
+    // consume cursor (unit ck, sweep cc)
+    int ck = 0, cc = 0;
+    Unit cu = u0;
+    auto consume = [&](int s, int j) {
+        if (s >= nsteps) return;                       // padding (wave-uniform)
+        const int u = cc * LPR + sl;
         const bool valid = u < NU;
         const int uu = valid ? u : 0;
 #pragma unroll
         for (int t = 0; t < MOE_MAX_T; t++) {
-            if (t < T && ((cur_mask >> t) & 1)) {
+            if (t < T && ((cu.mask >> t) & 1)) {       // wave-uniform
                 const f32x4 *xt = xl + (size_t)t * 8 * NU;
-                const float xsum = xs[(size_t)t * NU + uu];
+                const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                    const float p = nib_chunk_dot(wc[r], xt, NU, uu);
-                    const float tv = __builtin_fmaf(p, NIB_XSCALE, -8.0f * xsum);
-                    acc[t][r] = valid ? __builtin_fmaf(scur[r], tv, acc[t][r]) : acc[t][r];
+                    const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                    const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
+                    acc[t][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[t][r]);
                 }
             }
         }
-
-        if (c + 1 == nit) {
-            // unit done: row sums -> partials of every slot that chose cur_e
+        if (cc + 1 < nit) {
+            ++cc;
+            return;
+        }
+        // unit done: row sums -> partials of every slot that chose cu.e
 #pragma unroll
-            for (int t = 0; t < MOE_MAX_T; t++) {
-                if (t < T && ((cur_mask >> t) & 1)) {
+        for (int t = 0; t < MOE_MAX_T; t++) {
+            if (t < T && ((cu.mask >> t) & 1)) {
 #pragma unroll
-                    for (int r = 0; r < R; r++) {
-                        const float v = sub_reduce<LPR>(acc[t][r]);
-                        const int lr = cur_row0 + r - o0;
-                        if (sl == LPR - 1 && cur_row0 + r < O) {
-                            for (int kk = 0; kk < K; kk++)
-                                if (ids[t * K + kk] == cur_e) part[((size_t)t * K + kk) * RT + lr] = v;
-                        }
-                        acc[t][r] = 0.0f;
+                for (int r = 0; r < R; r++) {
+                    const float v = sub_reduce<LPR>(acc[t][r]);
+                    const int lr = cu.row0 + r - o0;
+                    for (int kk = 0; kk < K; kk++) {
+                        const int ek = __builtin_amdgcn_readlane(rt.e, t * K + kk);
+                        if (ek == cu.e && sl == LPR - 1 && cu.row0 + r < O)
+                            part[((size_t)t * K + kk) * RT + lr] = v;
                     }
+                    acc[t][r] = 0.0f;
                 }
             }
-            if (have_next) {
-                cur_e = nxt_e;
-                cur_mask = nxt_mask;
-                cur_row0 = nxt_row0;
-#pragma unroll
-                for (int r = 0; r < R; r++) { wr[r] = nwr[r]; sr[r] = nsr[r]; }
-            }
         }
-        if (have_next) {
+        cc = 0;
+        if (++ck < my_units) cu = unit_of(ck);
+    };
+
+    const int nrounds = nsteps_pad / PF;
+    for (int rd = 0; rd + 1 < nrounds; rd++) {
 #pragma unroll
-            for (int r = 0; r < R; r++) { wc[r] = wn[r]; scur[r] = sn[r]; }
+        for (int j = 0; j < PF; j++) {
+            const int s = rd * PF + j;
+            consume(s, j);
+            fetch(j);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    if (nrounds > 0) {
+#pragma unroll
+        for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
     }
     __syncthreads();
 
@@ -338,7 +358,7 @@ hipError_t launch_t(const uint8_t *w, const float *s, long long ws, long long ss
                     float *y, int I, int O, int gs, int RT, int *err, hipStream_t st)
 {
     const size_t lds = moe_lds_bytes(T, K, I, RT);
-    auto kern = moe_i4g_stream<LPR, R>;
+    auto kern = moe_i4g_stream<LPR, R, QG_MOE_PF>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     const int blocks = (O + RT - 1) / RT;
