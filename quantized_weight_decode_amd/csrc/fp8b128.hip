@@ -36,23 +36,27 @@ constexpr int FP8_FAST_MAX_S = 4;
 template <int NPRE>
 struct XStageF8 {
     f32x4 v[NPRE];
+    int rot;
 
     __device__ __forceinline__ void load(const float *__restrict__ x, int total)
     {
+        rot = stage_rot(total);
 #pragma unroll
         for (int j = 0; j < NPRE; j++)
-            v[j] = ldx4(x, (uint32_t)min((int)(threadIdx.x + j * blockDim.x), total - 1));
+            v[j] = ldx4(x, (uint32_t)stage_index((int)(threadIdx.x + j * blockDim.x), total, rot));
     }
 
-    // Out-of-range f writes the spare float4 after the staged vectors, so the
-    // store (and the load feeding it) is unconditional.
-    __device__ __forceinline__ static void put(f32x4 a, int f, int total, int NU,
+    // g is the float4 index read for the workgroup's f-th read.  Out-of-range
+    // f writes the spare float4 after the staged vectors, so the store (and
+    // the load feeding it) is unconditional.
+    __device__ __forceinline__ static void put(f32x4 a, int f, int g, int total, int NU,
                                                f32x4 *__restrict__ xl)
     {
         int t, rem;
-        split_f<8>(min(f, total - 1), NU * 4, t, rem);
-        const size_t idx = f < total ? (size_t)t * 4 * NU + (size_t)(rem & 3) * NU + (rem >> 2)
-                                     : (size_t)total;
+        split_f<8>(g, NU * 4, t, rem);
+        const size_t NS = (size_t)seg_stride(NU);
+        const size_t idx = f < total ? (size_t)t * 4 * NS + (size_t)(rem & 3) * NS + (rem >> 2)
+                                     : (size_t)(total / (4 * NU)) * 4 * NS;
         xl[idx] = a;
     }
 
@@ -60,10 +64,15 @@ struct XStageF8 {
                                           f32x4 *__restrict__ xl)
     {
 #pragma unroll
-        for (int j = 0; j < NPRE; j++) put(v[j], threadIdx.x + j * blockDim.x, total, NU, xl);
+        for (int j = 0; j < NPRE; j++) {
+            const int f = threadIdx.x + j * blockDim.x;
+            put(v[j], f, stage_index(f, total, rot), total, NU, xl);
+        }
         const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
-        for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x)
-            put(x4[f], f, total, NU, xl);
+        for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x) {
+            const int g = stage_index(f, total, rot);
+            put(x4[g], f, g, total, NU, xl);
+        }
     }
 };
 
@@ -76,7 +85,7 @@ __device__ __forceinline__ float fp8_chunk_dot(const u32x4 wv, const f32x4 *__re
     for (int d = 0; d < 4; d++) {
         float v[4];
         e4m3x4(wv[d], v);
-        const f32x4 xv = xl[(size_t)d * NU + u];
+        const f32x4 xv = xl[(size_t)d * seg_stride(NU) + u];
         p0 = __builtin_fmaf(v[0], xv.x, p0);
         p1 = __builtin_fmaf(v[1], xv.y, p1);
         p0 = __builtin_fmaf(v[2], xv.z, p0);
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     static_assert(128 % R == 0, "a lane group's rows must share one 128-row band");
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 16;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);   // [S][4][NU] + 1 spare
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);   // [S][4][NS] + 1 spare
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
         const float s = valid ? sb[j] : 0.0f;
 #pragma unroll
         for (int t = 0; t < S; t++) {
-            const f32x4 *xt = xl + (size_t)t * 4 * NU;
+            const f32x4 *xt = xl + (size_t)t * 4 * seg_stride(NU);
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 const float p = fp8_chunk_dot(wb[j][r], xt, NU, uu);
@@ -240,7 +249,10 @@ __global__ __launch_bounds__(256) void fp8_dequant(const uint8_t *__restrict__ w
 namespace {
 
 // 16 columns per lane chunk = 4 float4 segments, plus one spare float4
-size_t fp8_lds_bytes(int S, int I) { return ((size_t)S * (I / 16) * 4 + 1) * sizeof(f32x4); }
+size_t fp8_lds_bytes(int S, int I)
+{
+    return ((size_t)S * 4 * seg_stride(I / 16) + 1) * sizeof(f32x4);
+}
 
 template <int S, int LPR, int R, int PF>
 hipError_t launch_t(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,

@@ -28,6 +28,10 @@ namespace qg {
 #ifndef QG_I4G_WPB
 #define QG_I4G_WPB 4
 #endif
+// chunk-sweeps issued before the activations are staged (at most PF)
+#ifndef QG_I4G_PF0
+#define QG_I4G_PF0 0
+#endif
 
 // Largest S the streaming kernels are instantiated for; S up to QGEMV_MAX_S
 // goes through the general kernel.
@@ -40,10 +44,11 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     Div20 div_cpg, int ntiles)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    constexpr int PF0 = QG_I4G_PF0 < PF ? QG_I4G_PF0 : PF;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;                       // lane chunks per row
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NU]
-    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * NU);  // [S][NU]
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NS]
+    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * seg_stride(NU));  // [S][NU]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -72,31 +77,39 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any
-    // wave issues weight loads: the per-CU memory queue is in order, so the
-    // staging never waits behind the weight stream (raw barrier: no drain)
+    // wave issues weight loads (raw barrier: no drain)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the first PF chunk-sweeps of weights and scales
+    // 2. the first PF0 chunk-sweeps of weights and scales.  Only a few: the
+    //    memory system serves a flood of streaming weight requests ahead of
+    //    the isolated activation reads, so the stream is held back until the
+    //    activations have arrived, with just enough weight traffic in flight
+    //    to keep HBM busy meanwhile.
     u32x4 wb[PF][R];
     float sb[PF][R];
-#pragma unroll
-    for (int j = 0; j < PF; j++) {
-        const int u = min(j * LPR + sl, NU - 1);
+    auto fetch = [&](int c, int j) {
+        const int u = min(c * LPR + sl, NU - 1);
         const uint32_t g = div_cpg((uint32_t)u);
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
+            wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (uint32_t)u * 16u));
             sb[j][r] = ld_stream(&sr[r][g]);
         }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < PF0; j++) fetch(j, j);
 
-    // 3. activations into LDS (permuted, chunk sums)
+    // 3. activations into LDS (permuted, chunk sums), then the rest of the
+    //    first round of weights
     __builtin_amdgcn_sched_barrier(0);
     xst.store(x, total4, NU, xl, xs);
     __syncthreads();
     if (tile >= ntiles) return;
+#pragma unroll
+    for (int j = PF0; j < PF; j++) fetch(j, j);
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
 #pragma unroll
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
         const int uu = valid ? u : 0;
 #pragma unroll
         for (int t = 0; t < S; t++) {
-            const f32x4 *xt = xl + (size_t)t * 8 * NU;
+            const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
             const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -132,13 +145,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
         for (int j = 0; j < PF; j++) {
             const int c = rd * PF + j;
             consume(c, j);
-            const int un = min((c + PF) * LPR + sl, NU - 1);
-            const uint32_t g = div_cpg((uint32_t)un);
-#pragma unroll
-            for (int r = 0; r < R; r++) {
-                wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (uint32_t)un * 16u));
-                sb[j][r] = ld_stream(&sr[r][g]);
-            }
+            fetch(c + PF, j);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -281,7 +288,7 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
 
 size_t i4g_stream_lds_bytes(int S, int I)
 {
-    return (size_t)S * (I / 32) * (8 * sizeof(f32x4) + sizeof(float));
+    return (size_t)S * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float));
 }
 
 bool i4g_stream_ok(const void *w, const float *x, int S, int I, int gs)

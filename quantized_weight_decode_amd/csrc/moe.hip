@@ -35,6 +35,10 @@
 #ifndef QG_MOE_PF
 #define QG_MOE_PF 2
 #endif
+// sweeps issued before the activations are staged (at most PF)
+#ifndef QG_MOE_PF0
+#define QG_MOE_PF0 0
+#endif
 
 namespace qg {
 
@@ -69,11 +73,17 @@ __device__ __forceinline__ Routing route_ids(int id, int T, int K, int E)
     const bool valid = in && rt.e >= 0 && rt.e < E;
     bool first = valid;
     uint32_t mask = 0;
-    for (int q = 0; q < TK; q++) {
+    // slot q belongs to token tq = q / K, tracked incrementally (a division
+    // per iteration would run on the scalar unit of every wave)
+    for (int q = 0, tq = 0, kq = 0; q < TK; q++) {
         const int eq = __builtin_amdgcn_readlane(rt.e, q);
         if (eq == rt.e) {
             if (q < lane) first = false;
-            mask |= 1u << (q / K);
+            mask |= 1u << tq;
+        }
+        if (++kq == K) {
+            kq = 0;
+            ++tq;
         }
     }
     rt.first = __ballot(first);
@@ -110,11 +120,13 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     Div20 div_cpg, int RT, int *__restrict__ err_flag)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    constexpr int PF0 = QG_MOE_PF0 < PF ? QG_MOE_PF0 : PF;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [T][8][NU]
-    float *xs = reinterpret_cast<float *>(xl + (size_t)T * 8 * NU);  // [T][NU]
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [T][8][NS]
+    float *xs = reinterpret_cast<float *>(xl + (size_t)T * 8 * seg_stride(NU));  // [T][NU]
     float *part = xs + (size_t)T * NU;                               // [T][K][RT]
+    int *ids_l = reinterpret_cast<int *>(part + (size_t)T * K * RT); // [64]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,19 +140,27 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 
     // activations of all tokens are requested before any weight; every wave
     // has issued them before any wave issues a weight load
-    const int id = load_id(ids, T, K);
+    // one wave per workgroup reads the ids (thousands of waves reading the
+    // same line would queue on one L2 channel) and hands them over in LDS
+    int id = 0;
+    if (wave == 0) id = load_id(ids, T, K);
     const int total4 = T * NU * 8;
     constexpr int NPRE = 8;
     f32x4 xv[NPRE];
+    const int rot = stage_rot(total4);
 #pragma unroll
     for (int j = 0; j < NPRE; j++)
-        xv[j] = ldx4(x, (uint32_t)min((int)(threadIdx.x + j * blockDim.x), total4 - 1));
+        xv[j] = ldx4(x, (uint32_t)stage_index((int)(threadIdx.x + j * blockDim.x), total4, rot));
     __builtin_amdgcn_sched_barrier(0);
 
-    const Routing rt = route_ids(id, T, K, E);
-    if (blockIdx.x == 0 && threadIdx.x == 0) err_flag[0] = rt.bad ? 1 : 0;
+    if (wave == 0) ids_l[lane] = id;
+    // raw barrier (the activation loads stay in flight); the LDS write must
+    // have landed before it
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    const Routing rt = route_ids(ids_l[lane], T, K, E);
+    if (blockIdx.x == 0 && threadIdx.x == 0) err_flag[0] = rt.bad ? 1 : 0;
 
     // this wave's units: i = wave + k * nwaves (k < my_units); a unit is
     // (distinct expert ui, row sub-tile st); steps s = k * nit + c
@@ -193,8 +213,10 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         }
     };
 
+    // only PF0 sweeps go out before the activations are staged: a flood of
+    // streaming weight requests is served ahead of the activation reads
 #pragma unroll
-    for (int j = 0; j < PF; j++) fetch(j);
+    for (int j = 0; j < PF0; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
 
     // stage activations
@@ -203,17 +225,21 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     for (int j = 0; j < NPRE; j++) {
         const int f = threadIdx.x + j * blockDim.x;
         int t, rem;
-        split_f<MOE_MAX_T>(min(f, total4 - 1), cpv, t, rem);
+        split_f<MOE_MAX_T>(stage_index(f, total4, rot), cpv, t, rem);
         XStagePut(xv[j], f < total4, t, rem, NU, xl, xs);
     }
     const int nrest = (total4 - NPRE * (int)blockDim.x + (int)blockDim.x - 1) / (int)blockDim.x;
     for (int it = 0; it < nrest; it++) {
         const int f = threadIdx.x + (NPRE + it) * blockDim.x;
+        const int g = stage_index(f, total4, rot);
         int t, rem;
-        split_f<MOE_MAX_T>(min(f, total4 - 1), cpv, t, rem);
-        XStagePut(ldx4(x, (uint32_t)min(f, total4 - 1)), f < total4, t, rem, NU, xl, xs);
+        split_f<MOE_MAX_T>(g, cpv, t, rem);
+        XStagePut(ldx4(x, (uint32_t)g), f < total4, t, rem, NU, xl, xs);
     }
     __syncthreads();
+#pragma unroll
+    for (int j = PF0; j < PF; j++) fetch(j);
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[MOE_MAX_T][R];
 #pragma unroll
@@ -232,7 +258,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
         for (int t = 0; t < MOE_MAX_T; t++) {
             if (t < T && ((cu.mask >> t) & 1)) {       // wave-uniform
-                const f32x4 *xt = xl + (size_t)t * 8 * NU;
+                const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
                 const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
 #pragma unroll
                 for (int r = 0; r < R; r++) {
@@ -349,7 +375,8 @@ namespace {
 
 size_t moe_lds_bytes(int T, int K, int I, int RT)
 {
-    return (size_t)T * (I / 32) * (8 * sizeof(f32x4) + 4) + (size_t)T * K * RT * 4;
+    return (size_t)T * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float)) +
+           (size_t)T * K * RT * sizeof(float) + 64 * sizeof(int);
 }
 
 template <int LPR, int R>

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NU]
-    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * NU);  // [S][NU]
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NS]
+    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * seg_stride(NU));  // [S][NU]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
         }
 #pragma unroll
         for (int t = 0; t < S; t++) {
-            const f32x4 *xt = xl + (size_t)t * 8 * NU;
+            const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
             const float xsum = xs[(size_t)t * NU + uu];
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -264,7 +264,10 @@ __global__ __launch_bounds__(256) void fwht256_kernel(const float *__restrict__ 
 
 namespace {
 
-size_t mq4_lds_bytes(int S, int I) { return (size_t)S * (I / 32) * (8 * sizeof(f32x4) + 4); }
+size_t mq4_lds_bytes(int S, int I)
+{
+    return (size_t)S * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float));
+}
 
 template <int S, int LPR, int R, int PF>
 hipError_t launch_t(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)

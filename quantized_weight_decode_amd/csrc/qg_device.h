@@ -93,14 +93,18 @@ __device__ __forceinline__ float sub_reduce8(float v);
 // k = 0..7 the LDS holds one float4:
 //    k = 2d   : x[32u + 8d + {0,2,4,6}]   (matches low nibbles of dword d)
 //    k = 2d+1 : x[32u + 8d + {1,3,5,7}]   (matches high nibbles)
-// stored at float4 index (k * NU + u), NU = chunks per vector, so that lanes
+// stored at float4 index (k * NS + u), NU = chunks per vector, so that lanes
 // reading consecutive chunks touch consecutive 16-byte LDS words (no bank
-// conflicts).  xs[u] = plain f32 sum of the chunk's 32 activations, used to
+// conflicts).  The segment stride NS = NU + 1 is padded by one float4: with
+// NS a multiple of 16 the staging writes of the eight segments of one chunk
+// (made by eight neighbouring lanes) would all land in the same banks.  xs[u] = plain f32 sum of the chunk's 32 activations, used to
 // fold per-chunk affine offsets out of the inner loop.  The nibble decoder
 // returns q * 2^-9, so a chunk's dot product comes out as 2^-9 sum(q x) and
 // the fold multiplies it back by 2^9 (exact).
 // ---------------------------------------------------------------------------
 // float4 number i of an array (32-bit offset from a wave-uniform base)
+__host__ __device__ constexpr int seg_stride(int NU) { return NU + 1; }
+
 __device__ __forceinline__ f32x4 ldx4(const float *__restrict__ base, uint32_t i)
 {
     return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(base) + i * 16u);
@@ -116,9 +120,10 @@ __device__ __forceinline__ void XStagePut(f32x4 a, bool ok, int t, int rem, int 
 {
     const uint32_t u = (uint32_t)rem >> 3, k = (uint32_t)rem & 7;
     const uint32_t d = k >> 1, h = k & 1;
-    float *base = reinterpret_cast<float *>(xl) + (uint32_t)t * 32u * (uint32_t)NU;
-    const uint32_t oe = ((2 * d) * (uint32_t)NU + u) * 4 + 2 * h;
-    const uint32_t oo = oe + 4u * (uint32_t)NU;
+    const uint32_t NS = (uint32_t)seg_stride(NU);
+    float *base = reinterpret_cast<float *>(xl) + (uint32_t)t * 32u * NS;
+    const uint32_t oe = ((2 * d) * NS + u) * 4 + 2 * h;
+    const uint32_t oo = oe + 4u * NS;
     f32x2 ev = {a.x, a.z};
     f32x2 od = {a.y, a.w};
     const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
@@ -139,6 +144,24 @@ __device__ __forceinline__ void split_f(int f, int cpv, int &t, int &rem)
     rem = f - t * cpv;
 }
 
+// Every workgroup reads the same activation vectors.  If all of them walked
+// x in the same order, the workgroups sharing an L2 would request the same
+// few lines at the same moment and queue on one L2 channel; each workgroup
+// therefore starts at its own line-aligned offset (a multiple of 8 float4s,
+// so lane chunks stay aligned) and wraps around.  stage_rot() picks the
+// offset; stage_index() maps the f-th read of the workgroup to a float4
+// index (reads past the end are clamped onto a valid index).
+__device__ __forceinline__ int stage_rot(int total)
+{
+    const unsigned lines = (unsigned)total / 8u;
+    return lines ? (int)(((blockIdx.x * 2654435761u) >> 7) % lines) * 8 : 0;
+}
+__device__ __forceinline__ int stage_index(int f, int total, int rot)
+{
+    const int g = min(f, total - 1) + rot;
+    return g >= total ? g - total : g;
+}
+
 // Stages S (<= 8) activation vectors of I columns into the LDS layout above.
 // Loads are coalesced: thread f of the workgroup reads float4 number f of x
 // (each load instruction of a wave covers 1 KB of consecutive bytes); the
@@ -151,11 +174,14 @@ template <int S, int NPRE>
 struct XStageN {
     f32x4 v[NPRE];
 
+    int rot;
+
     __device__ __forceinline__ void load(const float *__restrict__ x, int total)
     {
+        rot = stage_rot(total);
 #pragma unroll
         for (int j = 0; j < NPRE; j++)
-            v[j] = ldx4(x, (uint32_t)min((int)(threadIdx.x + j * blockDim.x), total - 1));
+            v[j] = ldx4(x, (uint32_t)stage_index((int)(threadIdx.x + j * blockDim.x), total, rot));
     }
 
     __device__ __forceinline__ void store(const float *__restrict__ x, int total, int NU,
@@ -166,16 +192,17 @@ struct XStageN {
         for (int j = 0; j < NPRE; j++) {
             const int f = threadIdx.x + j * blockDim.x;
             int t, rem;
-            split_f<S>(min(f, total - 1), cpv, t, rem);
+            split_f<S>(stage_index(f, total, rot), cpv, t, rem);
             XStagePut(v[j], f < total, t, rem, NU, xl, xs);
         }
         // remainder (shapes with more than NPRE float4s per thread)
         const int nrest = (total - NPRE * (int)blockDim.x + (int)blockDim.x - 1) / (int)blockDim.x;
         for (int it = 0; it < nrest; it++) {
             const int f = threadIdx.x + (NPRE + it) * blockDim.x;
+            const int g = stage_index(f, total, rot);
             int t, rem;
-            split_f<S>(min(f, total - 1), cpv, t, rem);
-            XStagePut(ldx4(x, (uint32_t)min(f, total - 1)), f < total, t, rem, NU, xl, xs);
+            split_f<S>(g, cpv, t, rem);
+            XStagePut(ldx4(x, (uint32_t)g), f < total, t, rem, NU, xl, xs);
         }
     }
 };
@@ -189,8 +216,8 @@ __device__ __forceinline__ float nib_chunk_dot(const u32x4 wv, const f32x4 *__re
     for (int d = 0; d < 4; d++) {
         float e[4], o[4];
         nib8(wv[d], e, o);
-        const f32x4 xe = xl[(2 * d) * NU + u];
-        const f32x4 xo = xl[(2 * d + 1) * NU + u];
+        const f32x4 xe = xl[(2 * d) * seg_stride(NU) + u];
+        const f32x4 xo = xl[(2 * d + 1) * seg_stride(NU) + u];
         p0 = __builtin_fmaf(e[0], xe.x, p0);
         p1 = __builtin_fmaf(o[0], xo.x, p1);
         p0 = __builtin_fmaf(e[1], xe.y, p0);
