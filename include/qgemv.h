@@ -120,8 +120,10 @@ int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S,
  *   T in 1..8, K in 1..64, gs even >= 2
  *   workspace  device scratch of at least qgemv_moe_topk_workspace(T, K, O)
  *              bytes, 4-byte aligned; its contents are overwritten.
- * Each distinct selected expert is streamed from memory once per call, for
- * all tokens that selected it.  The routing never leaves the device.
+ * Each token streams each distinct expert it selected once (an id repeated
+ * within a token is read once and counted per slot; an expert selected by
+ * several tokens is read once per selecting token).  The routing never
+ * leaves the device.
  */
 size_t qgemv_moe_topk_workspace(int T, int K, int O);
 int qgemv_moe_topk(const void *w, const float *scales, long long w_stride,

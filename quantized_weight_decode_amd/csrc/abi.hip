@@ -159,9 +159,15 @@ int qgemv_moe_topk_error(const void *workspace, int *flag, void *stream)
     if (!workspace || !flag) return QGEMV_E_NULL;
     if (mis4(workspace)) return QGEMV_E_ALIGN;
     hipStream_t st = (hipStream_t)stream;
-    if (hipMemcpyAsync(flag, workspace, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess)
+    // one flag per token slot (QGEMV_MAX_S of them)
+    int f[QGEMV_MAX_S];
+    if (hipMemcpyAsync(f, workspace, sizeof(f), hipMemcpyDeviceToHost, st) != hipSuccess)
         return QGEMV_E_HIP;
-    return hipStreamSynchronize(st) == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return QGEMV_E_HIP;
+    int any = 0;
+    for (int v : f) any |= v != 0;
+    *flag = any;
+    return QGEMV_OK;
 }
 
 }  // extern "C"

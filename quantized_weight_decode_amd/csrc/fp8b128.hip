@@ -33,7 +33,7 @@ constexpr int FP8_FAST_MAX_S = 4;
 // Stages up to 8 vectors into the fp8 LDS layout with coalesced float4 loads;
 // as XStageN, the first NPRE float4s per thread are loaded unconditionally
 // (indices clamped) so later waits count exactly.
-template <int NPRE>
+template <int NPRE, int NT>
 struct XStageF8 {
     f32x4 v[NPRE];
     int rot;
@@ -43,7 +43,7 @@ struct XStageF8 {
         rot = stage_rot(total);
 #pragma unroll
         for (int j = 0; j < NPRE; j++)
-            v[j] = ldx4(x, (uint32_t)stage_index((int)(threadIdx.x + j * blockDim.x), total, rot));
+            v[j] = ldx4(x, (uint32_t)stage_index((int)threadIdx.x + j * NT, total, rot));
     }
 
     // g is the float4 index read for the workgroup's f-th read.  Out-of-range
@@ -65,11 +65,11 @@ struct XStageF8 {
     {
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
-            const int f = threadIdx.x + j * blockDim.x;
+            const int f = (int)threadIdx.x + j * NT;
             put(v[j], f, stage_index(f, total, rot), total, NU, xl);
         }
         const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
-        for (int f = threadIdx.x + NPRE * blockDim.x; f < total; f += blockDim.x) {
+        for (int f = (int)threadIdx.x + NPRE * NT; f < total; f += NT) {
             const int g = stage_index(f, total, rot);
             put(x4[g], f, g, total, NU, xl);
         }
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+    const int tile = blockIdx.x * QG_FP8_WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const int nit = (NU + LPR - 1) / LPR;
     const int nit_pad = (nit + PF - 1) / PF * PF;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
         wr[r] = w + (size_t)min(row0 + r, O - 1) * I;
 
     // activations first, then the first PF sweeps; every load unconditional
-    XStageF8<8> xst;
+    XStageF8<8, 64 * QG_FP8_WPB> xst;
     const int total4 = S * NU * 4;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+    const int tile = blockIdx.x * QG_I4G_WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const size_t rb = (size_t)I / 2;
     const int nit = (NU + LPR - 1) / LPR;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     // so the compiler can wait for exactly the load a value comes from
     // instead of draining all outstanding loads.
     // 1. activations first (L2-resident)
-    XStageN<S, 8> xst;
+    XStageN<S, 8, 64 * QG_I4G_WPB> xst;
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any

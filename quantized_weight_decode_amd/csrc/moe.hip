@@ -7,22 +7,25 @@
 // experts; colibri PR #457, section 4: routed experts are grouped-int4.)
 //
 // One launch, no host round trip, no atomics:
-//   * a workgroup owns RT consecutive output rows for every token;
-//   * each wave reads the T*K ids (T*K <= 64) into its lanes and derives with
-//     ballots the distinct valid experts (first-occurrence order) and, for
-//     each, the set of tokens that chose it -- the routing never leaves the
-//     device;
+//   * workgroup (t, b) owns token t and RT consecutive output rows; the
+//     T * NB workgroups (NB row blocks per token) cover about one CU each;
+//   * it stages x[t] in LDS as for the dense grouped-int4 GEMV (one vector:
+//     staging every token in every workgroup makes thousands of workgroups
+//     fetch the same lines at once, which costs more than it saves);
+//   * one wave reads the token's K ids and hands them over in LDS; every wave
+//     derives with ballots the distinct valid experts (first-occurrence
+//     order) -- the routing never leaves the device;
 //   * work units are (distinct expert, sub-tile of rows), dealt round-robin
-//     to the waves; a unit streams its rows of that expert once (dwordx4,
-//     scale gather) and forms the dot products of every token that chose it,
-//     with x of all tokens staged in LDS as for the dense grouped-int4 GEMV;
-//     a wave's (unit, sweep) steps form one stream with PF sweeps of loads in
-//     flight, crossing unit boundaries;
-//   * a unit's row sums go to an LDS partial array [T][K][RT] for every slot
-//     (t, k) that selected the expert; after a barrier the workgroup forms
-//     y = sum_k gates * partial in ascending k (deterministic).
+//     to the waves; a unit streams its rows of that expert (dwordx4, scale
+//     gather); a wave's (unit, sweep) steps form one stream with PF sweeps of
+//     loads in flight, crossing unit boundaries;
+//   * a unit's row sums go to an LDS partial array [K][RT] for every slot k
+//     that selected the expert (a duplicated id is streamed once and counted
+//     per slot); after a barrier the workgroup forms y[t] = sum_k gates *
+//     partial in ascending k (deterministic).
+// An expert selected by several tokens is streamed once per selecting token.
 // An id outside [0, E) is never dereferenced: its token's row of y is NaN and
-// the workspace error flag is set.
+// the token's error flag in the workspace is set.
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -43,72 +46,14 @@
 namespace qg {
 
 constexpr int MOE_MAX_T = 8;
-constexpr int MOE_FAST_MAX_TK = 64;
+constexpr int MOE_FAST_MAX_K = 64;
 
-struct Routing {
-    int e;            // this lane's id (lane < T*K), or -1
-    uint64_t first;   // lanes holding the first occurrence of a valid id
-    uint32_t mask;    // on a first-occurrence lane: tokens that chose the id
-    uint32_t bad;     // tokens with an out-of-range id
-    int nu;           // distinct valid experts
-};
-
-// The id of this lane's (token, slot), loaded unconditionally (clamped) so
-// that the load can be issued ahead of others and waited for on its own.
-__device__ __forceinline__ int load_id(const int32_t *__restrict__ ids, int T, int K)
+// Lane holding the ui-th set bit of a wave-uniform lane mask (-1 if none).
+__device__ __forceinline__ int nth_lane(uint64_t m, int ui)
 {
     const int lane = threadIdx.x & 63;
-    return ids[min(lane, T * K - 1)];
-}
-
-// Every lane of the wave calls this with its load_id() value (wave-uniform
-// results except e / mask).
-__device__ __forceinline__ Routing route_ids(int id, int T, int K, int E)
-{
-    const int lane = threadIdx.x & 63;
-    const int TK = T * K;
-    Routing rt;
-    rt.e = lane < TK ? id : -1;
-    const bool in = lane < TK;
-    const bool valid = in && rt.e >= 0 && rt.e < E;
-    bool first = valid;
-    uint32_t mask = 0;
-    // slot q belongs to token tq = q / K, tracked incrementally (a division
-    // per iteration would run on the scalar unit of every wave)
-    for (int q = 0, tq = 0, kq = 0; q < TK; q++) {
-        const int eq = __builtin_amdgcn_readlane(rt.e, q);
-        if (eq == rt.e) {
-            if (q < lane) first = false;
-            mask |= 1u << tq;
-        }
-        if (++kq == K) {
-            kq = 0;
-            ++tq;
-        }
-    }
-    rt.first = __ballot(first);
-    rt.mask = mask;
-    const uint64_t badl = __ballot(in && !valid);
-    uint32_t bad = 0;
-    for (int t = 0; t < T; t++)
-        if ((badl >> (t * K)) & ((K == 64) ? ~0ull : ((1ull << K) - 1))) bad |= 1u << t;
-    rt.bad = bad;
-    rt.nu = __popcll(rt.first);
-    return rt;
-}
-
-__device__ __forceinline__ Routing route(const int32_t *__restrict__ ids, int T, int K, int E)
-{
-    return route_ids(load_id(ids, T, K), T, K, E);
-}
-
-// Lane holding the ui-th distinct expert.
-__device__ __forceinline__ int unique_lane(const Routing &rt, int ui)
-{
-    const int lane = threadIdx.x & 63;
-    const uint64_t below = lane ? (rt.first & ((1ull << lane) - 1)) : 0ull;
-    const int idx = __popcll(below);
-    const uint64_t sel = __ballot(((rt.first >> lane) & 1) && idx == ui);
+    const uint64_t below = lane ? (m & ((1ull << lane) - 1)) : 0ull;
+    const uint64_t sel = __ballot(((m >> lane) & 1) && __popcll(below) == ui);
     return __ffsll((long long)sel) - 1;
 }
 
@@ -117,70 +62,74 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ scales, long long w_stride,
     long long s_stride, int E, const int32_t *__restrict__ ids, const float *__restrict__ gates,
     int T, int K, const float *__restrict__ x, float *__restrict__ y, int I, int O, int ng,
-    Div20 div_cpg, int RT, int *__restrict__ err_flag)
+    Div20 div_cpg, int RT, int NB, int *__restrict__ err_flag)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     constexpr int PF0 = QG_MOE_PF0 < PF ? QG_MOE_PF0 : PF;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [T][8][NS]
-    float *xs = reinterpret_cast<float *>(xl + (size_t)T * 8 * seg_stride(NU));  // [T][NU]
-    float *part = xs + (size_t)T * NU;                               // [T][K][RT]
-    int *ids_l = reinterpret_cast<int *>(part + (size_t)T * K * RT); // [64]
+    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                      // [8][NS]
+    float *xs = reinterpret_cast<float *>(xl + 8 * seg_stride(NU));       // [NU]
+    float *part = xs + NU;                                                // [K][RT]
+    int *ids_l = reinterpret_cast<int *>(part + (size_t)K * RT);          // [64]
 
+    const int t = blockIdx.x / NB;
+    const int o0 = (blockIdx.x - t * NB) * RT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwaves = blockDim.x >> 6;
+    constexpr int nwaves = QG_MOE_WPB;
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int o0 = blockIdx.x * RT;
     const size_t rb = (size_t)I / 2;
     const int nit = (NU + LPR - 1) / LPR;
     const int nsub = RT / ROWS_PER_WAVE;
 
-    // activations of all tokens are requested before any weight; every wave
-    // has issued them before any wave issues a weight load
-    // one wave per workgroup reads the ids (thousands of waves reading the
-    // same line would queue on one L2 channel) and hands them over in LDS
+    // the token's ids (one wave; thousands of waves reading one line would
+    // queue on one L2 channel) and its activations, before any weight load
     int id = 0;
-    if (wave == 0) id = load_id(ids, T, K);
-    const int total4 = T * NU * 8;
-    constexpr int NPRE = 8;
-    f32x4 xv[NPRE];
-    const int rot = stage_rot(total4);
-#pragma unroll
-    for (int j = 0; j < NPRE; j++)
-        xv[j] = ldx4(x, (uint32_t)stage_index((int)(threadIdx.x + j * blockDim.x), total4, rot));
+    if (wave == 0) id = ids[t * K + min(lane, K - 1)];
+    XStageN<1, 8, 64 * QG_MOE_WPB> xst;
+    const int total4 = NU * 8;
+    xst.load(x + (size_t)t * I, total4);
     __builtin_amdgcn_sched_barrier(0);
-
     if (wave == 0) ids_l[lane] = id;
     // raw barrier (the activation loads stay in flight); the LDS write must
     // have landed before it
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const Routing rt = route_ids(ids_l[lane], T, K, E);
-    if (blockIdx.x == 0 && threadIdx.x == 0) err_flag[0] = rt.bad ? 1 : 0;
+
+    // distinct valid experts of the token, first-occurrence order
+    const int e = lane < K ? ids_l[lane] : -1;
+    const bool valid = lane < K && e >= 0 && e < E;
+    bool first = valid;
+    for (int q = 0; q < K; q++)
+        if (q < lane && __builtin_amdgcn_readlane(e, q) == e) first = false;
+    const uint64_t firstm = __ballot(first);
+    const bool bad = __ballot(lane < K && !valid) != 0;
+    if (o0 == 0 && threadIdx.x == 0) {
+        err_flag[t] = bad ? 1 : 0;
+        if (t == 0)
+            for (int u = T; u < MOE_MAX_T; u++) err_flag[u] = 0;
+    }
 
     // this wave's units: i = wave + k * nwaves (k < my_units); a unit is
-    // (distinct expert ui, row sub-tile st); steps s = k * nit + c
-    const int nunits = rt.nu * nsub;
+    // (distinct expert ui, row sub-tile st)
+    const int nunits = __popcll(firstm) * nsub;
     const int my_units = wave < nunits ? (nunits - wave + nwaves - 1) / nwaves : 0;
     const int nsteps = my_units * nit;
     const int nsteps_pad = (nsteps + PF - 1) / PF * PF;
 
     struct Unit {
         int e, row0;
-        uint32_t mask;
     };
     auto unit_of = [&](int k) {
         const int i = wave + k * nwaves;
         const int ui = i / nsub, st = i - ui * nsub;
-        const int ql = unique_lane(rt, ui);
+        const int ql = nth_lane(firstm, ui);
         Unit u;
         // a wave without units still issues its (clamped) prefetch: expert 0
-        u.e = ql >= 0 ? __builtin_amdgcn_readlane(rt.e, ql) : 0;
-        u.mask = ql >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)rt.mask, ql) : 0u;
+        u.e = ql >= 0 ? __builtin_amdgcn_readlane(e, ql) : 0;
         u.row0 = o0 + st * ROWS_PER_WAVE + sub * R;
         return u;
     };
@@ -218,34 +167,15 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
     for (int j = 0; j < PF0; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
-
-    // stage activations
-    const int cpv = NU * 8;
-#pragma unroll
-    for (int j = 0; j < NPRE; j++) {
-        const int f = threadIdx.x + j * blockDim.x;
-        int t, rem;
-        split_f<MOE_MAX_T>(stage_index(f, total4, rot), cpv, t, rem);
-        XStagePut(xv[j], f < total4, t, rem, NU, xl, xs);
-    }
-    const int nrest = (total4 - NPRE * (int)blockDim.x + (int)blockDim.x - 1) / (int)blockDim.x;
-    for (int it = 0; it < nrest; it++) {
-        const int f = threadIdx.x + (NPRE + it) * blockDim.x;
-        const int g = stage_index(f, total4, rot);
-        int t, rem;
-        split_f<MOE_MAX_T>(g, cpv, t, rem);
-        XStagePut(ldx4(x, (uint32_t)g), f < total4, t, rem, NU, xl, xs);
-    }
+    xst.store(x + (size_t)t * I, total4, NU, xl, xs);
     __syncthreads();
 #pragma unroll
     for (int j = PF0; j < PF; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
 
-    float acc[MOE_MAX_T][R];
+    float acc[R];
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_T; t++)
-#pragma unroll
-        for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+    for (int r = 0; r < R; r++) acc[r] = 0.0f;
 
     // consume cursor (unit ck, sweep cc)
     int ck = 0, cc = 0;
@@ -253,20 +183,15 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     auto consume = [&](int s, int j) {
         if (s >= nsteps) return;                       // padding (wave-uniform)
         const int u = cc * LPR + sl;
-        const bool valid = u < NU;
-        const int uu = valid ? u : 0;
+        const bool in_row = u < NU;
+        const int uu = in_row ? u : 0;
+        const float m8xs = -8.0f * xs[uu];
 #pragma unroll
-        for (int t = 0; t < MOE_MAX_T; t++) {
-            if (t < T && ((cu.mask >> t) & 1)) {       // wave-uniform
-                const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
-                const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
-#pragma unroll
-                for (int r = 0; r < R; r++) {
-                    const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
-                    const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
-                    acc[t][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[t][r]);
-                }
-            }
+        for (int r = 0; r < R; r++) {
+            // s * (sum q x - 8 sum x); the chunk dot comes out as 2^-9 sum q x
+            const float p = nib_chunk_dot(wb[j][r], xl, NU, uu);
+            const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
+            acc[r] = __builtin_fmaf(in_row ? sb[j][r] : 0.0f, tv, acc[r]);
         }
         if (cc + 1 < nit) {
             ++cc;
@@ -274,20 +199,13 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         }
         // unit done: row sums -> partials of every slot that chose cu.e
 #pragma unroll
-        for (int t = 0; t < MOE_MAX_T; t++) {
-            if (t < T && ((cu.mask >> t) & 1)) {
-#pragma unroll
-                for (int r = 0; r < R; r++) {
-                    const float v = sub_reduce<LPR>(acc[t][r]);
-                    const int lr = cu.row0 + r - o0;
-                    for (int kk = 0; kk < K; kk++) {
-                        const int ek = __builtin_amdgcn_readlane(rt.e, t * K + kk);
-                        if (ek == cu.e && sl == LPR - 1 && cu.row0 + r < O)
-                            part[((size_t)t * K + kk) * RT + lr] = v;
-                    }
-                    acc[t][r] = 0.0f;
-                }
-            }
+        for (int r = 0; r < R; r++) {
+            const float v = sub_reduce<LPR>(acc[r]);
+            const int lr = cu.row0 + r - o0;
+            for (int kk = 0; kk < K; kk++)
+                if (__builtin_amdgcn_readlane(e, kk) == cu.e && sl == LPR - 1 && cu.row0 + r < O)
+                    part[(size_t)kk * RT + lr] = v;
+            acc[r] = 0.0f;
         }
         cc = 0;
         if (++ck < my_units) cu = unit_of(ck);
@@ -297,8 +215,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     for (int rd = 0; rd + 1 < nrounds; rd++) {
 #pragma unroll
         for (int j = 0; j < PF; j++) {
-            const int s = rd * PF + j;
-            consume(s, j);
+            consume(rd * PF + j, j);
             fetch(j);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -309,18 +226,17 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     }
     __syncthreads();
 
-    // combine in ascending k
-    for (int idx = threadIdx.x; idx < T * RT; idx += blockDim.x) {
-        const int t = idx / RT, i = idx - t * RT;
+    // y[t] = sum_k gates * partial, ascending k
+    for (int i = threadIdx.x; i < RT; i += 64 * QG_MOE_WPB) {
         const int row = o0 + i;
         if (row >= O) continue;
         float v;
-        if ((rt.bad >> t) & 1) {
+        if (bad) {
             v = __builtin_nanf("");
         } else {
             v = 0.0f;
             for (int kk = 0; kk < K; kk++)
-                v = __builtin_fmaf(gates[t * K + kk], part[((size_t)t * K + kk) * RT + i], v);
+                v = __builtin_fmaf(gates[t * K + kk], part[(size_t)kk * RT + i], v);
         }
         y[(size_t)t * O + row] = v;
     }
@@ -329,7 +245,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 // General kernel: any shape the streaming kernel does not take (T*K > 64,
 // unaligned rows or strides, LDS too small).  One wave per output row; each
 // (t, k) dot product is formed from per-weight f32 decodes, combined in
-// ascending k.  Also sets the error flag (block 0).
+// ascending k.  Also sets the per-token error flags (block 0).
 __global__ __launch_bounds__(256) void moe_i4g_general(
     const uint8_t *__restrict__ w, const float *__restrict__ scales, long long w_stride,
     long long s_stride, int E, const int32_t *__restrict__ ids, const float *__restrict__ gates,
@@ -338,10 +254,12 @@ __global__ __launch_bounds__(256) void moe_i4g_general(
 {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (blockIdx.x == 0 && threadIdx.x < MOE_MAX_T) {
+        const int tt = threadIdx.x;
         int bad = 0;
-        for (int p = 0; p < T * K; p++) bad |= (ids[p] < 0 || ids[p] >= E);
-        err_flag[0] = bad;
+        if (tt < T)
+            for (int kk = 0; kk < K; kk++) bad |= (ids[tt * K + kk] < 0 || ids[tt * K + kk] >= E);
+        err_flag[tt] = bad;
     }
     if (row >= O) return;
     const int rb = (I + 1) / 2;
@@ -373,25 +291,34 @@ __global__ __launch_bounds__(256) void moe_i4g_general(
 
 namespace {
 
-size_t moe_lds_bytes(int T, int K, int I, int RT)
+size_t moe_lds_bytes(int K, int I, int RT)
 {
-    return (size_t)T * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float)) +
-           (size_t)T * K * RT * sizeof(float) + 64 * sizeof(int);
+    return (size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float) +
+           (size_t)K * RT * sizeof(float) + 64 * sizeof(int);
+}
+
+// Row blocks: about one workgroup per CU over all T tokens, RT rows each (a
+// multiple of the wave tile rpw).
+void moe_blocks(int T, int O, int rpw, int &RT, int &NB)
+{
+    const int want = (256 + T - 1) / T;
+    const int per = (O + want - 1) / want;
+    RT = (per + rpw - 1) / rpw * rpw;
+    NB = (O + RT - 1) / RT;
 }
 
 template <int LPR, int R>
 hipError_t launch_t(const uint8_t *w, const float *s, long long ws, long long ss, int E,
                     const int32_t *ids, const float *gates, int T, int K, const float *x,
-                    float *y, int I, int O, int gs, int RT, int *err, hipStream_t st)
+                    float *y, int I, int O, int gs, int RT, int NB, int *err, hipStream_t st)
 {
-    const size_t lds = moe_lds_bytes(T, K, I, RT);
+    const size_t lds = moe_lds_bytes(K, I, RT);
     auto kern = moe_i4g_stream<LPR, R, QG_MOE_PF>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    const int blocks = (O + RT - 1) / RT;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * QG_MOE_WPB), lds, st, w, s, ws, ss, E, ids,
+    hipLaunchKernelGGL(kern, dim3(T * NB), dim3(64 * QG_MOE_WPB), lds, st, w, s, ws, ss, E, ids,
                        gates, T, K, x, y, I, O, (I + gs - 1) / gs,
-                       Div20::make((uint32_t)(gs / 32)), RT, err);
+                       Div20::make((uint32_t)(gs / 32)), RT, NB, err);
     return hipGetLastError();
 }
 
@@ -404,21 +331,19 @@ hipError_t launch_moe_topk(const void *w, const float *scales, long long w_strid
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const int lpr = pick_lpr(I / 32 > 0 ? I / 32 : 1);
-    const int R = QG_MOE_R;
-    const int rpw = (WAVE / lpr) * R;
-    // rows per workgroup: a multiple of the wave tile, about one workgroup per CU
-    const int per_cu = (O + 255) / 256;
-    const int RT = ((per_cu + rpw - 1) / rpw) * rpw;
-    const bool fast = T * K <= MOE_FAST_MAX_TK && I % 32 == 0 && gs % 32 == 0 &&
+    const int rpw = (WAVE / lpr) * QG_MOE_R;
+    int RT, NB;
+    moe_blocks(T, O, rpw, RT, NB);
+    const bool fast = K <= MOE_FAST_MAX_K && I % 32 == 0 && gs % 32 == 0 &&
                       ((uintptr_t)w & 15) == 0 && (w_stride & 15) == 0 &&
-                      ((uintptr_t)x & 15) == 0 && moe_lds_bytes(T, K, I, RT) <= LDS_BUDGET;
+                      ((uintptr_t)x & 15) == 0 && moe_lds_bytes(K, I, RT) <= LDS_BUDGET;
     if (fast) {
         switch (lpr) {
-        case 64: return launch_t<64, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
-        case 32: return launch_t<32, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
-        case 16: return launch_t<16, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
-        case 8: return launch_t<8, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
-        default: return launch_t<4, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, err_flag, st);
+        case 64: return launch_t<64, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
+        case 32: return launch_t<32, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
+        case 16: return launch_t<16, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
+        case 8: return launch_t<8, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
+        default: return launch_t<4, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
         }
     }
     const int wpb = 4;

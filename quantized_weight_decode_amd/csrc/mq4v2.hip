@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+    const int tile = blockIdx.x * QG_MQ4_WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const size_t rowbytes = (size_t)(I / 256) * MQ4_GROUP_BYTES;
     const int nit = (NU + LPR - 1) / LPR;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
 
-    XStageN<S, 8> xst;
+    XStageN<S, 8, 64 * QG_MQ4_WPB> xst;
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any

@@ -169,8 +169,10 @@ __device__ __forceinline__ int stage_index(int f, int total, int rot)
 // formed with an 8-lane DPP reduction.  load() issues NPRE float4s per thread
 // unconditionally (indices clamped into range) and store() consumes them
 // unconditionally, so a caller that issues the weight stream in between
-// waits for exactly these loads.  blockDim.x must be a multiple of 64.
-template <int S, int NPRE>
+// waits for exactly these loads.  NT is the workgroup size (a multiple of
+// 64), a compile-time constant: reading blockDim.x would cost a dependent
+// memory load before the first activation load could issue.
+template <int S, int NPRE, int NT>
 struct XStageN {
     f32x4 v[NPRE];
 
@@ -181,7 +183,7 @@ struct XStageN {
         rot = stage_rot(total);
 #pragma unroll
         for (int j = 0; j < NPRE; j++)
-            v[j] = ldx4(x, (uint32_t)stage_index((int)(threadIdx.x + j * blockDim.x), total, rot));
+            v[j] = ldx4(x, (uint32_t)stage_index((int)threadIdx.x + j * NT, total, rot));
     }
 
     __device__ __forceinline__ void store(const float *__restrict__ x, int total, int NU,
@@ -190,15 +192,15 @@ struct XStageN {
         const int cpv = NU * 8;
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
-            const int f = threadIdx.x + j * blockDim.x;
+            const int f = (int)threadIdx.x + j * NT;
             int t, rem;
             split_f<S>(stage_index(f, total, rot), cpv, t, rem);
             XStagePut(v[j], f < total, t, rem, NU, xl, xs);
         }
         // remainder (shapes with more than NPRE float4s per thread)
-        const int nrest = (total - NPRE * (int)blockDim.x + (int)blockDim.x - 1) / (int)blockDim.x;
+        const int nrest = (total - NPRE * NT + NT - 1) / NT;
         for (int it = 0; it < nrest; it++) {
-            const int f = threadIdx.x + (NPRE + it) * blockDim.x;
+            const int f = (int)threadIdx.x + (NPRE + it) * NT;
             const int g = stage_index(f, total, rot);
             int t, rem;
             split_f<S>(g, cpv, t, rem);
