@@ -16,14 +16,24 @@
 #include "qg_device.h"
 #include "qg_launch.h"
 
+// Tile shape of the streaming kernel: R rows per lane group, PF sweeps in
+// flight, WPB waves per workgroup.  At O = 7168, I = 16384 the 3584 two-row
+// waves form 512 workgroups, two per CU (two 64 KB activation copies fit the
+// LDS), so every CU gets the same share.
 #ifndef QG_FP8_R
-#define QG_FP8_R 1
+#define QG_FP8_R 2
 #endif
 #ifndef QG_FP8_PF
 #define QG_FP8_PF 4
 #endif
 #ifndef QG_FP8_WPB
-#define QG_FP8_WPB 8
+#define QG_FP8_WPB 7
+#endif
+// sweeps issued before the activations are staged (at most PF).  Unlike the
+// nibble formats, the fp8 stream is faster with its first round of weight
+// loads in flight while the (larger) activation vector is staged.
+#ifndef QG_FP8_PF0
+#define QG_FP8_PF0 4
 #endif
 
 namespace qg {
@@ -100,6 +110,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     float *__restrict__ y, int I, int O, int nbi, int ntiles)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    constexpr int PF0 = QG_FP8_PF0 < PF ? QG_FP8_PF0 : PF;
     static_assert(128 % R == 0, "a lane group's rows must share one 128-row band");
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 16;
@@ -120,32 +131,37 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * I;
 
-    // activations first, then the first PF sweeps; every load unconditional
+    // activations first; every load unconditional
     XStageF8<8, 64 * QG_FP8_WPB> xst;
     const int total4 = S * NU * 4;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any
-    // wave issues weight loads: the per-CU memory queue is in order, so the
-    // staging never waits behind the weight stream (raw barrier: no drain)
+    // wave issues weight loads (raw barrier: no drain)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
+    // only PF0 sweeps go out before the activations are staged: a flood of
+    // streaming weight requests is served ahead of the activation reads
     u32x4 wb[PF][R];
     float sb[PF];
-#pragma unroll
-    for (int j = 0; j < PF; j++) {
-        const int u = min(j * LPR + sl, NU - 1);
+    auto fetch = [&](int c, int j) {
+        const int u = min(c * LPR + sl, NU - 1);
 #pragma unroll
         for (int r = 0; r < R; r++)
             wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
         sb[j] = ld_stream(&scrow[u >> 3]);
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < PF0; j++) fetch(j, j);
 
     __builtin_amdgcn_sched_barrier(0);
     xst.store(x, total4, NU, xl);
     __syncthreads();
     if (tile >= ntiles) return;
+#pragma unroll
+    for (int j = PF0; j < PF; j++) fetch(j, j);
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
 #pragma unroll
