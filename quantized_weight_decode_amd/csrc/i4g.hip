@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     // so the compiler can wait for exactly the load a value comes from
     // instead of draining all outstanding loads.
     // 1. activations first (L2-resident)
-    XStageN<S, 8, 64 * QG_I4G_WPB> xst;
+    XStageN<S, 6, 64 * QG_I4G_WPB> xst;
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any

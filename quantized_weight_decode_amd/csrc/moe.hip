@@ -15,10 +15,11 @@
 //   * one wave reads the token's K ids and hands them over in LDS; every wave
 //     derives with ballots the distinct valid experts (first-occurrence
 //     order) -- the routing never leaves the device;
-//   * work units are (distinct expert, sub-tile of rows), dealt round-robin
-//     to the waves; a unit streams its rows of that expert (dwordx4, scale
-//     gather); a wave's (unit, sweep) steps form one stream with PF sweeps of
-//     loads in flight, crossing unit boundaries;
+//   * work units are (distinct expert, sub-tile of rows); each wave starts
+//     on one and takes the next free one from an LDS counter when it is
+//     done; a unit streams its rows of that expert (dwordx4, scale gather);
+//     a wave's (unit, sweep) steps form one stream with PF sweeps of loads in
+//     flight, crossing unit boundaries;
 //   * a unit's row sums go to an LDS partial array [K][RT] for every slot k
 //     that selected the expert (a duplicated id is streamed once and counted
 //     per slot); after a barrier the workgroup forms y[t] = sum_k gates *
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     float *xs = reinterpret_cast<float *>(xl + 8 * seg_stride(NU));       // [NU]
     float *part = xs + NU;                                                // [K][RT]
     int *ids_l = reinterpret_cast<int *>(part + (size_t)K * RT);          // [64]
+    int *ctr = ids_l + 64;                                                // next unit
 
     const int t = blockIdx.x / NB;
     const int o0 = (blockIdx.x - t * NB) * RT;
@@ -88,11 +90,12 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     // queue on one L2 channel) and its activations, before any weight load
     int id = 0;
     if (wave == 0) id = ids[t * K + min(lane, K - 1)];
-    XStageN<1, 8, 64 * QG_MOE_WPB> xst;
+    XStageN<1, 2, 64 * QG_MOE_WPB> xst;
     const int total4 = NU * 8;
     xst.load(x + (size_t)t * I, total4);
     __builtin_amdgcn_sched_barrier(0);
     if (wave == 0) ids_l[lane] = id;
+    if (threadIdx.x == 0) *ctr = nwaves;
     // raw barrier (the activation loads stay in flight); the LDS write must
     // have landed before it
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -113,36 +116,41 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
             for (int u = T; u < MOE_MAX_T; u++) err_flag[u] = 0;
     }
 
-    // this wave's units: i = wave + k * nwaves (k < my_units); a unit is
-    // (distinct expert ui, row sub-tile st)
+    // Work units are (distinct expert ui, row sub-tile st), numbered
+    // i = ui * nsub + st.  Wave w starts on unit w; each later unit goes to
+    // whichever wave asks first (an LDS counter), so waves that the SIMDs
+    // serve faster take more units and the workgroup finishes together.
     const int nunits = __popcll(firstm) * nsub;
-    const int my_units = wave < nunits ? (nunits - wave + nwaves - 1) / nwaves : 0;
-    const int nsteps = my_units * nit;
-    const int nsteps_pad = (nsteps + PF - 1) / PF * PF;
 
     struct Unit {
         int e, row0;
     };
-    auto unit_of = [&](int k) {
-        const int i = wave + k * nwaves;
+    auto unit_of = [&](int i) {
         const int ui = i / nsub, st = i - ui * nsub;
         const int ql = nth_lane(firstm, ui);
         Unit u;
-        // a wave without units still issues its (clamped) prefetch: expert 0
-        u.e = ql >= 0 ? __builtin_amdgcn_readlane(e, ql) : 0;
+        // past the last unit (or none): expert 0, so clamped loads stay valid
+        u.e = ql >= 0 && i < nunits ? __builtin_amdgcn_readlane(e, ql) : 0;
         u.row0 = o0 + st * ROWS_PER_WAVE + sub * R;
         return u;
+    };
+    auto grab = [&]() {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(ctr, 1);
+        return __builtin_amdgcn_readfirstlane(v);
     };
 
     u32x4 wb[PF][R];
     float sb[PF][R];
-    // fetch cursor (unit fk, sweep fc): the step whose loads are issued next.
-    // It stops on the wave's last step, so the padded tail of the stream
-    // re-issues that step's loads instead of branching around them.
-    const Unit u0 = unit_of(0);
-    int fk = 0, fc = 0;
-    Unit fu = u0;
+    // each ring slot records the unit and sweep its loads belong to
+    // (unit >= nunits: nothing, the loads re-read the previous step)
+    int slot_u[PF], slot_c[PF];
+    // fetch cursor: unit fi, sweep fc
+    int fi = wave, fc = 0;
+    Unit fu = unit_of(min(fi, nunits > 0 ? nunits - 1 : 0));
     auto fetch = [&](int j) {
+        slot_u[j] = fi;
+        slot_c[j] = fc;
         const uint8_t *we = w + (size_t)fu.e * (size_t)w_stride;
         const float *se = scales + (size_t)fu.e * (size_t)s_stride;
         const int u = min(fc * LPR + sl, NU - 1);
@@ -154,11 +162,19 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
                                                                  (uint32_t)u * 16u));
             sb[j][r] = ld_stream(se + (size_t)row * ng + g);
         }
-        if (fc + 1 < nit) {
-            ++fc;
-        } else if (fk + 1 < my_units) {
-            fc = 0;
-            fu = unit_of(++fk);
+        if (fi < nunits) {
+            if (fc + 1 < nit) {
+                ++fc;
+            } else {
+                const int nx = grab();
+                if (nx < nunits) {
+                    fi = nx;
+                    fc = 0;
+                    fu = unit_of(fi);
+                } else {
+                    fi = nunits;   // done; keep re-reading the last step
+                }
+            }
         }
     };
 
@@ -177,12 +193,10 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
     for (int r = 0; r < R; r++) acc[r] = 0.0f;
 
-    // consume cursor (unit ck, sweep cc)
-    int ck = 0, cc = 0;
-    Unit cu = u0;
-    auto consume = [&](int s, int j) {
-        if (s >= nsteps) return;                       // padding (wave-uniform)
-        const int u = cc * LPR + sl;
+    auto consume = [&](int j) {
+        const int ci = slot_u[j];
+        if (ci >= nunits) return;                      // nothing (wave-uniform)
+        const int u = slot_c[j] * LPR + sl;
         const bool in_row = u < NU;
         const int uu = in_row ? u : 0;
         const float m8xs = -8.0f * xs[uu];
@@ -193,11 +207,9 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
             const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
             acc[r] = __builtin_fmaf(in_row ? sb[j][r] : 0.0f, tv, acc[r]);
         }
-        if (cc + 1 < nit) {
-            ++cc;
-            return;
-        }
-        // unit done: row sums -> partials of every slot that chose cu.e
+        if (slot_c[j] + 1 < nit) return;
+        // unit done: row sums -> partials of every slot that chose its expert
+        const Unit cu = unit_of(ci);
 #pragma unroll
         for (int r = 0; r < R; r++) {
             const float v = sub_reduce<LPR>(acc[r]);
@@ -207,22 +219,17 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
                     part[(size_t)kk * RT + lr] = v;
             acc[r] = 0.0f;
         }
-        cc = 0;
-        if (++ck < my_units) cu = unit_of(ck);
     };
 
-    const int nrounds = nsteps_pad / PF;
-    for (int rd = 0; rd + 1 < nrounds; rd++) {
+    // rounds of PF slots: consume a slot, then refill it; stop once the
+    // oldest slot of a round holds nothing (slots are filled in order)
+    while (slot_u[0] < nunits) {
 #pragma unroll
         for (int j = 0; j < PF; j++) {
-            consume(rd * PF + j, j);
+            consume(j);
             fetch(j);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    if (nrounds > 0) {
-#pragma unroll
-        for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
     }
     __syncthreads();
 
@@ -294,7 +301,7 @@ namespace {
 size_t moe_lds_bytes(int K, int I, int RT)
 {
     return (size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float) +
-           (size_t)K * RT * sizeof(float) + 64 * sizeof(int);
+           (size_t)K * RT * sizeof(float) + 65 * sizeof(int);
 }
 
 // Row blocks: about one workgroup per CU over all T tokens, RT rows each (a
