@@ -18,13 +18,17 @@
 #include "qg_launch.h"
 
 #ifndef QG_MQ4_R
-#define QG_MQ4_R 4
+#define QG_MQ4_R 2
 #endif
 #ifndef QG_MQ4_PF
-#define QG_MQ4_PF 2
+#define QG_MQ4_PF 4
 #endif
 #ifndef QG_MQ4_WPB
 #define QG_MQ4_WPB 4
+#endif
+// sweeps issued before the activations are staged (at most PF)
+#ifndef QG_MQ4_PF0
+#define QG_MQ4_PF0 0
 #endif
 
 namespace qg {
@@ -46,6 +50,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int I,
     int O, int ntiles)
 {
+    constexpr int PF0 = QG_MQ4_PF0 < PF ? QG_MQ4_PF0 : PF;
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
@@ -71,8 +76,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any
-    // wave issues weight loads: the per-CU memory queue is in order, so the
-    // staging never waits behind the weight stream (raw barrier: no drain)
+    // wave issues weight loads (raw barrier: no drain)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -90,13 +94,18 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
 
     u32x4 wb[PF][R];
     uint32_t hb[PF][R];
+    // only PF0 sweeps go out before the activations are staged: a flood of
+    // streaming weight requests is served ahead of the activation reads
 #pragma unroll
-    for (int j = 0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
+    for (int j = 0; j < PF0; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
 
     __builtin_amdgcn_sched_barrier(0);
     xst.store(x, total4, NU, xl, xs);
     __syncthreads();
     if (tile >= ntiles) return;
+#pragma unroll
+    for (int j = PF0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
 #pragma unroll
