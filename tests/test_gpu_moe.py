@@ -3,8 +3,10 @@
 y[t] = sum_k gates[t][k] * W_{ids[t][k]} x[t] over grouped-int4 experts
 (regolith audit, section 2.2; colibri PR #457, section 4).  Includes the
 workload shape (256 experts of 2048x7168, gs 64, 4 tokens, top-8) checked on
-sampled rows, duplicate ids, an out-of-range id (NaN row plus the error
-flag) and the general kernel (T*K > 64, odd I).
+sampled rows, duplicate ids, experts shared by every token, K = E = 64,
+shapes smaller than one tile, out-of-range ids (NaN row plus the error flag,
+which each call resets), bitwise repeatability under the dynamic unit
+hand-out, and the general kernel (odd I, gs not a multiple of 32).
 """
 import numpy as np
 import pytest
@@ -77,3 +79,70 @@ def test_general_kernel(q, qref, E, O, I, gs, T, K):
     y, err = run(q, d)
     assert err == 0
     assert_y_close(y, oracle_y(qref, d))
+
+
+def test_experts_shared_by_every_token(q, qref):
+    # every token selects the same experts (in its own order): each token's
+    # workgroups stream them for that token
+    d = W.gen_moe(20, 128, 1024, 64, 4, 6, seed=21)
+    rng = np.random.default_rng(21)
+    for t in range(1, 4):
+        d["ids"][t] = rng.permutation(d["ids"][0])
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))
+
+
+def test_every_expert_selected(q, qref):
+    # K = 64 = E: one token selects all experts
+    d = W.gen_moe(64, 96, 512, 64, 1, 64, seed=22)
+    d["ids"][0] = np.random.default_rng(22).permutation(64).astype(np.int32)
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))
+
+
+def test_tiny_shapes(q, qref):
+    # fewer rows than one wave tile, one lane chunk per row
+    d = W.gen_moe(4, 3, 32, 32, 2, 2, seed=23)
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))
+
+
+def test_token_with_only_bad_ids(q, qref):
+    d = W.gen_moe(10, 64, 512, 64, 3, 4, seed=24)
+    d["ids"][0] = [-1, 10, 11, 99]
+    y, err = run(q, d)
+    assert err == 1
+    assert np.isnan(y[0]).all() and np.isfinite(y[1:]).all()
+    assert_y_close(y[1:], oracle_y(qref, d)[1:])
+
+
+def test_error_flag_is_per_call(q, qref):
+    # a flagged call followed by clean calls on the same workspace, including
+    # one with fewer tokens than the flagged one
+    ws = q.moe_topk_workspace(8, 4, 64, "cuda")
+    bad = W.gen_moe(10, 64, 512, 64, 8, 4, seed=25)
+    bad["ids"][7, 3] = 12
+    good = W.gen_moe(10, 64, 512, 64, 2, 4, seed=26)
+
+    def call(d):
+        y = q.moe_topk(dev(d["w"]), dev(d["scales"]), dev(d["ids"]), dev(d["gates"]),
+                       dev(d["x"]), d["gs"], workspace=ws)
+        return host(y), q.moe_topk_error(ws)
+
+    assert call(bad)[1] == 1
+    y, err = call(good)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, good))
+
+
+def test_repeated_calls_are_bitwise_identical(q):
+    # units are handed out dynamically; the result must not depend on which
+    # wave computed which unit
+    d = W.gen_moe(32, 512, 2048, 64, 4, 8, seed=27)
+    a, _ = run(q, d)
+    for _ in range(3):
+        b, _ = run(q, d)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
