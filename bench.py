@@ -5,6 +5,8 @@ A step is one pass of the hot path over one batch of synthetic input:
 
   i4g_O12288_I6144_gs64 (default), i4g_O12288_I6144_gs128:
       one qgemv_i4g call (grouped int4, one activation vector)
+  i4g_O12288_I6144_gs64_S2, _S4:
+      one qgemv_i4g call on 2 or 4 activation vectors (multi-token decode)
   fp8b128_O7168_I16384:
       one qgemv_fp8b128 call
   mq4v2_O8192_I8192:
@@ -71,17 +73,17 @@ def _rel(got, ref):
 class I4G(Case):
     kernel = "i4g_gemv_stream"
 
-    def __init__(self, O, I, gs, torch, q, o):
+    def __init__(self, O, I, gs, torch, q, o, S=1):
         import workloads as W
-        self.name = f"i4g_O{O}_I{I}_gs{gs}"
-        self.fmt_desc = "grouped int4, f32 scale per group"
-        self.O, self.I, self.gs = O, I, gs
+        self.name = f"i4g_O{O}_I{I}_gs{gs}" + (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = "grouped int4, f32 scale per group" + (f", {S} vectors per call" if S > 1 else "")
+        self.O, self.I, self.gs, self.S = O, I, gs, S
         rb, ng = (I + 1) // 2, (I + gs - 1) // gs
         self.weight_bytes = O * rb + O * ng * 4
-        self.alg_bytes = self.weight_bytes + I * 4 + O * 4
+        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4)
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
-        d = W.gen_i4g(O, I, gs, seed=0)
+        d = W.gen_i4g(O, I, gs, S=S, seed=0)
         self.n = n_copies(self.weight_bytes)
         g = torch.Generator(device=dev)
         g.manual_seed(1)
@@ -92,7 +94,7 @@ class I4G(Case):
                                          generator=g))
             self.ss.append(0.002 + 0.018 * torch.rand(d["scales"].shape, device=dev, generator=g))
         self.x = torch.from_numpy(d["x"]).to(dev)
-        self.y = torch.empty((1, O), dtype=torch.float32, device=dev)
+        self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
         self.step(0)
@@ -102,8 +104,8 @@ class I4G(Case):
 
     def step(self, i):
         wp, spp = self.ptrs[i % self.n]
-        st = self.q.qgemv_i4g(wp, spp, self.x.data_ptr(), self.y.data_ptr(), 1, self.I, self.O,
-                              self.gs, self.sp)
+        st = self.q.qgemv_i4g(wp, spp, self.x.data_ptr(), self.y.data_ptr(), self.S, self.I,
+                              self.O, self.gs, self.sp)
         if st:
             raise SystemExit(f"qgemv_i4g: {self.q.strerror(st)}")
 
@@ -134,7 +136,7 @@ class FP8(Case):
             self.ss.append(torch.exp(np.log(1e-4) + (np.log(1e-2) - np.log(1e-4)) *
                                      torch.rand((nbo, nbi), device=dev, generator=g)))
         self.x = torch.from_numpy(d["x"]).to(dev)
-        self.y = torch.empty((1, O), dtype=torch.float32, device=dev)
+        self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
         self.step(0)
@@ -271,12 +273,15 @@ def build_case(name, torch, q, o):
         "mq4v2_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o),
         "moe_E256_O2048_I7168_gs64_T4_K8": lambda: MoE(256, 2048, 7168, 64, 4, 8, torch, q, o),
         "i4g_O256_I512_gs64": lambda: I4G(256, 512, 64, torch, q, o),
+        "i4g_O12288_I6144_gs64_S2": lambda: I4G(12288, 6144, 64, torch, q, o, S=2),
+        "i4g_O12288_I6144_gs64_S4": lambda: I4G(12288, 6144, 64, torch, q, o, S=4),
     }
     return table[name]()
 
 
 CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_I16384",
-              "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64"]
+              "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64",
+              "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4"]
 
 
 KERNEL_SOURCES = {
@@ -418,7 +423,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": case.name, "batch": 1, "format": case.fmt_desc,
+        "config": {"workload": case.name, "batch": getattr(case, "S", 1), "format": case.fmt_desc,
                    "alg_bytes_per_step": round(step_bytes)},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "weights_gbs": round(wgbs, 1),

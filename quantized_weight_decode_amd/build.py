@@ -26,12 +26,30 @@ def sources():
 
 
 def build(out: str = LIB, extra=()) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *HIPFLAGS, *extra, *sources(), "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building " + out)
+    """Compiles every source to an object in parallel, then links the library."""
+    import concurrent.futures
+    import tempfile
+    flags = [f for f in HIPFLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="qgemv_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            r = subprocess.run([HIPCC, *flags, *extra, "-c", src, "-o", obj],
+                               capture_output=True, text=True)
+            return src, obj, r
+        jobs = max(1, min(len(sources()), os.cpu_count() or 1))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(compile_one, sources()))
+        for src, _, r in results:
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError("hipcc failed compiling " + src)
+        tmp = out + ".tmp"
+        r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                            *[o for _, o, _ in results], "-o", tmp],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking " + out)
     os.replace(tmp, out)
     return out
 

@@ -23,6 +23,23 @@ hipError_t set_max_lds(const void *kernel, size_t bytes)
     return e;
 }
 
+int cu_count()
+{
+    // per device, looked up once (256 on MI355X)
+    static std::mutex mu;
+    static std::unordered_map<int, int> cus;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cus.find(dev);
+    if (it != cus.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    cus[dev] = n;
+    return n;
+}
+
 }  // namespace qg
 
 namespace {

@@ -28,6 +28,12 @@ namespace qg {
 #ifndef QG_I4G_WPB
 #define QG_I4G_WPB 4
 #endif
+// Waves per workgroup for several vectors: the staged activations take S
+// times the LDS, so fewer workgroups fit a CU and each must hold more waves.
+#ifndef QG_I4G_WPB_MULTI
+#define QG_I4G_WPB_MULTI 16
+#endif
+
 // chunk-sweeps issued before the activations are staged (at most PF)
 #ifndef QG_I4G_PF0
 #define QG_I4G_PF0 0
@@ -37,8 +43,8 @@ namespace qg {
 // goes through the general kernel.
 constexpr int I4G_FAST_MAX_S = 4;
 
-template <int S, int LPR, int R, int PF>
-__global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
+template <int S, int LPR, int R, int PF, int WPB>
+__global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ scales,
     const float *__restrict__ x, float *__restrict__ y, int I, int O, int ng,
     Div20 div_cpg, int ntiles)
@@ -54,7 +60,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int tile = blockIdx.x * QG_I4G_WPB + wave;
+    const int tile = blockIdx.x * WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const size_t rb = (size_t)I / 2;
     const int nit = (NU + LPR - 1) / LPR;
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
     // so the compiler can wait for exactly the load a value comes from
     // instead of draining all outstanding loads.
     // 1. activations first (L2-resident)
-    XStageN<S, 6, 64 * QG_I4G_WPB> xst;
+    XStageN<S, 6, 64 * WPB> xst;
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any
@@ -126,16 +132,31 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
         const int u = c * LPR + sl;
         const bool valid = u < NU;
         const int uu = valid ? u : 0;
-#pragma unroll
-        for (int t = 0; t < S; t++) {
-            const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
-            const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
+        if constexpr (S == 1) {
+            const float m8xs = -8.0f * xs[uu];
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 // s * (sum q x - 8 sum x); the chunk dot comes out as 2^-9 sum q x
-                const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                const float p = nib_chunk_dot(wb[j][r], xl, NU, uu);
                 const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
-                acc[t][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[t][r]);
+                acc[0][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[0][r]);
+            }
+        } else {
+            // Several vectors: the select form below makes the compiler run
+            // each (vector, row) dot under its own lane mask, one after the
+            // other.  Written as a multiply by a zeroed scale, every vector's
+            // activations and every row's decode get scheduled up front,
+            // which takes the whole register file (one wave per SIMD).
+#pragma unroll
+            for (int t = 0; t < S; t++) {
+                const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
+                const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
+                    const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
+                    acc[t][r] = valid ? __builtin_fmaf(sb[j][r], tv, acc[t][r]) : acc[t][r];
+                }
             }
         }
     };
@@ -150,7 +171,10 @@ __global__ __launch_bounds__(64 * QG_I4G_WPB) void i4g_gemv_stream(
         }
     }
 #pragma unroll
-    for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
+    for (int j = 0; j < PF; j++) {
+        consume((nrounds - 1) * PF + j, j);
+        __builtin_amdgcn_sched_barrier(0);   // one slot at a time, as in the loop
+    }
 
 #pragma unroll
     for (int t = 0; t < S; t++)
@@ -235,10 +259,11 @@ hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, flo
     const int ng = (I + gs - 1) / gs;
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
-    const int waves_per_block = QG_I4G_WPB;
+    constexpr int WPB = S == 1 ? QG_I4G_WPB : QG_I4G_WPB_MULTI;
+    const int waves_per_block = WPB;
     const int blocks = (ntiles + waves_per_block - 1) / waves_per_block;
     const size_t lds = i4g_stream_lds_bytes(S, I);
-    auto kern = i4g_gemv_stream<S, LPR, R, PF>;
+    auto kern = i4g_gemv_stream<S, LPR, R, PF, WPB>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves_per_block), lds, st, w, s, x, y,
@@ -269,18 +294,56 @@ hipError_t launch_stream_pf(const uint8_t *w, const float *s, const float *x, fl
     }
 }
 
-template <int S>
-hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, float *y,
-                           int I, int O, int gs, hipStream_t st)
+template <int S, int R>
+hipError_t launch_stream_r(const uint8_t *w, const float *s, const float *x, float *y, int I,
+                           int O, int gs, hipStream_t st)
 {
-    // R rows of a lane group share each activation read from LDS
-    constexpr int R = S <= 2 ? QG_I4G_R : 2;
     switch (pick_lpr(I / 32)) {
     case 64: return launch_stream_pf<S, 64, R>(w, s, x, y, I, O, gs, st);
     case 32: return launch_stream_pf<S, 32, R>(w, s, x, y, I, O, gs, st);
     case 16: return launch_stream_pf<S, 16, R>(w, s, x, y, I, O, gs, st);
     case 8: return launch_stream_pf<S, 8, R>(w, s, x, y, I, O, gs, st);
     default: return launch_stream_pf<S, 4, R>(w, s, x, y, I, O, gs, st);
+    }
+}
+
+// Rows per lane group for several vectors.  The staged activations take S
+// times the LDS, so few workgroups fit a CU; R is picked so that all
+// workgroups are resident at once and the most loaded CU has the fewest rows
+// (e.g. 12288 rows, S = 2 or 4: R = 3, 256 workgroups of 48 rows).
+int pick_r_multi(int S, int I, int O)
+{
+    const int lpr = pick_lpr(I / 32);
+    const size_t lds = i4g_stream_lds_bytes(S, I);
+    int per_cu = (int)(LDS_BUDGET / lds);
+    per_cu = per_cu < 1 ? 1 : per_cu;
+    const int by_waves = 32 / QG_I4G_WPB_MULTI;
+    per_cu = per_cu < by_waves ? per_cu : by_waves;
+    const long ncu = cu_count();
+    int best = 4;
+    long best_rows = -1;
+    for (int r = 1; r <= 4; r++) {
+        const long rows_wg = (long)QG_I4G_WPB_MULTI * (WAVE / lpr) * r;
+        const long wgs = (O + rows_wg - 1) / rows_wg;
+        const long wg_per_cu = (wgs + ncu - 1) / ncu;
+        if (wg_per_cu > per_cu) continue;                 // more than one round
+        const long rows = wg_per_cu * rows_wg;
+        if (best_rows < 0 || rows < best_rows) { best_rows = rows; best = r; }
+    }
+    return best;
+}
+
+template <int S>
+hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, float *y,
+                           int I, int O, int gs, hipStream_t st)
+{
+    // R rows of a lane group share each activation read from LDS
+    if (S == 1) return launch_stream_r<S, QG_I4G_R>(w, s, x, y, I, O, gs, st);
+    switch (pick_r_multi(S, I, O)) {
+    case 1: return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
+    case 2: return launch_stream_r<S, 2>(w, s, x, y, I, O, gs, st);
+    case 3: return launch_stream_r<S, 3>(w, s, x, y, I, O, gs, st);
+    default: return launch_stream_r<S, 4>(w, s, x, y, I, O, gs, st);
     }
 }
 

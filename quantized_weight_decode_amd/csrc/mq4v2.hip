@@ -147,7 +147,10 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
         }
     }
 #pragma unroll
-    for (int j = 0; j < PF; j++) consume((nrounds - 1) * PF + j, j);
+    for (int j = 0; j < PF; j++) {
+        consume((nrounds - 1) * PF + j, j);
+        __builtin_amdgcn_sched_barrier(0);   // one slot at a time, as in the loop
+    }
 
 #pragma unroll
     for (int t = 0; t < S; t++)

@@ -232,6 +232,7 @@ __device__ __forceinline__ float nib_chunk_dot(const u32x4 wv, const f32x4 *__re
     return p0 + p1;
 }
 
+
 // ---------------------------------------------------------------------------
 // Sub-wave sum over LPR consecutive lanes (LPR in 4..64) with DPP.  The full
 // sum lands in the last lane of each LPR-lane group.

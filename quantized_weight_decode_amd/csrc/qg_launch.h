@@ -29,6 +29,8 @@ inline int pick_lpr(int nchunks)
 
 // Raises a kernel's dynamic-LDS limit to `bytes` once (cached per kernel).
 hipError_t set_max_lds(const void *kernel, size_t bytes);
+// Compute units of the current device.
+int cu_count();
 
 // grouped int4
 bool i4g_stream_ok(const void *w, const float *x, int S, int I, int gs);
