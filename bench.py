@@ -5,8 +5,9 @@ A step is one pass of the hot path over one batch of synthetic input:
 
   i4g_O12288_I6144_gs64 (default), i4g_O12288_I6144_gs128:
       one qgemv_i4g call (grouped int4, one activation vector)
-  i4g_O12288_I6144_gs64_S2, _S4:
-      one qgemv_i4g call on 2 or 4 activation vectors (multi-token decode)
+  i4g_O12288_I6144_gs64_S2, _S4, fp8b128_O7168_I16384_S2, _S4,
+  mq4v2_O8192_I8192_S2, _S4:
+      the same step on 2 or 4 activation vectors per call (multi-token decode)
   fp8b128_O7168_I16384:
       one qgemv_fp8b128 call
   mq4v2_O8192_I8192:
@@ -113,17 +114,17 @@ class I4G(Case):
 class FP8(Case):
     kernel = "fp8_gemv_stream"
 
-    def __init__(self, O, I, torch, q, o):
+    def __init__(self, O, I, torch, q, o, S=1):
         import workloads as W
-        self.name = f"fp8b128_O{O}_I{I}"
-        self.fmt_desc = "fp8 e4m3, f32 scale per 128x128 block"
-        self.O, self.I = O, I
+        self.name = f"fp8b128_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = "fp8 e4m3, f32 scale per 128x128 block" + (f", {S} vectors per call" if S > 1 else "")
+        self.O, self.I, self.S = O, I, S
         nbo, nbi = W.fp8_nblocks(O, I)
         self.weight_bytes = O * I + nbo * nbi * 4
-        self.alg_bytes = self.weight_bytes + I * 4 + O * 4
+        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4)
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
-        d = W.gen_fp8b128(O, I, seed=0)
+        d = W.gen_fp8b128(O, I, S=S, seed=0)
         self.n = n_copies(self.weight_bytes)
         g = torch.Generator(device=dev)
         g.manual_seed(1)
@@ -146,7 +147,7 @@ class FP8(Case):
 
     def step(self, i):
         wp, spp = self.ptrs[i % self.n]
-        st = self.q.qgemv_fp8b128(wp, spp, self.x.data_ptr(), self.y.data_ptr(), 1, self.I,
+        st = self.q.qgemv_fp8b128(wp, spp, self.x.data_ptr(), self.y.data_ptr(), self.S, self.I,
                                   self.O, self.sp)
         if st:
             raise SystemExit(f"qgemv_fp8b128: {self.q.strerror(st)}")
@@ -155,18 +156,18 @@ class FP8(Case):
 class MQ4(Case):
     kernel = "mq4v2_gemv_stream"
 
-    def __init__(self, O, I, torch, q, o):
+    def __init__(self, O, I, torch, q, o, S=1):
         import workloads as W
-        self.name = f"mq4v2_O{O}_I{I}"
-        self.fmt_desc = "MQ4-v2 136 B / 256 weights, FWHT-256 rotated activations"
-        self.O, self.I = O, I
+        self.name = f"mq4v2_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = "MQ4-v2 136 B / 256 weights, FWHT-256 rotated activations" + (f", {S} vectors per call" if S > 1 else "")
+        self.O, self.I, self.S = O, I, S
         self.weight_bytes = O * (I // 256) * 136
         # step: FWHT (x, signs in; x_rot out) + GEMV (weights, x_rot in; y out)
-        self.gemv_bytes = self.weight_bytes + I * 4 + O * 4
-        self.alg_bytes = self.gemv_bytes + I * 4 + I + I * 4
+        self.gemv_bytes = self.weight_bytes + S * (I * 4 + O * 4)
+        self.alg_bytes = self.gemv_bytes + S * (I * 4 + I * 4) + I
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
-        d = W.gen_mq4v2(O, I, seed=0)
+        d = W.gen_mq4v2(O, I, S=S, seed=0)
         self.n = n_copies(self.weight_bytes)
         g = torch.Generator(device=dev)
         g.manual_seed(1)
@@ -185,7 +186,7 @@ class MQ4(Case):
         self.x = torch.from_numpy(d["x"]).to(dev)
         self.signs = torch.from_numpy(d["signs"]).to(dev)
         self.xr = torch.empty_like(self.x)
-        self.y = torch.empty((1, O), dtype=torch.float32, device=dev)
+        self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [w.data_ptr() for w in self.ws]
         self.step(0)
@@ -196,16 +197,16 @@ class MQ4(Case):
 
     def step(self, i):
         q = self.q
-        st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(), 1,
-                             self.I, self.sp)
-        st = st or q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), 1,
-                                 self.I, self.O, self.sp)
+        st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(),
+                             self.S, self.I, self.sp)
+        st = st or q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(),
+                                 self.S, self.I, self.O, self.sp)
         if st:
             raise SystemExit(f"mq4v2 step: {q.strerror(st)}")
 
     def gemv_only(self, i):
-        st = self.q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), 1,
-                                self.I, self.O, self.sp)
+        st = self.q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(),
+                                self.S, self.I, self.O, self.sp)
         if st:
             raise SystemExit(f"qgemv_mq4v2: {self.q.strerror(st)}")
 
@@ -275,13 +276,19 @@ def build_case(name, torch, q, o):
         "i4g_O256_I512_gs64": lambda: I4G(256, 512, 64, torch, q, o),
         "i4g_O12288_I6144_gs64_S2": lambda: I4G(12288, 6144, 64, torch, q, o, S=2),
         "i4g_O12288_I6144_gs64_S4": lambda: I4G(12288, 6144, 64, torch, q, o, S=4),
+        "fp8b128_O7168_I16384_S2": lambda: FP8(7168, 16384, torch, q, o, S=2),
+        "fp8b128_O7168_I16384_S4": lambda: FP8(7168, 16384, torch, q, o, S=4),
+        "mq4v2_O8192_I8192_S2": lambda: MQ4(8192, 8192, torch, q, o, S=2),
+        "mq4v2_O8192_I8192_S4": lambda: MQ4(8192, 8192, torch, q, o, S=4),
     }
     return table[name]()
 
 
 CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_I16384",
               "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64",
-              "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4"]
+              "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4",
+              "fp8b128_O7168_I16384_S2", "fp8b128_O7168_I16384_S4",
+              "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4"]
 
 
 KERNEL_SOURCES = {

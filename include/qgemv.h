@@ -56,9 +56,10 @@ const char *qgemv_version(void);
  *   scales  f32 [O][ceil(I/gs)]  weight (o,i) = (nibble - 8) * scales[o][i/gs]
  *   x       f32 [S][I],  y f32 [S][O]
  *   gs      even, >= 2; any I >= 1 (a last partial group is allowed)
- * Rows whose bytes are 16-byte aligned (I % 32 == 0, w 16-byte aligned) with
- * gs % 32 == 0 take the streaming kernel; every other valid shape takes a
- * slower general kernel with the same result definition.
+ * Rows whose bytes are 16-byte aligned (I % 32 == 0, w and x 16-byte
+ * aligned) with gs % 32 == 0 take the streaming kernel (S > 4 runs in groups
+ * of up to 4 vectors, each group streaming the weights once); every other
+ * valid shape takes a slower general kernel with the same result definition.
  */
 int qgemv_i4g(const void *w, const float *scales, const float *x, float *y,
               int S, int I, int O, int gs, void *stream);

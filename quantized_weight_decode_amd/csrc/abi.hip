@@ -40,6 +40,29 @@ int cu_count()
     return n;
 }
 
+int pick_rows_per_group(int O, int lpr, int wpb, size_t lds, const int *cand, int ncand)
+{
+    const long ncu = cu_count();
+    long per_cu = lds ? (long)(LDS_BUDGET / lds) : 32;
+    const long by_waves = 32 / wpb;   // waves a CU holds
+    per_cu = per_cu < by_waves ? per_cu : by_waves;
+    per_cu = per_cu < 1 ? 1 : per_cu;
+    int best = cand[ncand - 1];
+    long best_rows = -1;
+    for (int i = 0; i < ncand; i++) {
+        const long rows_wg = (long)wpb * (64 / lpr) * cand[i];
+        const long wgs = (O + rows_wg - 1) / rows_wg;
+        const long wg_per_cu = (wgs + ncu - 1) / ncu;
+        if (wg_per_cu > per_cu) continue;
+        const long rows = wg_per_cu * rows_wg;
+        if (best_rows < 0 || rows < best_rows) {
+            best_rows = rows;
+            best = cand[i];
+        }
+    }
+    return best;
+}
+
 }  // namespace qg
 
 namespace {

@@ -29,6 +29,10 @@
 #ifndef QG_FP8_WPB
 #define QG_FP8_WPB 7
 #endif
+// waves per workgroup for several vectors (S times the LDS per workgroup)
+#ifndef QG_FP8_WPB_MULTI
+#define QG_FP8_WPB_MULTI 16
+#endif
 // sweeps issued before the activations are staged (at most PF).  Unlike the
 // nibble formats, the fp8 stream is faster with its first round of weight
 // loads in flight while the (larger) activation vector is staged.
@@ -104,8 +108,8 @@ __device__ __forceinline__ float fp8_chunk_dot(const u32x4 wv, const f32x4 *__re
     return p0 + p1;
 }
 
-template <int S, int LPR, int R, int PF>
-__global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
+template <int S, int LPR, int R, int PF, int WPB>
+__global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ sc, const float *__restrict__ x,
     float *__restrict__ y, int I, int O, int nbi, int ntiles)
 {
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int tile = blockIdx.x * QG_FP8_WPB + wave;
+    const int tile = blockIdx.x * WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const int nit = (NU + LPR - 1) / LPR;
     const int nit_pad = (nit + PF - 1) / PF * PF;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(64 * QG_FP8_WPB) void fp8_gemv_stream(
         wr[r] = w + (size_t)min(row0 + r, O - 1) * I;
 
     // activations first; every load unconditional
-    XStageF8<8, 64 * QG_FP8_WPB> xst;
+    XStageF8<8, 64 * WPB> xst;
     const int total4 = S * NU * 4;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any
@@ -273,36 +277,64 @@ size_t fp8_lds_bytes(int S, int I)
     return ((size_t)S * 4 * seg_stride(I / 16) + 1) * sizeof(f32x4);
 }
 
-template <int S, int LPR, int R, int PF>
+template <int S, int LPR, int R, int PF, int WPB>
 hipError_t launch_t(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
-    const int wpb = QG_FP8_WPB;
-    const int blocks = (ntiles + wpb - 1) / wpb;
+    const int blocks = (ntiles + WPB - 1) / WPB;
     const size_t lds = fp8_lds_bytes(S, I);
-    auto kern = fp8_gemv_stream<S, LPR, R, PF>;
+    auto kern = fp8_gemv_stream<S, LPR, R, PF, WPB>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * wpb), lds, st, w, sc, x, y, I, O,
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, sc, x, y, I, O,
                        (I + 127) / 128, ntiles);
     return hipGetLastError();
+}
+
+template <int S, int R>
+hipError_t launch_r(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
+                    hipStream_t st)
+{
+    constexpr int WPB = S == 1 ? QG_FP8_WPB : QG_FP8_WPB_MULTI;
+    // several vectors: 16-wave workgroups leave 128 registers per lane, so
+    // two sweeps in flight
+    constexpr int PF = S == 1 ? QG_FP8_PF : 2;
+    switch (pick_lpr(I / 16)) {
+    case 64: return launch_t<S, 64, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 32: return launch_t<S, 32, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 16: return launch_t<S, 16, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 8: return launch_t<S, 8, R, PF, WPB>(w, sc, x, y, I, O, st);
+    default: return launch_t<S, 4, R, PF, WPB>(w, sc, x, y, I, O, st);
+    }
 }
 
 template <int S>
 hipError_t launch_s(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
 {
-    constexpr int R = S <= 2 ? QG_FP8_R : 2;
-    constexpr int PF = S <= 2 ? QG_FP8_PF : 2;
-    switch (pick_lpr(I / 16)) {
-    case 64: return launch_t<S, 64, R, PF>(w, sc, x, y, I, O, st);
-    case 32: return launch_t<S, 32, R, PF>(w, sc, x, y, I, O, st);
-    case 16: return launch_t<S, 16, R, PF>(w, sc, x, y, I, O, st);
-    case 8: return launch_t<S, 8, R, PF>(w, sc, x, y, I, O, st);
-    default: return launch_t<S, 4, R, PF>(w, sc, x, y, I, O, st);
+    if constexpr (S == 1) {
+        return launch_r<S, QG_FP8_R>(w, sc, x, y, I, O, st);
+    } else {
+        // several vectors: R keeps every workgroup resident at once (the rows
+        // of a lane group must share a 128-row band, so R divides 128)
+        static const int cand[] = {1, 2};
+        switch (pick_rows_per_group(O, pick_lpr(I / 16), QG_FP8_WPB_MULTI, fp8_lds_bytes(S, I),
+                                    cand, 2)) {
+        case 1: return launch_r<S, 1>(w, sc, x, y, I, O, st);
+        default: return launch_r<S, 2>(w, sc, x, y, I, O, st);
+        }
     }
+}
+
+// Vectors one streaming launch takes for this shape (0: not applicable).
+int fp8_stream_vectors(const void *w, const float *x, int S, int I)
+{
+    if (I % 16 != 0 || ((uintptr_t)w & 15) != 0 || ((uintptr_t)x & 15) != 0) return 0;
+    int n = S < FP8_FAST_MAX_S ? S : FP8_FAST_MAX_S;
+    while (n > 0 && fp8_lds_bytes(n, I) > LDS_BUDGET) --n;
+    return n;
 }
 
 }  // namespace
@@ -311,15 +343,24 @@ hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const floa
                                int S, int I, int O, hipStream_t st)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
-    const bool fast = S <= FP8_FAST_MAX_S && I % 16 == 0 && ((uintptr_t)w & 15) == 0 &&
-                      ((uintptr_t)x & 15) == 0 && fp8_lds_bytes(S, I) <= LDS_BUDGET;
-    if (fast) {
-        switch (S) {
-        case 1: return launch_s<1>(wb, scale_inv, x, y, I, O, st);
-        case 2: return launch_s<2>(wb, scale_inv, x, y, I, O, st);
-        case 3: return launch_s<3>(wb, scale_inv, x, y, I, O, st);
-        default: return launch_s<4>(wb, scale_inv, x, y, I, O, st);
+    // more vectors than one launch takes (S > 4, or their activations do not
+    // fit the LDS) run in groups, each streaming the weights once
+    const int nmax = fp8_stream_vectors(w, x, S, I);
+    if (nmax > 0) {
+        for (int s0 = 0; s0 < S; s0 += nmax) {
+            const int n = S - s0 < nmax ? S - s0 : nmax;
+            const float *xs = x + (size_t)s0 * I;
+            float *ys = y + (size_t)s0 * O;
+            hipError_t e;
+            switch (n) {
+            case 1: e = launch_s<1>(wb, scale_inv, xs, ys, I, O, st); break;
+            case 2: e = launch_s<2>(wb, scale_inv, xs, ys, I, O, st); break;
+            case 3: e = launch_s<3>(wb, scale_inv, xs, ys, I, O, st); break;
+            default: e = launch_s<4>(wb, scale_inv, xs, ys, I, O, st); break;
+            }
+            if (e != hipSuccess) return e;
         }
+        return hipSuccess;
     }
     const int wpb = 4;
     hipLaunchKernelGGL(fp8_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,

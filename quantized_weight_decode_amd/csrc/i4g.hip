@@ -39,8 +39,7 @@ namespace qg {
 #define QG_I4G_PF0 0
 #endif
 
-// Largest S the streaming kernels are instantiated for; S up to QGEMV_MAX_S
-// goes through the general kernel.
+// Largest S one streaming launch takes; larger S runs in groups.
 constexpr int I4G_FAST_MAX_S = 4;
 
 template <int S, int LPR, int R, int PF, int WPB>
@@ -287,10 +286,16 @@ template <int S, int LPR, int R>
 hipError_t launch_stream_pf(const uint8_t *w, const float *s, const float *x, float *y, int I,
                             int O, int gs, hipStream_t st)
 {
-    switch (pick_pf((I / 32 + LPR - 1) / LPR)) {
-    case 2: return launch_stream_t<S, LPR, R, 2>(w, s, x, y, I, O, gs, st);
-    case 3: return launch_stream_t<S, LPR, R, 3>(w, s, x, y, I, O, gs, st);
-    default: return launch_stream_t<S, LPR, R, 4>(w, s, x, y, I, O, gs, st);
+    // several vectors: 16-wave workgroups leave 128 registers per lane, so
+    // two sweeps in flight
+    if constexpr (S > 1) {
+        return launch_stream_t<S, LPR, R, 2>(w, s, x, y, I, O, gs, st);
+    } else {
+        switch (pick_pf((I / 32 + LPR - 1) / LPR)) {
+        case 2: return launch_stream_t<S, LPR, R, 2>(w, s, x, y, I, O, gs, st);
+        case 3: return launch_stream_t<S, LPR, R, 3>(w, s, x, y, I, O, gs, st);
+        default: return launch_stream_t<S, LPR, R, 4>(w, s, x, y, I, O, gs, st);
+        }
     }
 }
 
@@ -307,43 +312,24 @@ hipError_t launch_stream_r(const uint8_t *w, const float *s, const float *x, flo
     }
 }
 
-// Rows per lane group for several vectors.  The staged activations take S
-// times the LDS, so few workgroups fit a CU; R is picked so that all
-// workgroups are resident at once and the most loaded CU has the fewest rows
-// (e.g. 12288 rows, S = 2 or 4: R = 3, 256 workgroups of 48 rows).
-int pick_r_multi(int S, int I, int O)
-{
-    const int lpr = pick_lpr(I / 32);
-    const size_t lds = i4g_stream_lds_bytes(S, I);
-    int per_cu = (int)(LDS_BUDGET / lds);
-    per_cu = per_cu < 1 ? 1 : per_cu;
-    const int by_waves = 32 / QG_I4G_WPB_MULTI;
-    per_cu = per_cu < by_waves ? per_cu : by_waves;
-    const long ncu = cu_count();
-    int best = 4;
-    long best_rows = -1;
-    for (int r = 1; r <= 4; r++) {
-        const long rows_wg = (long)QG_I4G_WPB_MULTI * (WAVE / lpr) * r;
-        const long wgs = (O + rows_wg - 1) / rows_wg;
-        const long wg_per_cu = (wgs + ncu - 1) / ncu;
-        if (wg_per_cu > per_cu) continue;                 // more than one round
-        const long rows = wg_per_cu * rows_wg;
-        if (best_rows < 0 || rows < best_rows) { best_rows = rows; best = r; }
-    }
-    return best;
-}
-
 template <int S>
 hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, float *y,
                            int I, int O, int gs, hipStream_t st)
 {
     // R rows of a lane group share each activation read from LDS
-    if (S == 1) return launch_stream_r<S, QG_I4G_R>(w, s, x, y, I, O, gs, st);
-    switch (pick_r_multi(S, I, O)) {
-    case 1: return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
-    case 2: return launch_stream_r<S, 2>(w, s, x, y, I, O, gs, st);
-    case 3: return launch_stream_r<S, 3>(w, s, x, y, I, O, gs, st);
-    default: return launch_stream_r<S, 4>(w, s, x, y, I, O, gs, st);
+    if constexpr (S == 1) {
+        return launch_stream_r<S, QG_I4G_R>(w, s, x, y, I, O, gs, st);
+    } else {
+        // several vectors: the staged activations take S times the LDS, so
+        // few workgroups fit a CU; R keeps them all resident (12288 rows,
+        // S = 2 or 4: R = 3, 256 workgroups of 48 rows)
+        static const int cand[] = {1, 2, 3};
+        switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_I4G_WPB_MULTI,
+                                    i4g_stream_lds_bytes(S, I), cand, 3)) {
+        case 1: return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
+        case 2: return launch_stream_r<S, 2>(w, s, x, y, I, O, gs, st);
+        default: return launch_stream_r<S, 3>(w, s, x, y, I, O, gs, st);
+        }
     }
 }
 
@@ -354,25 +340,37 @@ size_t i4g_stream_lds_bytes(int S, int I)
     return (size_t)S * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float));
 }
 
-bool i4g_stream_ok(const void *w, const float *x, int S, int I, int gs)
+int i4g_stream_vectors(const void *w, const float *x, int S, int I, int gs)
 {
-    if (S > I4G_FAST_MAX_S || I % 32 != 0 || gs % 32 != 0 || ((uintptr_t)w & 15) != 0 ||
-        ((uintptr_t)x & 15) != 0)
-        return false;
-    return i4g_stream_lds_bytes(S, I) <= LDS_BUDGET;
+    if (I % 32 != 0 || gs % 32 != 0 || ((uintptr_t)w & 15) != 0 || ((uintptr_t)x & 15) != 0)
+        return 0;
+    int n = S < I4G_FAST_MAX_S ? S : I4G_FAST_MAX_S;
+    while (n > 0 && i4g_stream_lds_bytes(n, I) > LDS_BUDGET) --n;
+    return n;
 }
 
 hipError_t launch_i4g_gemv(const void *w, const float *scales, const float *x, float *y,
                            int S, int I, int O, int gs, hipStream_t st)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
-    if (i4g_stream_ok(w, x, S, I, gs)) {
-        switch (S) {
-        case 1: return launch_stream_s<1>(wb, scales, x, y, I, O, gs, st);
-        case 2: return launch_stream_s<2>(wb, scales, x, y, I, O, gs, st);
-        case 3: return launch_stream_s<3>(wb, scales, x, y, I, O, gs, st);
-        default: return launch_stream_s<4>(wb, scales, x, y, I, O, gs, st);
+    // vectors per streaming launch; more vectors than one launch takes are
+    // done in groups (each group streams the weights once)
+    const int nmax = i4g_stream_vectors(w, x, S, I, gs);
+    if (nmax > 0) {
+        for (int s0 = 0; s0 < S; s0 += nmax) {
+            const int n = S - s0 < nmax ? S - s0 : nmax;
+            const float *xs = x + (size_t)s0 * I;
+            float *ys = y + (size_t)s0 * O;
+            hipError_t e;
+            switch (n) {
+            case 1: e = launch_stream_s<1>(wb, scales, xs, ys, I, O, gs, st); break;
+            case 2: e = launch_stream_s<2>(wb, scales, xs, ys, I, O, gs, st); break;
+            case 3: e = launch_stream_s<3>(wb, scales, xs, ys, I, O, gs, st); break;
+            default: e = launch_stream_s<4>(wb, scales, xs, ys, I, O, gs, st); break;
+            }
+            if (e != hipSuccess) return e;
         }
+        return hipSuccess;
     }
     const int wpb = 4;
     hipLaunchKernelGGL(i4g_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,

@@ -26,6 +26,10 @@
 #ifndef QG_MQ4_WPB
 #define QG_MQ4_WPB 4
 #endif
+// waves per workgroup for several vectors (S times the LDS per workgroup)
+#ifndef QG_MQ4_WPB_MULTI
+#define QG_MQ4_WPB_MULTI 16
+#endif
 // sweeps issued before the activations are staged (at most PF)
 #ifndef QG_MQ4_PF0
 #define QG_MQ4_PF0 0
@@ -45,8 +49,8 @@ __device__ __forceinline__ u32x4 load16_a8(const uint8_t *p)
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
-template <int S, int LPR, int R, int PF>
-__global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
+template <int S, int LPR, int R, int PF, int WPB>
+__global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int I,
     int O, int ntiles)
 {
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int sl = lane % LPR;
-    const int tile = blockIdx.x * QG_MQ4_WPB + wave;
+    const int tile = blockIdx.x * WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const size_t rowbytes = (size_t)(I / 256) * MQ4_GROUP_BYTES;
     const int nit = (NU + LPR - 1) / LPR;
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(64 * QG_MQ4_WPB) void mq4v2_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
 
-    XStageN<S, 8, 64 * QG_MQ4_WPB> xst;
+    XStageN<S, 8, 64 * WPB> xst;
     const int total4 = S * NU * 8;
     xst.load(x, total4);
     // every wave of the workgroup has issued its activation loads before any
@@ -281,32 +285,59 @@ size_t mq4_lds_bytes(int S, int I)
     return (size_t)S * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float));
 }
 
-template <int S, int LPR, int R, int PF>
+template <int S, int LPR, int R, int PF, int WPB>
 hipError_t launch_t(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
-    const int wpb = QG_MQ4_WPB;
-    const int blocks = (ntiles + wpb - 1) / wpb;
+    const int blocks = (ntiles + WPB - 1) / WPB;
     const size_t lds = mq4_lds_bytes(S, I);
-    auto kern = mq4v2_gemv_stream<S, LPR, R, PF>;
+    auto kern = mq4v2_gemv_stream<S, LPR, R, PF, WPB>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * wpb), lds, st, w, x, y, I, O, ntiles);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, x, y, I, O, ntiles);
     return hipGetLastError();
+}
+
+template <int S, int R>
+hipError_t launch_r(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
+{
+    constexpr int WPB = S == 1 ? QG_MQ4_WPB : QG_MQ4_WPB_MULTI;
+    // several vectors: 16-wave workgroups leave 128 registers per lane, so
+    // two sweeps in flight
+    constexpr int PF = S == 1 ? QG_MQ4_PF : 2;
+    switch (pick_lpr(I / 32)) {
+    case 64: return launch_t<S, 64, R, PF, WPB>(w, x, y, I, O, st);
+    case 32: return launch_t<S, 32, R, PF, WPB>(w, x, y, I, O, st);
+    case 16: return launch_t<S, 16, R, PF, WPB>(w, x, y, I, O, st);
+    default: return launch_t<S, 8, R, PF, WPB>(w, x, y, I, O, st);
+    }
 }
 
 template <int S>
 hipError_t launch_s(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
 {
-    constexpr int R = S <= 2 ? QG_MQ4_R : 2;
-    constexpr int PF = QG_MQ4_PF;
-    switch (pick_lpr(I / 32)) {
-    case 64: return launch_t<S, 64, R, PF>(w, x, y, I, O, st);
-    case 32: return launch_t<S, 32, R, PF>(w, x, y, I, O, st);
-    case 16: return launch_t<S, 16, R, PF>(w, x, y, I, O, st);
-    default: return launch_t<S, 8, R, PF>(w, x, y, I, O, st);
+    if constexpr (S == 1) {
+        return launch_r<S, QG_MQ4_R>(w, x, y, I, O, st);
+    } else {
+        // several vectors: R keeps every workgroup resident at once
+        static const int cand[] = {1, 2, 3};
+        switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_MQ4_WPB_MULTI, mq4_lds_bytes(S, I),
+                                    cand, 3)) {
+        case 1: return launch_r<S, 1>(w, x, y, I, O, st);
+        case 2: return launch_r<S, 2>(w, x, y, I, O, st);
+        default: return launch_r<S, 3>(w, x, y, I, O, st);
+        }
     }
+}
+
+// Vectors one streaming launch takes for this shape (0: not applicable).
+int mq4_stream_vectors(const void *w, const float *x, int S, int I)
+{
+    if (((uintptr_t)w & 7) != 0 || ((uintptr_t)x & 15) != 0) return 0;
+    int n = S < MQ4_FAST_MAX_S ? S : MQ4_FAST_MAX_S;
+    while (n > 0 && mq4_lds_bytes(n, I) > LDS_BUDGET) --n;
+    return n;
 }
 
 }  // namespace
@@ -315,15 +346,24 @@ hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int
                              hipStream_t st)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
-    const bool fast = S <= MQ4_FAST_MAX_S && ((uintptr_t)w & 7) == 0 &&
-                      ((uintptr_t)x & 15) == 0 && mq4_lds_bytes(S, I) <= LDS_BUDGET;
-    if (fast) {
-        switch (S) {
-        case 1: return launch_s<1>(wb, x, y, I, O, st);
-        case 2: return launch_s<2>(wb, x, y, I, O, st);
-        case 3: return launch_s<3>(wb, x, y, I, O, st);
-        default: return launch_s<4>(wb, x, y, I, O, st);
+    // more vectors than one launch takes run in groups, each streaming the
+    // weights once
+    const int nmax = mq4_stream_vectors(w, x, S, I);
+    if (nmax > 0) {
+        for (int s0 = 0; s0 < S; s0 += nmax) {
+            const int n = S - s0 < nmax ? S - s0 : nmax;
+            const float *xs = x + (size_t)s0 * I;
+            float *ys = y + (size_t)s0 * O;
+            hipError_t e;
+            switch (n) {
+            case 1: e = launch_s<1>(wb, xs, ys, I, O, st); break;
+            case 2: e = launch_s<2>(wb, xs, ys, I, O, st); break;
+            case 3: e = launch_s<3>(wb, xs, ys, I, O, st); break;
+            default: e = launch_s<4>(wb, xs, ys, I, O, st); break;
+            }
+            if (e != hipSuccess) return e;
         }
+        return hipSuccess;
     }
     const int wpb = 4;
     hipLaunchKernelGGL(mq4v2_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,

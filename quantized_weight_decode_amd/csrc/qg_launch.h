@@ -32,8 +32,17 @@ hipError_t set_max_lds(const void *kernel, size_t bytes);
 // Compute units of the current device.
 int cu_count();
 
+// Rows per lane group, out of the ncand candidates, for a streaming kernel
+// whose workgroups hold wpb waves of 64 / lpr lane groups and lds bytes of
+// LDS: the choice keeps every workgroup resident at once (one round) and
+// gives the most loaded CU the fewest rows.  Falls back to the largest
+// candidate when none fits one round.
+int pick_rows_per_group(int O, int lpr, int wpb, size_t lds, const int *cand, int ncand);
+
 // grouped int4
-bool i4g_stream_ok(const void *w, const float *x, int S, int I, int gs);
+// Vectors one streaming launch takes for this shape (0: the streaming
+// kernel does not apply; larger S runs in groups of this many).
+int i4g_stream_vectors(const void *w, const float *x, int S, int I, int gs);
 size_t i4g_stream_lds_bytes(int S, int I);
 hipError_t launch_i4g_gemv(const void *w, const float *scales, const float *x, float *y,
                            int S, int I, int O, int gs, hipStream_t st);
