@@ -7,26 +7,33 @@
 // before the sum across groups.
 //
 // Streaming kernel (rows of 16-byte lane chunks, gs % 32 == 0):
-//   * each workgroup stages x (permuted, with per-chunk sums) in LDS once;
+//   * each workgroup stages x once in LDS, per 32-column chunk as a
+//     shared-exponent fixed point split into signed 4-bit digits;
 //   * a wave covers 64/LPR row groups of R rows; LPR lanes sweep a row in
 //     16-byte dwordx4 loads (fully coalesced), the R rows of a lane group share
-//     the activations they read from LDS, and the next chunk's loads are in
-//     flight while the current one is decoded;
-//   * per lane chunk c (32 columns, one group): P = sum q*x, then
-//     acc += s_g * (P - 8 * sum x), which is sum (q - 8) s_g x reassociated;
-//   * the row sum is a DPP reduction over the LPR lanes.
+//     the activation digits they read from LDS, and the next chunks' loads are
+//     in flight while the current one is multiplied;
+//   * per lane chunk c (32 columns, one group): the integer sum of (q - 8) v
+//     comes from 24 hardware 8-way 4-bit dot products, and
+//     acc += s_g * 2^(E_c - 21) * sum (q - 8) v;
+//   * the row sum is a DPP reduction over the LPR lanes;
+//   * a workgroup that meets an infinity or NaN in x computes its rows with
+//     per-element f32 products instead, so they propagate as in the plain
+//     definition.
 #include "qg_device.h"
 #include "qg_launch.h"
 
 namespace qg {
 
-// Tile shape of the streaming kernel for S <= 2: rows per lane group and
-// waves per workgroup.
+// Tile shape of the streaming kernel for one vector: rows per lane group and
+// waves per workgroup.  Measured on the 12288 x 6144 workload: 2 rows x 12
+// waves (512 workgroups, two per CU) beat 4 x 4, 3 x 8, 2 x 8, 4 x 12 and
+// 3 x 16 by 0.1-0.5 us.
 #ifndef QG_I4G_R
-#define QG_I4G_R 4
+#define QG_I4G_R 2
 #endif
 #ifndef QG_I4G_WPB
-#define QG_I4G_WPB 4
+#define QG_I4G_WPB 12
 #endif
 // Waves per workgroup for several vectors: the staged activations take S
 // times the LDS, so fewer workgroups fit a CU and each must hold more waves.
@@ -34,13 +41,60 @@ namespace qg {
 #define QG_I4G_WPB_MULTI 16
 #endif
 
-// chunk-sweeps issued before the activations are staged (at most PF)
-#ifndef QG_I4G_PF0
-#define QG_I4G_PF0 0
+// activation items (8 columns each) each thread loads up front
+#ifndef QG_I4G_NPRE
+#define QG_I4G_NPRE 2
 #endif
 
 // Largest S one streaming launch takes; larger S runs in groups.
 constexpr int I4G_FAST_MAX_S = 4;
+
+// Rows row0 .. row0 + R - 1 (those below O) of one lane group, with each
+// weight decoded to f32 as (q - 8) * s and multiplied by x read from global
+// memory: the plain definition's arithmetic, for activations that hold an
+// infinity or NaN.
+template <int S, int LPR, int R>
+__device__ __noinline__ void i4g_rows_plain(const uint8_t *__restrict__ w,
+                                            const float *__restrict__ scales,
+                                            const float *__restrict__ x, float *__restrict__ y,
+                                            int I, int O, int ng, Div20 div_cpg, int row0, int sl)
+{
+    const int NU = I / 32;
+#pragma unroll 1
+    for (int r = 0; r < R; r++) {
+        const int row = min(row0 + r, O - 1);
+        const uint8_t *wr = w + (size_t)row * (I / 2);
+        const float *sr = scales + (size_t)row * ng;
+        float acc[S];
+#pragma unroll
+        for (int t = 0; t < S; t++) acc[t] = 0.0f;
+        for (int u = sl; u < NU; u += LPR) {
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(wr + (size_t)u * 16);
+            const float sg = sr[div_cpg((uint32_t)u)];
+#pragma unroll
+            for (int dd = 0; dd < 4; dd++) {
+                float e[4], o[4];
+                nib8(wv[dd], e, o);
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const float we = (e[k] * NIB_XSCALE - 8.0f) * sg;
+                    const float wo = (o[k] * NIB_XSCALE - 8.0f) * sg;
+                    const int col = 32 * u + 8 * dd + 2 * k;
+#pragma unroll
+                    for (int t = 0; t < S; t++) {
+                        acc[t] = __builtin_fmaf(we, x[(size_t)t * I + col], acc[t]);
+                        acc[t] = __builtin_fmaf(wo, x[(size_t)t * I + col + 1], acc[t]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < S; t++) {
+            const float v = sub_reduce<LPR>(acc[t]);
+            if (sl == LPR - 1 && row0 + r < O) y[(size_t)t * O + row0 + r] = v;
+        }
+    }
+}
 
 template <int S, int LPR, int R, int PF, int WPB>
 __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
@@ -49,11 +103,11 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     Div20 div_cpg, int ntiles)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
-    constexpr int PF0 = QG_I4G_PF0 < PF ? QG_I4G_PF0 : PF;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;                       // lane chunks per row
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NS]
-    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * seg_stride(NU));  // [S][NU]
+    u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                        // [S][6][NU]
+    float *xc = reinterpret_cast<float *>(xq + (size_t)S * 6 * NU);        // [S][NU]
+    int *wflag = reinterpret_cast<int *>(xc + (size_t)S * NU);             // [WPB]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -78,20 +132,19 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     // so the compiler can wait for exactly the load a value comes from
     // instead of draining all outstanding loads.
     // 1. activations first (L2-resident)
-    XStageN<S, 6, 64 * WPB> xst;
-    const int total4 = S * NU * 8;
-    xst.load(x, total4);
+    XStageQ<S, QG_I4G_NPRE, 64 * WPB> xst;
+    const int items = S * NU * 4;
+    xst.load(x, items);
     // every wave of the workgroup has issued its activation loads before any
     // wave issues weight loads (raw barrier: no drain)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the first PF0 chunk-sweeps of weights and scales.  Only a few: the
-    //    memory system serves a flood of streaming weight requests ahead of
-    //    the isolated activation reads, so the stream is held back until the
-    //    activations have arrived, with just enough weight traffic in flight
-    //    to keep HBM busy meanwhile.
+    // 2. weight and scale loads of one chunk-sweep into ring slot j.  The
+    //    first round goes out only once the activations are staged: issued
+    //    earlier (before the activation loads return, or between their return
+    //    and the conversion) it measured slower.
     u32x4 wb[PF][R];
     float sb[PF][R];
     auto fetch = [&](int c, int j) {
@@ -103,17 +156,22 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
             sb[j][r] = ld_stream(&sr[r][g]);
         }
     };
-#pragma unroll
-    for (int j = 0; j < PF0; j++) fetch(j, j);
-
-    // 3. activations into LDS (permuted, chunk sums), then the rest of the
-    //    first round of weights
-    __builtin_amdgcn_sched_barrier(0);
-    xst.store(x, total4, NU, xl, xs);
+    // 3. activations into LDS as fixed-point digits
+    const uint32_t bad = xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, nullptr);
+    const bool wbad = __ballot(bad != 0) != 0;
+    if (lane == 0) wflag[wave] = wbad;
     __syncthreads();
-    if (tile >= ntiles) return;
+    int anybad = 0;
 #pragma unroll
-    for (int j = PF0; j < PF; j++) fetch(j, j);
+    for (int k = 0; k < WPB; k++) anybad |= wflag[k];
+    anybad = __builtin_amdgcn_readfirstlane(anybad);
+    if (tile >= ntiles) return;
+    if (anybad) {
+        i4g_rows_plain<S, LPR, R>(w, scales, x, y, I, O, ng, div_cpg, row0, sl);
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < PF; j++) fetch(j, j);
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
@@ -121,42 +179,42 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     for (int t = 0; t < S; t++)
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+    // one vector: running digit sums per row (see q8_dot_run)
+    uint32_t P[R][6], V[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        V[r] = 0;
+#pragma unroll
+        for (int k = 0; k < 6; k++) P[r][k] = 0;
+    }
 
     // 4. sweep in rounds of PF chunk-sweeps: consume ring slot j, then refill
     //    it with the sweep one round ahead.  All refills are unconditional
     //    (clamped) and pinned in place, so every wait is for exactly the slot
     //    about to be used; the last round issues no refills.  Padding sweeps
-    //    past the row end add zero.
+    //    past the row end are multiplied by a zero chunk scale.
     auto consume = [&](int c, int j) {
         const int u = c * LPR + sl;
         const bool valid = u < NU;
         const int uu = valid ? u : 0;
-        if constexpr (S == 1) {
-            const float m8xs = -8.0f * xs[uu];
+        uint32_t wx[R][4];
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) wx[r][d] = wb[j][r][d] ^ Q8_NIB_FLIP;
+#pragma unroll
+        for (int t = 0; t < S; t++) {
+            const u32x4 *xt = xq + (size_t)t * 6 * NU;
+            u32x4 L[6];
+#pragma unroll
+            for (int k = 0; k < 6; k++) L[k] = xt[k * NU + uu];
+            const float cs = valid ? xc[(size_t)t * NU + uu] : 0.0f;
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                // s * (sum q x - 8 sum x); the chunk dot comes out as 2^-9 sum q x
-                const float p = nib_chunk_dot(wb[j][r], xl, NU, uu);
-                const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
-                acc[0][r] = __builtin_fmaf(valid ? sb[j][r] : 0.0f, tv, acc[0][r]);
+                const int dv = S == 1 ? q8_dot_run(wx[r], L, P[r], V[r]) : q8_dot(wx[r], L);
+                acc[t][r] = __builtin_fmaf(sb[j][r] * cs, (float)dv, acc[t][r]);
             }
-        } else {
-            // Several vectors: the select form below makes the compiler run
-            // each (vector, row) dot under its own lane mask, one after the
-            // other.  Written as a multiply by a zeroed scale, every vector's
-            // activations and every row's decode get scheduled up front,
-            // which takes the whole register file (one wave per SIMD).
-#pragma unroll
-            for (int t = 0; t < S; t++) {
-                const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
-                const float m8xs = -8.0f * xs[(size_t)t * NU + uu];
-#pragma unroll
-                for (int r = 0; r < R; r++) {
-                    const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
-                    const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
-                    acc[t][r] = valid ? __builtin_fmaf(sb[j][r], tv, acc[t][r]) : acc[t][r];
-                }
-            }
+            if constexpr (S > 1) pin_values(acc[t]);   // one vector's digits live at a time
         }
     };
     const int nrounds = nit_pad / PF;
@@ -165,6 +223,8 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
         for (int j = 0; j < PF; j++) {
             const int c = rd * PF + j;
             consume(c, j);
+#pragma unroll
+            for (int t = 0; t < S; t++) pin_values(acc[t]);
             fetch(c + PF, j);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -172,7 +232,9 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
 #pragma unroll
     for (int j = 0; j < PF; j++) {
         consume((nrounds - 1) * PF + j, j);
-        __builtin_amdgcn_sched_barrier(0);   // one slot at a time, as in the loop
+#pragma unroll
+        for (int t = 0; t < S; t++) pin_values(acc[t]);   // one slot at a time, as in the loop
+        __builtin_amdgcn_sched_barrier(0);
     }
 
 #pragma unroll
@@ -337,7 +399,7 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
 
 size_t i4g_stream_lds_bytes(int S, int I)
 {
-    return (size_t)S * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float));
+    return q8_stage_bytes(S, I / 32, false) + 16 * sizeof(int);
 }
 
 int i4g_stream_vectors(const void *w, const float *x, int S, int I, int gs)

@@ -9,9 +9,12 @@
 // One launch, no host round trip, no atomics:
 //   * workgroup (t, b) owns token t and RT consecutive output rows; the
 //     T * NB workgroups (NB row blocks per token) cover about one CU each;
-//   * it stages x[t] in LDS as for the dense grouped-int4 GEMV (one vector:
+//   * it stages x[t] in LDS as the dense grouped-int4 GEMV does (per-chunk
+//     fixed-point digits for the 4-bit integer dot product; one vector:
 //     staging every token in every workgroup makes thousands of workgroups
-//     fetch the same lines at once, which costs more than it saves);
+//     fetch the same lines at once, which costs more than it saves); a token
+//     whose activations hold an infinity or NaN is multiplied per element in
+//     f32 instead, so they propagate as in the plain definition;
 //   * one wave reads the token's K ids and hands them over in LDS; every wave
 //     derives with ballots the distinct valid experts (first-occurrence
 //     order) -- the routing never leaves the device;
@@ -39,10 +42,6 @@
 #ifndef QG_MOE_PF
 #define QG_MOE_PF 2
 #endif
-// sweeps issued before the activations are staged (at most PF)
-#ifndef QG_MOE_PF0
-#define QG_MOE_PF0 0
-#endif
 
 namespace qg {
 
@@ -66,14 +65,14 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     Div20 div_cpg, int RT, int NB, int *__restrict__ err_flag)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
-    constexpr int PF0 = QG_MOE_PF0 < PF ? QG_MOE_PF0 : PF;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                      // [8][NS]
-    float *xs = reinterpret_cast<float *>(xl + 8 * seg_stride(NU));       // [NU]
-    float *part = xs + NU;                                                // [K][RT]
+    u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                      // [6][NU]
+    float *xc = reinterpret_cast<float *>(xq + 6 * NU);                   // [NU]
+    float *part = xc + NU;                                                // [K][RT]
     int *ids_l = reinterpret_cast<int *>(part + (size_t)K * RT);          // [64]
     int *ctr = ids_l + 64;                                                // next unit
+    int *wflag = ctr + 1;                                                 // [WPB]
 
     const int t = blockIdx.x / NB;
     const int o0 = (blockIdx.x - t * NB) * RT;
@@ -90,15 +89,16 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     // queue on one L2 channel) and its activations, before any weight load
     int id = 0;
     if (wave == 0) id = ids[t * K + min(lane, K - 1)];
-    XStageN<1, 2, 64 * QG_MOE_WPB> xst;
-    const int total4 = NU * 8;
-    xst.load(x + (size_t)t * I, total4);
+    const float *xt = x + (size_t)t * I;
+    XStageQ<1, 1, 64 * QG_MOE_WPB> xst;
+    const int items = NU * 4;
+    xst.load(xt, items);
     __builtin_amdgcn_sched_barrier(0);
     if (wave == 0) ids_l[lane] = id;
     if (threadIdx.x == 0) *ctr = nwaves;
     // raw barrier (the activation loads stay in flight); the LDS write must
     // have landed before it
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(QG_WAIT_LGKM0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -178,20 +178,29 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         }
     };
 
-    // only PF0 sweeps go out before the activations are staged: a flood of
+    // the weight stream starts once the activations are staged: a flood of
     // streaming weight requests is served ahead of the activation reads
-#pragma unroll
-    for (int j = 0; j < PF0; j++) fetch(j);
-    __builtin_amdgcn_sched_barrier(0);
-    xst.store(x + (size_t)t * I, total4, NU, xl, xs);
+    const uint32_t xbad = xst.store(xt, items, NU, reinterpret_cast<uint32_t *>(xq), xc, nullptr);
+    const bool wbad = __ballot(xbad != 0) != 0;
+    if (lane == 0) wflag[wave] = wbad;
     __syncthreads();
+    int xnan = 0;
 #pragma unroll
-    for (int j = PF0; j < PF; j++) fetch(j);
+    for (int k = 0; k < QG_MOE_WPB; k++) xnan |= wflag[k];
+    xnan = __builtin_amdgcn_readfirstlane(xnan);
+#pragma unroll
+    for (int j = 0; j < PF; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[R];
+    uint32_t P[R][6], V[R];   // running digit sums per row (see q8_dot_run)
 #pragma unroll
-    for (int r = 0; r < R; r++) acc[r] = 0.0f;
+    for (int r = 0; r < R; r++) {
+        acc[r] = 0.0f;
+        V[r] = 0;
+#pragma unroll
+        for (int k = 0; k < 6; k++) P[r][k] = 0;
+    }
 
     auto consume = [&](int j) {
         const int ci = slot_u[j];
@@ -199,13 +208,24 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         const int u = slot_c[j] * LPR + sl;
         const bool in_row = u < NU;
         const int uu = in_row ? u : 0;
-        const float m8xs = -8.0f * xs[uu];
+        if (xnan) {
+            if (in_row)
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            // s * (sum q x - 8 sum x); the chunk dot comes out as 2^-9 sum q x
-            const float p = nib_chunk_dot(wb[j][r], xl, NU, uu);
-            const float tv = __builtin_fmaf(p, NIB_XSCALE, m8xs);
-            acc[r] = __builtin_fmaf(in_row ? sb[j][r] : 0.0f, tv, acc[r]);
+                for (int r = 0; r < R; r++)
+                    acc[r] += nib_chunk_plain(wb[j][r], sb[j][r], xt + (size_t)uu * 32);
+        } else {
+            u32x4 L[6];
+#pragma unroll
+            for (int k = 0; k < 6; k++) L[k] = xq[k * NU + uu];
+            const float cs = in_row ? xc[uu] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                uint32_t wx[4];
+#pragma unroll
+                for (int d = 0; d < 4; d++) wx[d] = wb[j][r][d] ^ Q8_NIB_FLIP;
+                const int dv = q8_dot_run(wx, L, P[r], V[r]);
+                acc[r] = __builtin_fmaf(sb[j][r] * cs, (float)dv, acc[r]);
+            }
         }
         if (slot_c[j] + 1 < nit) return;
         // unit done: row sums -> partials of every slot that chose its expert
@@ -227,6 +247,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
         for (int j = 0; j < PF; j++) {
             consume(j);
+            pin_values(acc);
             fetch(j);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -300,8 +321,8 @@ namespace {
 
 size_t moe_lds_bytes(int K, int I, int RT)
 {
-    return (size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float) +
-           (size_t)K * RT * sizeof(float) + 65 * sizeof(int);
+    return q8_stage_bytes(1, I / 32, false) + (size_t)K * RT * sizeof(float) +
+           (65 + QG_MOE_WPB) * sizeof(int);
 }
 
 // Row blocks: about one workgroup per CU over all T tokens, RT rows each (a

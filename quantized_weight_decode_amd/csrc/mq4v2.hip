@@ -11,9 +11,13 @@
 // follows from the chunk's own byte offset.  The chunk is fetched with one
 // 16-byte load at an 8-byte-aligned address (136 g + 8 + 16 p); the lane's
 // header dword (+0 or +4) is a separate 4-byte load that hits the same lines.
-// With x staged exactly as for grouped int4 (permuted, per-chunk sums),
-// acc += scale * sum(q x) + zero * sum(x): weight = q*scale + zero
-// reassociated.
+// x is staged as for grouped int4 (per-chunk fixed-point digits, chunk scale
+// c = 2^(E-21)) plus the chunk sums xsum = c * sum v.  A payload dword XOR
+// 0x88888888 read as signed nibbles is q - 8, so the integer dot gives
+// P = sum (q - 8) v and
+//     sum w x~ = scale * c * P + (8 * scale + zero) * xsum,
+// weight = q * scale + zero reassociated.  Activations holding an infinity or
+// NaN are multiplied per element in f32 instead (fma(q, scale, zero) * x).
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -30,9 +34,9 @@
 #ifndef QG_MQ4_WPB_MULTI
 #define QG_MQ4_WPB_MULTI 16
 #endif
-// sweeps issued before the activations are staged (at most PF)
-#ifndef QG_MQ4_PF0
-#define QG_MQ4_PF0 0
+// activation items (8 columns each) each thread loads up front
+#ifndef QG_MQ4_NPRE
+#define QG_MQ4_NPRE 2
 #endif
 
 namespace qg {
@@ -49,17 +53,71 @@ __device__ __forceinline__ u32x4 load16_a8(const uint8_t *p)
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
+// f32 sum over one chunk (x32 = x + 32u) of fma(q, scale, zero) * x: the
+// plain definition's arithmetic, for activations holding an infinity or NaN.
+__device__ __forceinline__ float mq4_chunk_plain(const u32x4 wv, float scl, float zro,
+                                                 const float *__restrict__ x32)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        float e[4], o[4];
+        nib8(wv[d], e, o);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            acc = __builtin_fmaf(__builtin_fmaf(e[k] * NIB_XSCALE, scl, zro), x32[8 * d + 2 * k], acc);
+            acc = __builtin_fmaf(__builtin_fmaf(o[k] * NIB_XSCALE, scl, zro), x32[8 * d + 2 * k + 1],
+                                 acc);
+        }
+    }
+    return acc;
+}
+
+// Rows row0 .. row0 + R - 1 (those below O) of one lane group with the plain
+// per-element arithmetic (x read from global memory).
+template <int S, int LPR, int R>
+__device__ __noinline__ void mq4_rows_plain(const uint8_t *__restrict__ w,
+                                            const float *__restrict__ x, float *__restrict__ y,
+                                            int I, int O, int row0, int sl)
+{
+    const int NU = I / 32;
+    const size_t rowbytes = (size_t)(I / 256) * MQ4_GROUP_BYTES;
+#pragma unroll 1
+    for (int r = 0; r < R; r++) {
+        const uint8_t *wr = w + (size_t)min(row0 + r, O - 1) * rowbytes;
+        float acc[S];
+#pragma unroll
+        for (int t = 0; t < S; t++) acc[t] = 0.0f;
+        for (int u = sl; u < NU; u += LPR) {
+            const int g = u >> 3, p = u & 7;
+            const uint8_t *gp = wr + (size_t)g * MQ4_GROUP_BYTES;
+            const u32x4 wv = load16_a8(gp + 8 + 16 * p);
+            const uint32_t hd = *reinterpret_cast<const uint32_t *>(gp + (p >= 4 ? 4 : 0));
+            const float scl = f16_to_f32(hd & 0xFFFFu), zro = f16_to_f32(hd >> 16);
+#pragma unroll
+            for (int t = 0; t < S; t++)
+                acc[t] += mq4_chunk_plain(wv, scl, zro, x + (size_t)t * I + (size_t)u * 32);
+        }
+#pragma unroll
+        for (int t = 0; t < S; t++) {
+            const float v = sub_reduce<LPR>(acc[t]);
+            if (sl == LPR - 1 && row0 + r < O) y[(size_t)t * O + row0 + r] = v;
+        }
+    }
+}
+
 template <int S, int LPR, int R, int PF, int WPB>
 __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int I,
     int O, int ntiles)
 {
-    constexpr int PF0 = QG_MQ4_PF0 < PF ? QG_MQ4_PF0 : PF;
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
-    f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);                  // [S][8][NS]
-    float *xs = reinterpret_cast<float *>(xl + (size_t)S * 8 * seg_stride(NU));  // [S][NU]
+    u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                        // [S][6][NU]
+    float *xc = reinterpret_cast<float *>(xq + (size_t)S * 6 * NU);        // [S][NU]
+    float *xsm = xc + (size_t)S * NU;                                      // [S][NU]
+    int *wflag = reinterpret_cast<int *>(xsm + (size_t)S * NU);            // [WPB]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -76,14 +134,9 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
 
-    XStageN<S, 8, 64 * WPB> xst;
-    const int total4 = S * NU * 8;
-    xst.load(x, total4);
-    // every wave of the workgroup has issued its activation loads before any
-    // wave issues weight loads (raw barrier: no drain)
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    XStageQ<S, QG_MQ4_NPRE, 64 * WPB, true> xst;
+    const int items = S * NU * 4;
+    xst.load(x, items);
 
     // payload chunk u: group u/8, bytes 8 + 16 (u%8); header dword +0 / +4
     auto fetch = [&](int u, u32x4 *wv, uint32_t *hv) {
@@ -98,17 +151,23 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
 
     u32x4 wb[PF][R];
     uint32_t hb[PF][R];
-    // only PF0 sweeps go out before the activations are staged: a flood of
+    // the weight stream starts once the activations are staged: a flood of
     // streaming weight requests is served ahead of the activation reads
-#pragma unroll
-    for (int j = 0; j < PF0; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
-
-    __builtin_amdgcn_sched_barrier(0);
-    xst.store(x, total4, NU, xl, xs);
+    const uint32_t bad = xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, xsm);
+    const bool wbad = __ballot(bad != 0) != 0;
+    if (lane == 0) wflag[wave] = wbad;
     __syncthreads();
-    if (tile >= ntiles) return;
+    int xnan = 0;
 #pragma unroll
-    for (int j = PF0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
+    for (int k = 0; k < WPB; k++) xnan |= wflag[k];
+    xnan = __builtin_amdgcn_readfirstlane(xnan);
+    if (tile >= ntiles) return;
+    if (xnan) {
+        mq4_rows_plain<S, LPR, R>(w, x, y, I, O, row0, sl);
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
@@ -116,6 +175,13 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     for (int t = 0; t < S; t++)
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
+    uint32_t P[R][6], V[R];   // one vector: running digit sums per row (see q8_dot_run)
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        V[r] = 0;
+#pragma unroll
+        for (int k = 0; k < 6; k++) P[r][k] = 0;
+    }
 
     auto consume = [&](int c, int j) {
         const int u = c * LPR + sl;
@@ -127,17 +193,26 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
             scl[r] = f16_to_f32(hb[j][r] & 0xFFFFu);
             zro[r] = f16_to_f32(hb[j][r] >> 16);
         }
+        uint32_t wx[R][4];
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) wx[r][d] = wb[j][r][d] ^ Q8_NIB_FLIP;
 #pragma unroll
         for (int t = 0; t < S; t++) {
-            const f32x4 *xt = xl + (size_t)t * 8 * seg_stride(NU);
-            const float xsum = xs[(size_t)t * NU + uu];
+            const u32x4 *xt = xq + (size_t)t * 6 * NU;
+            u32x4 L[6];
+#pragma unroll
+            for (int k = 0; k < 6; k++) L[k] = xt[k * NU + uu];
+            const float cs = valid ? xc[(size_t)t * NU + uu] : 0.0f;
+            const float xsum = valid ? xsm[(size_t)t * NU + uu] : 0.0f;
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                // scale * sum q x + zero * sum x; the chunk dot is 2^-9 sum q x
-                const float p = nib_chunk_dot(wb[j][r], xt, NU, uu);
-                const float v = __builtin_fmaf(scl[r] * NIB_XSCALE, p, zro[r] * xsum);
-                acc[t][r] = valid ? acc[t][r] + v : acc[t][r];
+                const int dv = S == 1 ? q8_dot_run(wx[r], L, P[r], V[r]) : q8_dot(wx[r], L);
+                const float off = __builtin_fmaf(8.0f, scl[r], zro[r]) * xsum;
+                acc[t][r] = __builtin_fmaf(scl[r] * cs, (float)dv, acc[t][r] + off);
             }
+            if constexpr (S > 1) pin_values(acc[t]);   // one vector's digits live at a time
         }
     };
     const int nrounds = nit_pad / PF;
@@ -146,6 +221,8 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
         for (int j = 0; j < PF; j++) {
             const int c = rd * PF + j;
             consume(c, j);
+#pragma unroll
+            for (int t = 0; t < S; t++) pin_values(acc[t]);
             fetch(min((c + PF) * LPR + sl, NU - 1), wb[j], hb[j]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -153,7 +230,9 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
 #pragma unroll
     for (int j = 0; j < PF; j++) {
         consume((nrounds - 1) * PF + j, j);
-        __builtin_amdgcn_sched_barrier(0);   // one slot at a time, as in the loop
+#pragma unroll
+        for (int t = 0; t < S; t++) pin_values(acc[t]);   // one slot at a time, as in the loop
+        __builtin_amdgcn_sched_barrier(0);
     }
 
 #pragma unroll
@@ -282,7 +361,7 @@ namespace {
 
 size_t mq4_lds_bytes(int S, int I)
 {
-    return (size_t)S * ((size_t)8 * seg_stride(I / 32) * sizeof(f32x4) + (I / 32) * sizeof(float));
+    return q8_stage_bytes(S, I / 32, true) + 16 * sizeof(int);
 }
 
 template <int S, int LPR, int R, int PF, int WPB>

@@ -15,6 +15,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
+// s_waitcnt operands (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a field at its maximum does not wait)
+#define QG_WAIT_VM0 0x0F70      /* all vector memory loads returned */
+#define QG_WAIT_LGKM0 0xC07F    /* all LDS / scalar memory operations done */
+
 // Weight streams are read with the non-temporal hint: each byte is used once
 // per call, and keeping it out of the caches leaves the activations (read by
 // every workgroup) resident in L2 across calls.
@@ -232,6 +237,249 @@ __device__ __forceinline__ float nib_chunk_dot(const u32x4 wv, const f32x4 *__re
     return p0 + p1;
 }
 
+
+// ---------------------------------------------------------------------------
+// Integer-dot form of the 4-bit chunk product.
+//
+// The activations of each 32-column lane chunk are staged in a shared-exponent
+// fixed point.  With E the smallest integer such that max|x| < 2^E over the
+// chunk (E clamped to at least -100), v = RNE(x * 2^(21 - E)), so |v| <= 2^21
+// and x~ = v * 2^(E - 21) is within 2^-21 max|x| of x.  v is written in six
+// balanced base-16 digits, v = sum_j d_j 16^j with d_j in [-8, 7], and digit j
+// of the eight columns under packed weight dword d forms one dword (column
+// 8d + k in nibble k): the operand layout of the 8-way signed 4-bit dot
+// product (v_dot8_i32_i4).  A packed weight dword XOR 0x88888888, read as eight
+// signed nibbles, is exactly q - 8 per column, so
+//     sum over the chunk of (q - 8) v = sum_j 16^j dot8(w ^ 0x88888888, D_j),
+// exact in 32-bit integers (|sum| <= 32 * 8 * 2^21 = 2^29).  The fixed-point
+// values come from one FMA: x * 2^(21-E) + 1.5 * 2^23 lies in [2^23, 2^24),
+// where the float spacing is 1, so the FMA's single rounding is the RNE of
+// x * 2^(21-E) and the low bits of the result are 0x400000 + v.
+//
+// LDS layout of one vector (NU chunks): u32x4 xq[6][NU], component d of
+// xq[j][u] = digit j of columns 32u + 8d + 0..7 (biased to the two's-complement
+// nibble pattern); float xc[NU] = 2^(E_u - 21); optionally float xsum[NU] =
+// 2^(E_u - 21) * sum v over the chunk (for offsets such as MQ4's zero).
+// ---------------------------------------------------------------------------
+// Orders code: every value in v is computed before this point, and no memory
+// operation moves across it.  Used between the consume and refill of a ring
+// slot so that the refill can reuse the slot's registers (otherwise the
+// compiler may sink a slot's arithmetic below the following loads and keep
+// every slot's data live at once).
+template <int N>
+__device__ __forceinline__ void pin_values(const float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("" ::"v"(v[i]) : "memory");
+}
+
+constexpr float Q8_MAGIC = 12582912.0f;        // 1.5 * 2^23
+constexpr uint32_t Q8_UNBIAS = 0x4AB77778u;    // 0x4B400000 - 0x888888
+constexpr uint32_t Q8_DIGIT_BIAS = 0x888888u;  // 8 * (16^0 + ... + 16^5)
+constexpr uint32_t Q8_NIB_FLIP = 0x88888888u;
+
+// max over the four lanes 4c..4c+3
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t m)
+{
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+    return m;
+}
+__device__ __forceinline__ int quad_sum_i32(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    return v;
+}
+
+// Converts the eight activations of one weight dword (columns 32u + 8d + 0..7,
+// in a and b) and stores their digit dwords.  The four lanes 4c..4c+3 hold the
+// four dwords d = 0..3 of one chunk and must all call this together (the
+// chunk exponent is a max over them).  Lanes with ok == false store nothing.
+// Returns nonzero if the chunk holds an infinity or NaN (its staged values
+// are then meaningless).
+template <bool SUM>
+__device__ __forceinline__ uint32_t q8_put(f32x4 a, f32x4 b, bool ok, uint32_t t, uint32_t u,
+                                           uint32_t d, uint32_t NU, uint32_t *__restrict__ xq,
+                                           float *__restrict__ xc, float *__restrict__ xsum)
+{
+    const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    // |x| as ordered integers: every NaN sorts above infinity, above every finite
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) m = max(m, __builtin_bit_cast(uint32_t, xv[k]) & 0x7FFFFFFFu);
+    m = quad_max_u32(m);
+    const uint32_t eb = m >> 23;                 // biased exponent of max|x|: E = eb - 126
+    const uint32_t e = max(eb, 26u);             // E >= -100
+    const float sin = __builtin_bit_cast(float, (274u - e) << 23);   // 2^(21 - E)
+    uint32_t n[8];                                // v + 0x888888, in [0x688888, 0xA88888]
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        n[k] = __builtin_bit_cast(uint32_t, __builtin_fmaf(xv[k], sin, Q8_MAGIC)) - Q8_UNBIAS;
+    // byte b of the even columns (0, 2, 4, 6) and of the odd columns (1, 3, 5, 7)
+    const uint32_t te = __builtin_amdgcn_perm(n[2], n[0], 0x05010400u);
+    const uint32_t ue = __builtin_amdgcn_perm(n[6], n[4], 0x05010400u);
+    const uint32_t te2 = __builtin_amdgcn_perm(n[2], n[0], 0x06020602u);
+    const uint32_t ue2 = __builtin_amdgcn_perm(n[6], n[4], 0x06020602u);
+    const uint32_t to = __builtin_amdgcn_perm(n[3], n[1], 0x05010400u);
+    const uint32_t uo = __builtin_amdgcn_perm(n[7], n[5], 0x05010400u);
+    const uint32_t to2 = __builtin_amdgcn_perm(n[3], n[1], 0x06020602u);
+    const uint32_t uo2 = __builtin_amdgcn_perm(n[7], n[5], 0x06020602u);
+    const uint32_t be[3] = {__builtin_amdgcn_perm(ue, te, 0x05040100u),
+                            __builtin_amdgcn_perm(ue, te, 0x07060302u),
+                            __builtin_amdgcn_perm(ue2, te2, 0x05040100u)};
+    const uint32_t bo[3] = {__builtin_amdgcn_perm(uo, to, 0x05040100u),
+                            __builtin_amdgcn_perm(uo, to, 0x07060302u),
+                            __builtin_amdgcn_perm(uo2, to2, 0x05040100u)};
+    // digit 2b is the low nibble of byte b, digit 2b+1 the high nibble; the
+    // even column goes to the low nibble of each output byte
+    uint32_t L[6];
+#pragma unroll
+    for (int b = 0; b < 3; b++) {
+        L[2 * b] = ((bo[b] << 4) & 0xF0F0F0F0u) | (be[b] & 0x0F0F0F0Fu);
+        L[2 * b + 1] = (bo[b] & 0xF0F0F0F0u) | ((be[b] >> 4) & 0x0F0F0F0Fu);
+    }
+    int vs = 0;
+    if constexpr (SUM) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) vs += (int)(n[k] - Q8_DIGIT_BIAS);
+        vs = quad_sum_i32(vs);
+    }
+    const float cs = __builtin_bit_cast(float, (e - 20u) << 23);     // 2^(E - 21)
+    if (ok) {
+        uint32_t *q = xq + (t * 6u * NU + u) * 4u + d;
+#pragma unroll
+        for (int j = 0; j < 6; j++) q[j * NU * 4u] = L[j] ^ Q8_NIB_FLIP;
+        if (d == 0) {
+            xc[t * NU + u] = cs;
+            if constexpr (SUM) xsum[t * NU + u] = cs * (float)vs;
+        }
+    }
+    return eb == 255u;
+}
+
+// Stages S activation vectors of I columns (I % 32 == 0) in the fixed-point
+// layout above.  Thread f of the workgroup takes item f: the eight columns
+// 8f .. 8f + 7 (two float4 loads), so a chunk is four consecutive lanes.  As
+// with XStageN, each workgroup starts at its own chunk-aligned offset and
+// wraps around.  load() issues the thread's first NPRE items (those that
+// exist) and store() converts them, then any further items one at a time.
+// Items past the end belong to whole four-lane groups (items is a multiple
+// of four, NT of 64), which skip both.  NT is the workgroup size.  store()
+// returns nonzero in a lane that met an infinity or NaN.
+template <int S, int NPRE, int NT, bool SUM = false>
+struct XStageQ {
+    f32x4 a[NPRE], b[NPRE];
+    int rot;
+
+    __device__ __forceinline__ void load(const float *__restrict__ x, int items)
+    {
+        const unsigned chunks = (unsigned)items / 4u;
+        rot = chunks ? (int)(((blockIdx.x * 2654435761u) >> 7) % chunks) * 4 : 0;
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const int f = (int)threadIdx.x + j * NT;
+            if (f < items) {
+                const uint32_t g = (uint32_t)stage_index(f, items, rot);
+                a[j] = ldx4(x, 2u * g);
+                b[j] = ldx4(x, 2u * g + 1u);
+            }
+        }
+    }
+
+    __device__ __forceinline__ uint32_t store(const float *__restrict__ x, int items, int NU,
+                                              uint32_t *__restrict__ xq, float *__restrict__ xc,
+                                              float *__restrict__ xsum)
+    {
+        const int ipv = NU * 4;   // items per vector
+        uint32_t bad = 0;
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const int f = (int)threadIdx.x + j * NT;
+            if (f < items) {
+                int t, rem;
+                split_f<S>(stage_index(f, items, rot), ipv, t, rem);
+                bad |= q8_put<SUM>(a[j], b[j], true, (uint32_t)t, (uint32_t)rem >> 2,
+                                   (uint32_t)rem & 3u, (uint32_t)NU, xq, xc, xsum);
+            }
+        }
+        for (int f = (int)threadIdx.x + NPRE * NT; f < items; f += NT) {
+            const int g = stage_index(f, items, rot);
+            int t, rem;
+            split_f<S>(g, ipv, t, rem);
+            bad |= q8_put<SUM>(ldx4(x, 2u * (uint32_t)g), ldx4(x, 2u * (uint32_t)g + 1u), true,
+                               (uint32_t)t, (uint32_t)rem >> 2, (uint32_t)rem & 3u,
+                               (uint32_t)NU, xq, xc, xsum);
+        }
+        return bad;
+    }
+};
+
+// f32 sum over one lane chunk (columns 32u .. 32u + 31, x32 = x + 32u) of
+// ((q - 8) * s) * x with each weight decoded as the plain definition does it
+// (one rounding) and multiplied by the f32 activation: the fallback for
+// activations holding an infinity or NaN, which then propagate as in the
+// plain definition.
+__device__ __forceinline__ float nib_chunk_plain(const u32x4 wv, float s,
+                                                 const float *__restrict__ x32)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        float e[4], o[4];
+        nib8(wv[d], e, o);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            acc = __builtin_fmaf((e[k] * NIB_XSCALE - 8.0f) * s, x32[8 * d + 2 * k], acc);
+            acc = __builtin_fmaf((o[k] * NIB_XSCALE - 8.0f) * s, x32[8 * d + 2 * k + 1], acc);
+        }
+    }
+    return acc;
+}
+
+// LDS bytes of the fixed-point staging of S vectors of NU chunks
+__host__ __device__ constexpr size_t q8_stage_bytes(int S, int NU, bool sum)
+{
+    return (size_t)S * NU * (6 * 16 + 4 + (sum ? 4 : 0));
+}
+
+// sum (q - 8) v over one lane chunk of packed weights wx (already XOR-ed with
+// 0x88888888) against the chunk's digit dwords L.  P and V carry running
+// per-digit sums across calls for the same row (the dot8 accumulates into
+// them, so no accumulator is cleared); the chunk's value is the change of
+// the combined sum, exact modulo 2^32.
+__device__ __forceinline__ int q8_dot_run(const uint32_t wx[4], const u32x4 L[6], uint32_t P[6],
+                                          uint32_t &V)
+{
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+        for (int j = 0; j < 6; j++)
+            P[j] = (uint32_t)__builtin_amdgcn_sdot8((int)wx[d], (int)L[j][d], (int)P[j], false);
+    uint32_t v = P[5];
+#pragma unroll
+    for (int j = 4; j >= 0; j--) v = (v << 4) + P[j];
+    const int dv = (int)(v - V);
+    V = v;
+    return dv;
+}
+
+// Same product with fresh accumulators (no carried state).
+__device__ __forceinline__ int q8_dot(const uint32_t wx[4], const u32x4 L[6])
+{
+    int P[6];
+#pragma unroll
+    for (int j = 0; j < 6; j++) P[j] = __builtin_amdgcn_sdot8((int)wx[0], (int)L[j][0], 0, false);
+#pragma unroll
+    for (int d = 1; d < 4; d++)
+#pragma unroll
+        for (int j = 0; j < 6; j++)
+            P[j] = __builtin_amdgcn_sdot8((int)wx[d], (int)L[j][d], P[j], false);
+    uint32_t v = (uint32_t)P[5];
+#pragma unroll
+    for (int j = 4; j >= 0; j--) v = (v << 4) + (uint32_t)P[j];
+    return (int)v;
+}
 
 // ---------------------------------------------------------------------------
 // Sub-wave sum over LPR consecutive lanes (LPR in 4..64) with DPP.  The full

@@ -38,7 +38,10 @@ def assert_y_close(got, ref, tol=REL_L2_TOL):
     ref = np.asarray(ref)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.array_equal(np.isnan(got), np.isnan(ref)), "NaN pattern differs"
-    ok = ~np.isnan(ref)
+    gi, ri = np.isinf(got), np.isinf(ref)
+    assert np.array_equal(gi, ri), "infinity pattern differs"
+    assert np.array_equal(got[gi], ref[ri]), "infinity signs differ"
+    ok = ~np.isnan(ref) & ~ri
     r = rel_l2(got[ok], ref[ok])
     assert r <= tol, f"rel L2 {r:.3e} > {tol:.0e}"
     return r

@@ -72,6 +72,41 @@ def test_nan_activation_poisons_all_rows(q):
     assert np.isnan(y).all()
 
 
+@pytest.mark.parametrize("O,I,S", [(300, 512, 1), (12288, 6144, 1), (200, 6144, 2)])
+def test_infinite_activations_propagate(q, qref, O, I, S):
+    # an infinity makes its rows +-inf, or NaN where a zero weight meets it or
+    # two infinities of opposite sign meet, exactly as in the plain definition
+    d = W.gen_i4g(O, I, 64, S=S, seed=O + S)
+    d["x"][0, 37] = np.inf
+    d["x"][S - 1, I - 3] = -np.inf
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
+    ref = qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, 64)
+    assert np.isinf(ref).any() and np.isnan(ref).any()
+    assert_y_close(y, ref)
+
+
+@pytest.mark.parametrize("O,I,S", [(512, 6144, 1), (256, 2048, 2)])
+def test_wide_dynamic_range_activations(q, qref, O, I, S):
+    # magnitudes spread over twelve decades, zeros, subnormals and one chunk
+    # holding a value 1e4 times its neighbours
+    d = W.gen_i4g(O, I, 64, S=S, seed=3 * O + S)
+    rng = np.random.default_rng(99)
+    x = d["x"] * (10.0 ** rng.uniform(-6, 6, size=d["x"].shape)).astype(np.float32)
+    x[:, 64:96] = 0.0
+    x[:, 96:100] = np.float32(1e-40)
+    x[:, 130] = 1e4 * np.abs(x[:, 131]).max() + 1.0
+    d["x"] = x.astype(np.float32)
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, 64))
+
+
+def test_zero_activations_give_zero(q):
+    d = W.gen_i4g(128, 2048, 64, seed=8)
+    d["x"][:] = 0.0
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
+    assert np.all(y == 0.0)
+
+
 def test_misaligned_weights_take_general_path(q, qref):
     import torch
     O, I, gs = 20, 512, 64

@@ -138,6 +138,31 @@ def test_error_flag_is_per_call(q, qref):
     assert_y_close(y, oracle_y(qref, good))
 
 
+def test_infinite_activation_in_one_token(q, qref):
+    # the token with an infinity gets the plain definition's +-inf / NaN rows;
+    # the other tokens are unaffected
+    d = W.gen_moe(12, 256, 2048, 64, 3, 4, seed=28)
+    d["x"][1, 100] = np.inf
+    y, err = run(q, d)
+    assert err == 0
+    ref = oracle_y(qref, d)
+    assert np.isinf(ref[1]).any()
+    assert_y_close(y, ref)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_wide_dynamic_range_activations(q, qref, T):
+    d = W.gen_moe(16, 256, 7168, 64, T, 4, seed=29 + T)
+    rng = np.random.default_rng(97)
+    x = d["x"] * (10.0 ** rng.uniform(-6, 6, size=d["x"].shape)).astype(np.float32)
+    x[:, 64:96] = 0.0
+    x[:, 130] = 1e4 * np.abs(x[:, 131]).max() + 1.0
+    d["x"] = x.astype(np.float32)
+    y, err = run(q, d)
+    assert err == 0
+    assert_y_close(y, oracle_y(qref, d))
+
+
 def test_repeated_calls_are_bitwise_identical(q):
     # units are handed out dynamically; the result must not depend on which
     # wave computed which unit

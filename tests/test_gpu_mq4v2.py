@@ -50,6 +50,41 @@ def test_gemv_matches_oracle(q, qref, O, I, S):
     assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I))
 
 
+@pytest.mark.parametrize("O,I,S", [(256, 512, 1), (8192, 8192, 1), (300, 2048, 2)])
+def test_infinite_activations_propagate(q, qref, O, I, S):
+    # infinities give +-inf rows (NaN where two of opposite sign meet), as in
+    # the plain definition
+    d = W.gen_mq4v2(O, I, S=S, seed=O + S)
+    d["x"][0, 37] = np.inf
+    d["x"][S - 1, I - 3] = -np.inf
+    y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), dev(d["x"])))
+    ref = qref.mq4v2_gemv(d["w"], d["x"], O, I)
+    assert np.isinf(ref).any()
+    assert_y_close(y, ref)
+
+
+def test_nan_activation_poisons_all_rows(q):
+    d = W.gen_mq4v2(40, 512, seed=4)
+    d["x"][0, 300] = np.nan
+    y = host(q.mq4v2(dev(d["w"].reshape(40, -1)), dev(d["x"])))
+    assert np.isnan(y).all()
+
+
+@pytest.mark.parametrize("O,I,S", [(512, 8192, 1), (256, 2048, 2)])
+def test_wide_dynamic_range_activations(q, qref, O, I, S):
+    # magnitudes over twelve decades, a zero chunk, subnormals and a value
+    # 1e4 times its chunk neighbours
+    d = W.gen_mq4v2(O, I, S=S, seed=5 * O + S)
+    rng = np.random.default_rng(98)
+    x = d["x"] * (10.0 ** rng.uniform(-6, 6, size=d["x"].shape)).astype(np.float32)
+    x[:, 64:96] = 0.0
+    x[:, 96:100] = np.float32(1e-40)
+    x[:, 130] = 1e4 * np.abs(x[:, 131]).max() + 1.0
+    d["x"] = x.astype(np.float32)
+    y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), dev(d["x"])))
+    assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I))
+
+
 def test_unaligned_rows_take_general_path(q, qref):
     import torch
     O, I = 12, 512
