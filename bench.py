@@ -11,7 +11,9 @@ A step is one pass of the hot path over one batch of synthetic input:
   fp8b128_O7168_I16384:
       one qgemv_fp8b128 call
   mq4v2_O8192_I8192:
-      qgemv_fwht256 (rotate x) then qgemv_mq4v2
+      one qgemv_mq4v2_rot call (the FWHT-256 rotation of x fused into the
+      GEMV; the same result as qgemv_fwht256 followed by qgemv_mq4v2); the
+      _S2 / _S4 steps call qgemv_fwht256 then qgemv_mq4v2
   moe_E256_O2048_I7168_gs64_T4_K8:
       one qgemv_moe_topk call (4 tokens, top-8 of 256 experts)
 
@@ -22,7 +24,8 @@ the routed-expert step cycles through 16 seeded routings over one resident
 
 Prints one JSON line.  `value` is the algorithmic bytes of K steps divided by
 the time between two HIP events bracketing them on the launch stream;
-`roofline.achieved` is the same for the dominant (GEMV) kernel timed alone.
+`roofline.achieved` is the same for the step's kernel launches (one launch
+per vector group, except the rotation launch of the multi-vector MQ4 steps).
 `--copy-calibrate` instead runs a plain device-to-device copy of known size
 (used to scale the HBM traffic counters).
 """
@@ -57,9 +60,6 @@ class Case:
 
     def step(self, i):
         raise NotImplementedError
-
-    def gemv_only(self, i):
-        self.step(i)
 
 
 def _check(rel, what):
@@ -162,9 +162,14 @@ class MQ4(Case):
         self.fmt_desc = "MQ4-v2 136 B / 256 weights, FWHT-256 rotated activations" + (f", {S} vectors per call" if S > 1 else "")
         self.O, self.I, self.S = O, I, S
         self.weight_bytes = O * (I // 256) * 136
-        # step: FWHT (x, signs in; x_rot out) + GEMV (weights, x_rot in; y out)
-        self.gemv_bytes = self.weight_bytes + S * (I * 4 + O * 4)
-        self.alg_bytes = self.gemv_bytes + S * (I * 4 + I * 4) + I
+        # one vector: one fused launch (weights, x, signs in; y out), the
+        # rotated activations never leave the chip.  Several vectors: the
+        # rotation kernel (x, signs in; x_rot out) then the GEMV (weights,
+        # x_rot in; y out) -- every workgroup of the fused kernel would
+        # rotate all S vectors, which costs more than the extra launch
+        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4) + I
+        if S > 1:
+            self.alg_bytes += S * I * 8
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
         d = W.gen_mq4v2(O, I, S=S, seed=0)
@@ -197,18 +202,17 @@ class MQ4(Case):
 
     def step(self, i):
         q = self.q
-        st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(),
-                             self.S, self.I, self.sp)
-        st = st or q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(),
-                                 self.S, self.I, self.O, self.sp)
+        if self.S == 1:
+            st = q.qgemv_mq4v2_rot(self.ptrs[i % self.n], self.x.data_ptr(),
+                                   self.signs.data_ptr(), self.y.data_ptr(), 1, self.I, self.O,
+                                   self.sp)
+        else:
+            st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(),
+                                 self.S, self.I, self.sp)
+            st = st or q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(),
+                                     self.y.data_ptr(), self.S, self.I, self.O, self.sp)
         if st:
             raise SystemExit(f"mq4v2 step: {q.strerror(st)}")
-
-    def gemv_only(self, i):
-        st = self.q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(),
-                                self.S, self.I, self.O, self.sp)
-        if st:
-            raise SystemExit(f"qgemv_mq4v2: {self.q.strerror(st)}")
 
 
 class MoE(Case):
@@ -416,12 +420,8 @@ def main():
         step_bytes = case.alg_bytes
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel alone (identical to the step for single-kernel steps)
-    if isinstance(case, MQ4):
-        kms = timed(torch, case.gemv_only, 0, args.steps) / args.steps
-        kbytes = case.gemv_bytes
-    else:
-        kms, kbytes = ms_step, step_bytes
+    # the dominant kernel is the step's one launch
+    kms, kbytes = ms_step, step_bytes
     kgbs = kbytes / (kms * 1e-3) / 1e9
     wgbs = case.weight_bytes / (kms * 1e-3) / 1e9
 

@@ -92,6 +92,22 @@ int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I,
                 int O, void *stream);
 
 /*
+ * MQ4-v2 GEMV on unrotated activations: the FWHT-256 pre-rotation below
+ * (hipfire "MQ4 V2", section 1) fused into the GEMV (sections 2 and 4),
+ *     y = W . x_rot,  x_rot = (1/16) H256 (signs (.) x) per 256-column block,
+ * with x_rot bit-identical to qgemv_fwht256's output and y as qgemv_mq4v2
+ * computes it from that x_rot, in one launch.
+ *   w      as qgemv_mq4v2, 8-byte aligned;  x f32 [S][I], 16-byte aligned;
+ *   signs  int8 [I] (each +1 or -1), 8-byte aligned;  y f32 [S][O];
+ *   I % 256 == 0.
+ * Refusals: QGEMV_E_ALIGN for other alignments, QGEMV_E_DIMS when one
+ * vector's staged activations exceed the LDS (I above 40000); rotate with
+ * qgemv_fwht256 and call qgemv_mq4v2 for those.
+ */
+int qgemv_mq4v2_rot(const void *w, const float *x, const int8_t *signs, float *y, int S,
+                    int I, int O, void *stream);
+
+/*
  * FWHT-256 pre-rotation of activations for MQ4 weights (hipfire "MQ4 V2",
  * section 1: the weights are FWHT-256 rotated with per-element signs).
  * Per 256-element block b of each vector:

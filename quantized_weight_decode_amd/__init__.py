@@ -32,6 +32,8 @@ _SIGS = {
                                 C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_mq4v2_rot": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_fwht256": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_int, C.c_int, C.c_void_p]),
     "qgemv_moe_topk_workspace": (C.c_size_t, [C.c_int, C.c_int, C.c_int]),
@@ -109,6 +111,10 @@ def qgemv_fp8b128(w, scale_inv, x, y, S, I, O, stream):
 
 def qgemv_mq4v2(w, x_rot, y, S, I, O, stream):
     return lib().qgemv_mq4v2(w, x_rot, y, S, I, O, stream)
+
+
+def qgemv_mq4v2_rot(w, x, signs, y, S, I, O, stream):
+    return lib().qgemv_mq4v2_rot(w, x, signs, y, S, I, O, stream)
 
 
 def qgemv_fwht256(x, signs, x_rot, S, I, stream):
@@ -195,6 +201,17 @@ def mq4v2(w, x_rot, out=None):
     y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x_rot.device)
     _call("qgemv_mq4v2", _dev(w, "w", torch.uint8), _dev(x_rot, "x_rot", torch.float32),
           _dev(y, "y", torch.float32), S, I, O, _stream())
+    return y
+
+
+def mq4v2_rot(w, x, signs, out=None):
+    """MQ4-v2 GEMV on unrotated x: the FWHT-256 pre-rotation fused in."""
+    torch = _torch()
+    O, I = w.shape[0], x.shape[-1]
+    S = _vecs(x, I)
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _call("qgemv_mq4v2_rot", _dev(w, "w", torch.uint8), _dev(x, "x", torch.float32),
+          _dev(signs, "signs", torch.int8), _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
 
 

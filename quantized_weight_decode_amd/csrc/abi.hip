@@ -149,6 +149,17 @@ int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I, int O
     return launched(qg::launch_mq4v2_gemv(w, x_rot, y, S, I, O, (hipStream_t)stream));
 }
 
+int qgemv_mq4v2_rot(const void *w, const float *x, const int8_t *signs, float *y, int S, int I,
+                    int O, void *stream)
+{
+    if (!w || !x || !signs || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(y)) return QGEMV_E_ALIGN;
+    if (int e = qg::mq4v2_rot_check(w, x, signs, I)) return e;
+    return launched(qg::launch_mq4v2_rot_gemv(w, x, signs, y, S, I, O, (hipStream_t)stream));
+}
+
 int qgemv_dequant_mq4v2(const void *w, float *W, int I, int O, void *stream)
 {
     if (!w || !W) return QGEMV_E_NULL;

@@ -37,7 +37,11 @@
 #define QG_MOE_R 2
 #endif
 #ifndef QG_MOE_WPB
-#define QG_MOE_WPB 16
+#define QG_MOE_WPB 8
+#endif
+// workgroups per launch the row blocking aims at (over all tokens)
+#ifndef QG_MOE_WGS
+#define QG_MOE_WGS 256
 #endif
 #ifndef QG_MOE_PF
 #define QG_MOE_PF 2
@@ -329,7 +333,7 @@ size_t moe_lds_bytes(int K, int I, int RT)
 // multiple of the wave tile rpw).
 void moe_blocks(int T, int O, int rpw, int &RT, int &NB)
 {
-    const int want = (256 + T - 1) / T;
+    const int want = (QG_MOE_WGS + T - 1) / T;
     const int per = (O + want - 1) / want;
     RT = (per + rpw - 1) / rpw * rpw;
     NB = (O + RT - 1) / RT;

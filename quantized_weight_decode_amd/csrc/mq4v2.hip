@@ -28,7 +28,7 @@
 #define QG_MQ4_PF 4
 #endif
 #ifndef QG_MQ4_WPB
-#define QG_MQ4_WPB 4
+#define QG_MQ4_WPB 16
 #endif
 // waves per workgroup for several vectors (S times the LDS per workgroup)
 #ifndef QG_MQ4_WPB_MULTI
@@ -106,10 +106,13 @@ __device__ __noinline__ void mq4_rows_plain(const uint8_t *__restrict__ w,
     }
 }
 
-template <int S, int LPR, int R, int PF, int WPB>
+// ROT: x is unrotated and the workgroup applies the FWHT-256 pre-rotation
+// (signs, then H256 / 16 per block) while staging it; the rotated values are
+// bit-identical to the stand-alone rotation kernel's.
+template <int S, int LPR, int R, int PF, int WPB, bool ROT>
 __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
-    const uint8_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int I,
-    int O, int ntiles)
+    const uint8_t *__restrict__ w, const float *__restrict__ x, const int8_t *__restrict__ signs,
+    float *__restrict__ y, int I, int O, int ntiles)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -117,7 +120,9 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                        // [S][6][NU]
     float *xc = reinterpret_cast<float *>(xq + (size_t)S * 6 * NU);        // [S][NU]
     float *xsm = xc + (size_t)S * NU;                                      // [S][NU]
-    int *wflag = reinterpret_cast<int *>(xsm + (size_t)S * NU);            // [WPB]
+    int *wflag = reinterpret_cast<int *>(xsm + (size_t)S * NU);            // [16]
+    // ROT fallback: x_rot as f32 [S][I], over the staging area once it is unused
+    float *xf = reinterpret_cast<float *>(lds_raw);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,9 +139,9 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
 
-    XStageQ<S, QG_MQ4_NPRE, 64 * WPB, true> xst;
+    XStageQ<S, QG_MQ4_NPRE, 64 * WPB, true, ROT> xst;
     const int items = S * NU * 4;
-    xst.load(x, items);
+    xst.load(x, items, signs, NU * 4);
 
     // payload chunk u: group u/8, bytes 8 + 16 (u%8); header dword +0 / +4
     auto fetch = [&](int u, u32x4 *wv, uint32_t *hv) {
@@ -153,7 +158,8 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     uint32_t hb[PF][R];
     // the weight stream starts once the activations are staged: a flood of
     // streaming weight requests is served ahead of the activation reads
-    const uint32_t bad = xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, xsm);
+    const uint32_t bad =
+        xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, xsm, signs);
     const bool wbad = __ballot(bad != 0) != 0;
     if (lane == 0) wflag[wave] = wbad;
     __syncthreads();
@@ -161,11 +167,18 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
 #pragma unroll
     for (int k = 0; k < WPB; k++) xnan |= wflag[k];
     xnan = __builtin_amdgcn_readfirstlane(xnan);
-    if (tile >= ntiles) return;
     if (xnan) {
-        mq4_rows_plain<S, LPR, R>(w, x, y, I, O, row0, sl);
+        // the whole workgroup takes this branch; with ROT it first rebuilds
+        // x_rot as f32 over the staging area (every wave has read the flags)
+        if constexpr (ROT) {
+            __syncthreads();
+            xst.store_rotated_f32(x, items, NU, signs, xf);
+            __syncthreads();
+        }
+        if (tile < ntiles) mq4_rows_plain<S, LPR, R>(w, ROT ? xf : x, y, I, O, row0, sl);
         return;
     }
+    if (tile >= ntiles) return;
 #pragma unroll
     for (int j = 0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
     __builtin_amdgcn_sched_barrier(0);
@@ -359,64 +372,94 @@ __global__ __launch_bounds__(256) void fwht256_kernel(const float *__restrict__ 
 
 namespace {
 
-size_t mq4_lds_bytes(int S, int I)
+size_t mq4_lds_bytes(int S, int I, bool rot)
 {
-    return q8_stage_bytes(S, I / 32, true) + 16 * sizeof(int);
+    const size_t stage = q8_stage_bytes(S, I / 32, true) + 16 * sizeof(int);
+    const size_t fallback = rot ? (size_t)S * I * sizeof(float) : 0;
+    return stage > fallback ? stage : fallback;
 }
 
-template <int S, int LPR, int R, int PF, int WPB>
-hipError_t launch_t(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
+template <int S, int LPR, int R, int PF, int WPB, bool ROT>
+hipError_t launch_t(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
+                    hipStream_t st)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
     const int blocks = (ntiles + WPB - 1) / WPB;
-    const size_t lds = mq4_lds_bytes(S, I);
-    auto kern = mq4v2_gemv_stream<S, LPR, R, PF, WPB>;
+    const size_t lds = mq4_lds_bytes(S, I, ROT);
+    auto kern = mq4v2_gemv_stream<S, LPR, R, PF, WPB, ROT>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, x, y, I, O, ntiles);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, x, sg, y, I, O, ntiles);
     return hipGetLastError();
 }
 
-template <int S, int R>
-hipError_t launch_r(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
+template <int S, int R, bool ROT>
+hipError_t launch_r(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
+                    hipStream_t st)
 {
     constexpr int WPB = S == 1 ? QG_MQ4_WPB : QG_MQ4_WPB_MULTI;
     // several vectors: 16-wave workgroups leave 128 registers per lane, so
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_MQ4_PF : 2;
     switch (pick_lpr(I / 32)) {
-    case 64: return launch_t<S, 64, R, PF, WPB>(w, x, y, I, O, st);
-    case 32: return launch_t<S, 32, R, PF, WPB>(w, x, y, I, O, st);
-    case 16: return launch_t<S, 16, R, PF, WPB>(w, x, y, I, O, st);
-    default: return launch_t<S, 8, R, PF, WPB>(w, x, y, I, O, st);
+    case 64: return launch_t<S, 64, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    case 32: return launch_t<S, 32, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    case 16: return launch_t<S, 16, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    default: return launch_t<S, 8, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
     }
 }
 
-template <int S>
-hipError_t launch_s(const uint8_t *w, const float *x, float *y, int I, int O, hipStream_t st)
+template <int S, bool ROT>
+hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
+                    hipStream_t st)
 {
     if constexpr (S == 1) {
-        return launch_r<S, QG_MQ4_R>(w, x, y, I, O, st);
+        return launch_r<S, QG_MQ4_R, ROT>(w, x, sg, y, I, O, st);
     } else {
-        // several vectors: R keeps every workgroup resident at once
+        // several vectors: R keeps every workgroup resident at once.  With the
+        // rotation every workgroup rotates all S vectors, so ties go to the
+        // larger R (fewer workgroups)
         static const int cand[] = {1, 2, 3};
-        switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_MQ4_WPB_MULTI, mq4_lds_bytes(S, I),
-                                    cand, 3)) {
-        case 1: return launch_r<S, 1>(w, x, y, I, O, st);
-        case 2: return launch_r<S, 2>(w, x, y, I, O, st);
-        default: return launch_r<S, 3>(w, x, y, I, O, st);
+        static const int cand_rot[] = {3, 2, 1};
+        switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_MQ4_WPB_MULTI,
+                                    mq4_lds_bytes(S, I, ROT), ROT ? cand_rot : cand, 3)) {
+        case 1: return launch_r<S, 1, ROT>(w, x, sg, y, I, O, st);
+        case 2: return launch_r<S, 2, ROT>(w, x, sg, y, I, O, st);
+        default: return launch_r<S, 3, ROT>(w, x, sg, y, I, O, st);
         }
     }
 }
 
 // Vectors one streaming launch takes for this shape (0: not applicable).
-int mq4_stream_vectors(const void *w, const float *x, int S, int I)
+int mq4_stream_vectors(const void *w, const float *x, const int8_t *sg, int S, int I, bool rot)
 {
     if (((uintptr_t)w & 7) != 0 || ((uintptr_t)x & 15) != 0) return 0;
+    if (rot && ((uintptr_t)sg & 7) != 0) return 0;
     int n = S < MQ4_FAST_MAX_S ? S : MQ4_FAST_MAX_S;
-    while (n > 0 && mq4_lds_bytes(n, I) > LDS_BUDGET) --n;
+    while (n > 0 && mq4_lds_bytes(n, I, rot) > LDS_BUDGET) --n;
     return n;
+}
+
+// Streaming launches in groups of at most nmax vectors.
+template <bool ROT>
+hipError_t launch_groups(const uint8_t *w, const float *x, const int8_t *sg, float *y, int S,
+                         int I, int O, int nmax, hipStream_t st)
+{
+    for (int s0 = 0; s0 < S; s0 += nmax) {
+        const int n = S - s0 < nmax ? S - s0 : nmax;
+        const float *xs = x + (size_t)s0 * I;
+        float *ys = y + (size_t)s0 * O;
+        hipError_t e;
+        switch (n) {
+        case 1: e = launch_s<1, ROT>(w, xs, sg, ys, I, O, st); break;
+        case 2: e = launch_s<2, ROT>(w, xs, sg, ys, I, O, st); break;
+        case 3: e = launch_s<3, ROT>(w, xs, sg, ys, I, O, st); break;
+        default: e = launch_s<4, ROT>(w, xs, sg, ys, I, O, st); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -427,27 +470,28 @@ hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     // more vectors than one launch takes run in groups, each streaming the
     // weights once
-    const int nmax = mq4_stream_vectors(w, x, S, I);
-    if (nmax > 0) {
-        for (int s0 = 0; s0 < S; s0 += nmax) {
-            const int n = S - s0 < nmax ? S - s0 : nmax;
-            const float *xs = x + (size_t)s0 * I;
-            float *ys = y + (size_t)s0 * O;
-            hipError_t e;
-            switch (n) {
-            case 1: e = launch_s<1>(wb, xs, ys, I, O, st); break;
-            case 2: e = launch_s<2>(wb, xs, ys, I, O, st); break;
-            case 3: e = launch_s<3>(wb, xs, ys, I, O, st); break;
-            default: e = launch_s<4>(wb, xs, ys, I, O, st); break;
-            }
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }
+    const int nmax = mq4_stream_vectors(w, x, nullptr, S, I, false);
+    if (nmax > 0) return launch_groups<false>(wb, x, nullptr, y, S, I, O, nmax, st);
     const int wpb = 4;
     hipLaunchKernelGGL(mq4v2_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
                        x, y, S, I, O);
     return hipGetLastError();
+}
+
+int mq4v2_rot_check(const void *w, const float *x, const int8_t *signs, int I)
+{
+    if (((uintptr_t)w & 7) != 0 || ((uintptr_t)x & 15) != 0 || ((uintptr_t)signs & 7) != 0)
+        return QGEMV_E_ALIGN;
+    if (mq4_lds_bytes(1, I, true) > LDS_BUDGET) return QGEMV_E_DIMS;
+    return QGEMV_OK;
+}
+
+hipError_t launch_mq4v2_rot_gemv(const void *w, const float *x, const int8_t *signs, float *y,
+                                 int S, int I, int O, hipStream_t st)
+{
+    const int nmax = mq4_stream_vectors(w, x, signs, S, I, true);
+    if (nmax <= 0) return hipErrorInvalidValue;   // callers check mq4v2_rot_check first
+    return launch_groups<true>(static_cast<const uint8_t *>(w), x, signs, y, S, I, O, nmax, st);
 }
 
 hipError_t launch_mq4v2_dequant(const void *w, float *W, int I, int O, hipStream_t st)

@@ -292,18 +292,19 @@ __device__ __forceinline__ int quad_sum_i32(int v)
     return v;
 }
 
-// Converts the eight activations of one weight dword (columns 32u + 8d + 0..7,
-// in a and b) and stores their digit dwords.  The four lanes 4c..4c+3 hold the
+// Converts the eight activations of one weight dword (columns 32u + 8d + 0..7)
+// and stores their digit dwords; the stored chunk scale (and sum) is
+// multiplied by post, a power of two.  The four lanes 4c..4c+3 hold the
 // four dwords d = 0..3 of one chunk and must all call this together (the
 // chunk exponent is a max over them).  Lanes with ok == false store nothing.
 // Returns nonzero if the chunk holds an infinity or NaN (its staged values
 // are then meaningless).
 template <bool SUM>
-__device__ __forceinline__ uint32_t q8_put(f32x4 a, f32x4 b, bool ok, uint32_t t, uint32_t u,
+__device__ __forceinline__ uint32_t q8_put(const float xv[8], bool ok, uint32_t t, uint32_t u,
                                            uint32_t d, uint32_t NU, uint32_t *__restrict__ xq,
-                                           float *__restrict__ xc, float *__restrict__ xsum)
+                                           float *__restrict__ xc, float *__restrict__ xsum,
+                                           float post = 1.0f)
 {
-    const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     // |x| as ordered integers: every NaN sorts above infinity, above every finite
     uint32_t m = 0;
 #pragma unroll
@@ -345,7 +346,7 @@ __device__ __forceinline__ uint32_t q8_put(f32x4 a, f32x4 b, bool ok, uint32_t t
         for (int k = 0; k < 8; k++) vs += (int)(n[k] - Q8_DIGIT_BIAS);
         vs = quad_sum_i32(vs);
     }
-    const float cs = __builtin_bit_cast(float, (e - 20u) << 23);     // 2^(E - 21)
+    const float cs = __builtin_bit_cast(float, (e - 20u) << 23) * post;   // 2^(E - 21)
     if (ok) {
         uint32_t *q = xq + (t * 6u * NU + u) * 4u + d;
 #pragma unroll
@@ -358,24 +359,78 @@ __device__ __forceinline__ uint32_t q8_put(f32x4 a, f32x4 b, bool ok, uint32_t t
     return eb == 255u;
 }
 
+// Radix-2 Walsh-Hadamard butterflies, (a, b) -> (a + b, a - b), for the
+// strides 8, 16, ..., 128 of a 256-element block held as eight consecutive
+// values per lane by 32 consecutive lanes (lane bit m <-> stride 8 * 2^m).
+// The lane whose stride bit is set holds b and keeps a - b.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v)
+{
+    const int iv = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);
+    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);
+    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);  // row_ror:8
+    else r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (M << 10));   // xor M within 32 lanes
+    return __builtin_bit_cast(float, r);
+}
+template <int M>
+__device__ __forceinline__ void fwht_lane_stage(float v[8], int lane)
+{
+    const float sg = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) v[k] = __builtin_fmaf(sg, v[k], lane_xor<M>(v[k]));
+}
+// Unnormalised H256 of the block: strides 1, 2, 4 inside the lane, then
+// 8 .. 128 across lanes, ascending (the order of the stand-alone kernel).
+__device__ __forceinline__ void fwht256_item(float v[8], int lane)
+{
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            if (!(k & h)) {
+                const float a = v[k], b = v[k + h];
+                v[k] = a + b;
+                v[k + h] = a - b;
+            }
+    fwht_lane_stage<1>(v, lane);
+    fwht_lane_stage<2>(v, lane);
+    fwht_lane_stage<4>(v, lane);
+    fwht_lane_stage<8>(v, lane);
+    fwht_lane_stage<16>(v, lane);
+}
+
 // Stages S activation vectors of I columns (I % 32 == 0) in the fixed-point
 // layout above.  Thread f of the workgroup takes item f: the eight columns
 // 8f .. 8f + 7 (two float4 loads), so a chunk is four consecutive lanes.  As
-// with XStageN, each workgroup starts at its own chunk-aligned offset and
-// wraps around.  load() issues the thread's first NPRE items (those that
-// exist) and store() converts them, then any further items one at a time.
-// Items past the end belong to whole four-lane groups (items is a multiple
-// of four, NT of 64), which skip both.  NT is the workgroup size.  store()
-// returns nonzero in a lane that met an infinity or NaN.
-template <int S, int NPRE, int NT, bool SUM = false>
+// with XStageN, each workgroup starts at its own aligned offset and wraps
+// around.  load() issues the thread's first NPRE items (those that exist)
+// and store() converts them, then any further items one at a time.  Items
+// past the end belong to whole lane groups (items is a multiple of 32 with
+// ROT, of 4 otherwise; NT a multiple of 64), which skip both.  NT is the
+// workgroup size.  store() returns nonzero in a lane that met an infinity or
+// NaN.
+//
+// With ROT the vectors are first rotated as the FWHT-256 pre-rotation
+// defines it: x_rot = H256 (signs . x) / 16 per 256-column block (I % 256 ==
+// 0; a block is 32 items in 32 consecutive lanes, the rotation offset a
+// multiple of a block).  The butterflies run in the stand-alone kernel's
+// order, so x_rot is the same to the bit; the 1/16 goes into the chunk
+// scales.  store_rotated_f32() writes x_rot itself as f32 (the fallback for
+// activations holding an infinity or NaN).
+template <int S, int NPRE, int NT, bool SUM = false, bool ROT = false>
 struct XStageQ {
     f32x4 a[NPRE], b[NPRE];
+    u32x2 sg[ROT ? NPRE : 1];
     int rot;
 
-    __device__ __forceinline__ void load(const float *__restrict__ x, int items)
+    __device__ __forceinline__ void load(const float *__restrict__ x, int items,
+                                         const int8_t *__restrict__ signs = nullptr, int ipv = 0)
     {
-        const unsigned chunks = (unsigned)items / 4u;
-        rot = chunks ? (int)(((blockIdx.x * 2654435761u) >> 7) % chunks) * 4 : 0;
+        constexpr unsigned G = ROT ? 32u : 4u;   // rotation granule in items
+        const unsigned groups = (unsigned)items / G;
+        rot = groups ? (int)(((blockIdx.x * 2654435761u) >> 7) % groups * G) : 0;
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
             const int f = (int)threadIdx.x + j * NT;
@@ -383,35 +438,79 @@ struct XStageQ {
                 const uint32_t g = (uint32_t)stage_index(f, items, rot);
                 a[j] = ldx4(x, 2u * g);
                 b[j] = ldx4(x, 2u * g + 1u);
+                if constexpr (ROT)
+                    sg[j] = *reinterpret_cast<const u32x2 *>(signs + 8u * (g % (uint32_t)ipv));
             }
         }
     }
 
-    __device__ __forceinline__ uint32_t store(const float *__restrict__ x, int items, int NU,
-                                              uint32_t *__restrict__ xq, float *__restrict__ xc,
-                                              float *__restrict__ xsum)
+    __device__ __forceinline__ uint32_t put(f32x4 va, f32x4 vb, u32x2 sv, int g, int NU,
+                                            uint32_t *__restrict__ xq, float *__restrict__ xc,
+                                            float *__restrict__ xsum)
     {
         const int ipv = NU * 4;   // items per vector
+        int t, rem;
+        split_f<S>(g, ipv, t, rem);
+        float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        float post = 1.0f;
+        if constexpr (ROT) {
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const int8_t sk = (int8_t)((k < 4 ? sv.x : sv.y) >> (8 * (k & 3)));
+                v[k] *= (float)sk;
+            }
+            fwht256_item(v, (int)threadIdx.x & 63);
+            post = 0.0625f;
+        }
+        return q8_put<SUM>(v, true, (uint32_t)t, (uint32_t)rem >> 2, (uint32_t)rem & 3u,
+                           (uint32_t)NU, xq, xc, xsum, post);
+    }
+
+    __device__ __forceinline__ uint32_t store(const float *__restrict__ x, int items, int NU,
+                                              uint32_t *__restrict__ xq, float *__restrict__ xc,
+                                              float *__restrict__ xsum,
+                                              const int8_t *__restrict__ signs = nullptr)
+    {
         uint32_t bad = 0;
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
             const int f = (int)threadIdx.x + j * NT;
-            if (f < items) {
-                int t, rem;
-                split_f<S>(stage_index(f, items, rot), ipv, t, rem);
-                bad |= q8_put<SUM>(a[j], b[j], true, (uint32_t)t, (uint32_t)rem >> 2,
-                                   (uint32_t)rem & 3u, (uint32_t)NU, xq, xc, xsum);
-            }
+            if (f < items)
+                bad |= put(a[j], b[j], ROT ? sg[j] : u32x2{0, 0}, stage_index(f, items, rot), NU,
+                           xq, xc, xsum);
         }
         for (int f = (int)threadIdx.x + NPRE * NT; f < items; f += NT) {
             const int g = stage_index(f, items, rot);
-            int t, rem;
-            split_f<S>(g, ipv, t, rem);
-            bad |= q8_put<SUM>(ldx4(x, 2u * (uint32_t)g), ldx4(x, 2u * (uint32_t)g + 1u), true,
-                               (uint32_t)t, (uint32_t)rem >> 2, (uint32_t)rem & 3u,
-                               (uint32_t)NU, xq, xc, xsum);
+            u32x2 sv = {0, 0};
+            if constexpr (ROT)
+                sv = *reinterpret_cast<const u32x2 *>(signs + 8u * ((uint32_t)g % (uint32_t)(NU * 4)));
+            bad |= put(ldx4(x, 2u * (uint32_t)g), ldx4(x, 2u * (uint32_t)g + 1u), sv, g, NU, xq,
+                       xc, xsum);
         }
         return bad;
+    }
+
+    // ROT only: writes the rotated vectors as f32, xf[t][I] = x_rot (the
+    // stand-alone kernel's values to the bit), for the per-element fallback.
+    __device__ __forceinline__ void store_rotated_f32(const float *__restrict__ x, int items, int NU,
+                                                      const int8_t *__restrict__ signs,
+                                                      float *__restrict__ xf)
+    {
+        const int ipv = NU * 4;
+        for (int f = (int)threadIdx.x; f < items; f += NT) {
+            int t, rem;
+            split_f<S>(f, ipv, t, rem);
+            const f32x4 va = ldx4(x, 2u * (uint32_t)f), vb = ldx4(x, 2u * (uint32_t)f + 1u);
+            const u32x2 sv = *reinterpret_cast<const u32x2 *>(signs + 8u * (uint32_t)rem);
+            float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                v[k] *= (float)(int8_t)((k < 4 ? sv.x : sv.y) >> (8 * (k & 3)));
+            fwht256_item(v, (int)threadIdx.x & 63);
+            f32x4 *dst = reinterpret_cast<f32x4 *>(xf + ((size_t)t * ipv * 8 + (size_t)rem * 8));
+            dst[0] = f32x4{v[0] * 0.0625f, v[1] * 0.0625f, v[2] * 0.0625f, v[3] * 0.0625f};
+            dst[1] = f32x4{v[4] * 0.0625f, v[5] * 0.0625f, v[6] * 0.0625f, v[7] * 0.0625f};
+        }
     }
 };
 

@@ -58,6 +58,12 @@ hipError_t launch_fp8b128_dequant(const void *w, const float *scale_inv, float *
 // MQ4-v2 and the FWHT-256 rotation
 hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int I, int O,
                              hipStream_t st);
+// Fused rotation + GEMV: QGEMV_OK if the fused kernel takes the shape
+// (8-byte aligned w and signs, 16-byte aligned x, one vector's staging within
+// the LDS), else the refusal code.
+int mq4v2_rot_check(const void *w, const float *x, const int8_t *signs, int I);
+hipError_t launch_mq4v2_rot_gemv(const void *w, const float *x, const int8_t *signs, float *y,
+                                 int S, int I, int O, hipStream_t st);
 hipError_t launch_mq4v2_dequant(const void *w, float *W, int I, int O, hipStream_t st);
 hipError_t launch_fwht256(const float *x, const int8_t *signs, float *xr, int S, int I,
                           hipStream_t st);

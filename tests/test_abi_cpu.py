@@ -53,3 +53,24 @@ def test_i4g_refusals(q):
     assert f(BAD, BAD, BAD, BAD + 1, 1, 64, 8, 64, 0) == 4      # misaligned y
     assert q.qgemv_dequant_i4g(BAD, BAD, 0, 64, 8, 64, 0) == 1
     assert q.qgemv_dequant_i4g(BAD, BAD, BAD, 64, 8, 5, 0) == 3
+
+
+def test_mq4_refusals(q):
+    assert q.qgemv_mq4v2(BAD, BAD, BAD, 1, 300, 8, 0) == 5                 # I % 256
+    assert q.qgemv_mq4v2(BAD, BAD, 0, 1, 256, 8, 0) == 1
+    assert q.qgemv_fwht256(BAD, BAD, BAD + 4, 1, 256, 0) == 4              # x_rot misaligned
+    r = q.qgemv_mq4v2_rot
+    assert r(BAD, BAD, 0, BAD, 1, 256, 8, 0) == 1                          # NULL signs
+    assert r(BAD, BAD, BAD, BAD, 9, 256, 8, 0) == 2                        # S > 8
+    assert r(BAD, BAD, BAD, BAD, 1, 300, 8, 0) == 5                        # I % 256
+    assert r(BAD, BAD, BAD + 4, BAD, 1, 256, 8, 0) == 4                    # signs misaligned
+    assert r(BAD, BAD + 8, BAD, BAD, 1, 256, 8, 0) == 4                    # x misaligned
+    assert r(BAD + 4, BAD, BAD, BAD, 1, 256, 8, 0) == 4                    # w misaligned
+    assert r(BAD, BAD, BAD, BAD, 1, 65536, 8, 0) == 2                      # staging > LDS
+
+
+def test_fp8_refusals(q):
+    f = q.qgemv_fp8b128
+    assert f(0, BAD, BAD, BAD, 1, 64, 8, 0) == 1
+    assert f(BAD, BAD, BAD, BAD, 1, 64, 0, 0) == 2
+    assert f(BAD, BAD + 1, BAD, BAD, 1, 64, 8, 0) == 4

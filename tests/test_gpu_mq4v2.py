@@ -127,3 +127,52 @@ def test_rotate_then_gemv_end_to_end(q, qref):
     y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), xr))
     ref = qref.mq4v2_gemv(d["w"], qref.fwht256(d["x"], d["signs"], I), O, I)
     assert_y_close(y, ref)
+
+
+def _two_launch(q, w, x, signs):
+    xr = q.fwht256(x, signs)
+    return q.mq4v2(w, xr)
+
+
+@pytest.mark.parametrize("O,I,S", [(8192, 8192, 1), (256, 512, 1), (300, 1024, 2),
+                                   (77, 256, 3), (1000, 4096, 4), (33, 2304, 1), (5, 768, 6)])
+def test_fused_rotation_matches_two_launches_bitwise(q, qref, O, I, S):
+    # one launch == qgemv_fwht256 then qgemv_mq4v2, to the bit; and the oracle
+    d = W.gen_mq4v2(O, I, S=S, seed=O + 11)
+    w, x, sg = dev(d["w"].reshape(O, -1)), dev(d["x"]), dev(d["signs"])
+    fused = host(q.mq4v2_rot(w, x, sg))
+    two = host(_two_launch(q, w, x, sg))
+    assert np.array_equal(fused.view(np.uint32), two.view(np.uint32))
+    if O * I <= 1 << 22:
+        ref = qref.mq4v2_gemv(d["w"], qref.fwht256(d["x"], d["signs"], I), O, I)
+    else:
+        rows = np.arange(0, O, 97)
+        ref = qref.mq4v2_gemv(d["w"], qref.fwht256(d["x"], d["signs"], I), O, I, rows=rows)
+        fused = fused[:, rows]
+    assert_y_close(fused, ref)
+
+
+def test_fused_rotation_non_finite_activations(q):
+    # an infinity and a NaN in x: the same NaN / inf pattern and values as the
+    # two-launch path
+    O, I, S = 200, 2048, 2
+    d = W.gen_mq4v2(O, I, S=S, seed=3)
+    d["x"][0, 700] = np.inf
+    d["x"][1, 5] = np.nan
+    w, x, sg = dev(d["w"].reshape(O, -1)), dev(d["x"]), dev(d["signs"])
+    fused = host(q.mq4v2_rot(w, x, sg))
+    two = host(_two_launch(q, w, x, sg))
+    assert np.array_equal(np.isnan(fused), np.isnan(two))
+    ok = ~np.isnan(two)
+    assert np.array_equal(fused[ok].view(np.uint32), two[ok].view(np.uint32))
+
+
+def test_fused_rotation_refuses_large_i(q):
+    import torch
+    O, I = 4, 65536
+    d = W.gen_mq4v2(O, I, seed=1)
+    y = torch.empty((1, O), device="cuda")
+    st = q.qgemv_mq4v2_rot(dev(d["w"]).data_ptr(), dev(d["x"]).data_ptr(),
+                           dev(d["signs"]).data_ptr(), y.data_ptr(), 1, I, O,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 2
