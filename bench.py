@@ -12,8 +12,8 @@ A step is one pass of the hot path over one batch of synthetic input:
       one qgemv_fp8b128 call
   mq4v2_O8192_I8192:
       one qgemv_mq4v2_rot call (the FWHT-256 rotation of x fused into the
-      GEMV; the same result as qgemv_fwht256 followed by qgemv_mq4v2); the
-      _S2 / _S4 steps call qgemv_fwht256 then qgemv_mq4v2
+      GEMV; the same result as qgemv_fwht256 followed by qgemv_mq4v2), also
+      for _S2; the _S4 step calls qgemv_fwht256 then qgemv_mq4v2
   moe_E256_O2048_I7168_gs64_T4_K8:
       one qgemv_moe_topk call (4 tokens, top-8 of 256 experts)
 
@@ -162,13 +162,13 @@ class MQ4(Case):
         self.fmt_desc = "MQ4-v2 136 B / 256 weights, FWHT-256 rotated activations" + (f", {S} vectors per call" if S > 1 else "")
         self.O, self.I, self.S = O, I, S
         self.weight_bytes = O * (I // 256) * 136
-        # one vector: one fused launch (weights, x, signs in; y out), the
-        # rotated activations never leave the chip.  Several vectors: the
-        # rotation kernel (x, signs in; x_rot out) then the GEMV (weights,
-        # x_rot in; y out) -- every workgroup of the fused kernel would
-        # rotate all S vectors, which costs more than the extra launch
+        # up to two vectors: one fused launch (weights, x, signs in; y out),
+        # the rotated activations never leave the chip.  Four: the rotation
+        # kernel (x, signs in; x_rot out) then the GEMV (weights, x_rot in;
+        # y out) -- every workgroup of the fused kernel rotates all S
+        # vectors, which at S = 4 costs more than the extra launch
         self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4) + I
-        if S > 1:
+        if S > 2:
             self.alg_bytes += S * I * 8
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
@@ -202,10 +202,10 @@ class MQ4(Case):
 
     def step(self, i):
         q = self.q
-        if self.S == 1:
+        if self.S <= 2:
             st = q.qgemv_mq4v2_rot(self.ptrs[i % self.n], self.x.data_ptr(),
-                                   self.signs.data_ptr(), self.y.data_ptr(), 1, self.I, self.O,
-                                   self.sp)
+                                   self.signs.data_ptr(), self.y.data_ptr(), self.S, self.I,
+                                   self.O, self.sp)
         else:
             st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(),
                                  self.S, self.I, self.sp)

@@ -44,9 +44,10 @@ namespace qg {
 
 constexpr int FP8_FAST_MAX_S = 4;
 
-// Stages up to 8 vectors into the fp8 LDS layout with coalesced float4 loads;
-// as XStageN, the first NPRE float4s per thread are loaded unconditionally
-// (indices clamped) so later waits count exactly.
+// Stages up to 8 vectors into the fp8 LDS layout with coalesced float4 loads
+// (thread f reads float4 number f, from the offset stage_rot picks); the
+// first NPRE float4s per thread are loaded unconditionally (indices clamped)
+// so later waits count exactly.
 template <int NPRE, int NT>
 struct XStageF8 {
     f32x4 v[NPRE];

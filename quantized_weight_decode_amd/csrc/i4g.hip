@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     // so the compiler can wait for exactly the load a value comes from
     // instead of draining all outstanding loads.
     // 1. activations first (L2-resident)
-    XStageQ<S, QG_I4G_NPRE, 64 * WPB> xst;
+    XStageQ<S, (S > 2 ? 4 : QG_I4G_NPRE), 64 * WPB> xst;
     const int items = S * NU * 4;
     xst.load(x, items);
     // every wave of the workgroup has issued its activation loads before any

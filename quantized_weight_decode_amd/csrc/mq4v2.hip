@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * rowbytes;
 
-    XStageQ<S, QG_MQ4_NPRE, 64 * WPB, true, ROT> xst;
+    XStageQ<S, (S > 2 ? 4 : QG_MQ4_NPRE), 64 * WPB, true, ROT> xst;
     const int items = S * NU * 4;
     xst.load(x, items, signs, NU * 4);
 

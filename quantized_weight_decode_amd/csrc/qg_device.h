@@ -88,55 +88,17 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
 }
 
-// 8-lane sum (lanes 8m..8m+7); lane 8m+7 holds it.  Defined before use.
-__device__ __forceinline__ float sub_reduce8(float v);
-
 // ---------------------------------------------------------------------------
-// Activation staging for the 4-bit formats.
-//
-// A "lane chunk" is 16 packed bytes = 32 columns.  For chunk u and segment
-// k = 0..7 the LDS holds one float4:
-//    k = 2d   : x[32u + 8d + {0,2,4,6}]   (matches low nibbles of dword d)
-//    k = 2d+1 : x[32u + 8d + {1,3,5,7}]   (matches high nibbles)
-// stored at float4 index (k * NS + u), NU = chunks per vector, so that lanes
-// reading consecutive chunks touch consecutive 16-byte LDS words (no bank
-// conflicts).  The segment stride NS = NU + 1 is padded by one float4: with
-// NS a multiple of 16 the staging writes of the eight segments of one chunk
-// (made by eight neighbouring lanes) would all land in the same banks.  xs[u] = plain f32 sum of the chunk's 32 activations, used to
-// fold per-chunk affine offsets out of the inner loop.  The nibble decoder
-// returns q * 2^-9, so a chunk's dot product comes out as 2^-9 sum(q x) and
-// the fold multiplies it back by 2^9 (exact).
+// Activation staging helpers.
 // ---------------------------------------------------------------------------
-// float4 number i of an array (32-bit offset from a wave-uniform base)
+// Segment stride (in float4s) of the fp8 kernel's staged activations: one
+// float4 of padding keeps the staging writes of one chunk out of one bank.
 __host__ __device__ constexpr int seg_stride(int NU) { return NU + 1; }
 
+// float4 number i of an array (32-bit offset from a wave-uniform base)
 __device__ __forceinline__ f32x4 ldx4(const float *__restrict__ base, uint32_t i)
 {
     return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(base) + i * 16u);
-}
-
-// Places float4 number f of vector t into the LDS layout and adds its part of
-// the chunk sum.  rem = f - t * 8 NU is the float4's index inside its vector.
-// Every lane of the wave must call this (the chunk sum is an 8-lane DPP
-// reduction over consecutive lanes); lanes with ok == false compute but store
-// nothing (their 8-lane group is entirely out of range).
-__device__ __forceinline__ void XStagePut(f32x4 a, bool ok, int t, int rem, int NU,
-                                          f32x4 *__restrict__ xl, float *__restrict__ xs)
-{
-    const uint32_t u = (uint32_t)rem >> 3, k = (uint32_t)rem & 7;
-    const uint32_t d = k >> 1, h = k & 1;
-    const uint32_t NS = (uint32_t)seg_stride(NU);
-    float *base = reinterpret_cast<float *>(xl) + (uint32_t)t * 32u * NS;
-    const uint32_t oe = ((2 * d) * NS + u) * 4 + 2 * h;
-    const uint32_t oo = oe + 4u * NS;
-    f32x2 ev = {a.x, a.z};
-    f32x2 od = {a.y, a.w};
-    const float cs = sub_reduce8((a.x + a.y) + (a.z + a.w));
-    if (ok) {
-        *reinterpret_cast<f32x2 *>(base + oe) = ev;
-        *reinterpret_cast<f32x2 *>(base + oo) = od;
-        if (k == 7) xs[(uint32_t)t * (uint32_t)NU + u] = cs;
-    }
 }
 
 // vector index t (< TMAX) and in-vector index of float4 number f; cpv = 8 NU
@@ -166,77 +128,6 @@ __device__ __forceinline__ int stage_index(int f, int total, int rot)
     const int g = min(f, total - 1) + rot;
     return g >= total ? g - total : g;
 }
-
-// Stages S (<= 8) activation vectors of I columns into the LDS layout above.
-// Loads are coalesced: thread f of the workgroup reads float4 number f of x
-// (each load instruction of a wave covers 1 KB of consecutive bytes); the
-// eight float4s of one lane chunk sit in eight consecutive lanes, whose sum is
-// formed with an 8-lane DPP reduction.  load() issues NPRE float4s per thread
-// unconditionally (indices clamped into range) and store() consumes them
-// unconditionally, so a caller that issues the weight stream in between
-// waits for exactly these loads.  NT is the workgroup size (a multiple of
-// 64), a compile-time constant: reading blockDim.x would cost a dependent
-// memory load before the first activation load could issue.
-template <int S, int NPRE, int NT>
-struct XStageN {
-    f32x4 v[NPRE];
-
-    int rot;
-
-    __device__ __forceinline__ void load(const float *__restrict__ x, int total)
-    {
-        rot = stage_rot(total);
-#pragma unroll
-        for (int j = 0; j < NPRE; j++)
-            v[j] = ldx4(x, (uint32_t)stage_index((int)threadIdx.x + j * NT, total, rot));
-    }
-
-    __device__ __forceinline__ void store(const float *__restrict__ x, int total, int NU,
-                                          f32x4 *__restrict__ xl, float *__restrict__ xs)
-    {
-        const int cpv = NU * 8;
-#pragma unroll
-        for (int j = 0; j < NPRE; j++) {
-            const int f = (int)threadIdx.x + j * NT;
-            int t, rem;
-            split_f<S>(stage_index(f, total, rot), cpv, t, rem);
-            XStagePut(v[j], f < total, t, rem, NU, xl, xs);
-        }
-        // remainder (shapes with more than NPRE float4s per thread)
-        const int nrest = (total - NPRE * NT + NT - 1) / NT;
-        for (int it = 0; it < nrest; it++) {
-            const int f = (int)threadIdx.x + (NPRE + it) * NT;
-            const int g = stage_index(f, total, rot);
-            int t, rem;
-            split_f<S>(g, cpv, t, rem);
-            XStagePut(ldx4(x, (uint32_t)g), f < total, t, rem, NU, xl, xs);
-        }
-    }
-};
-
-// 2^-9 * sum over the 32 columns of one lane chunk of q*x.
-__device__ __forceinline__ float nib_chunk_dot(const u32x4 wv, const f32x4 *__restrict__ xl,
-                                               int NU, int u)
-{
-    float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-        float e[4], o[4];
-        nib8(wv[d], e, o);
-        const f32x4 xe = xl[(2 * d) * seg_stride(NU) + u];
-        const f32x4 xo = xl[(2 * d + 1) * seg_stride(NU) + u];
-        p0 = __builtin_fmaf(e[0], xe.x, p0);
-        p1 = __builtin_fmaf(o[0], xo.x, p1);
-        p0 = __builtin_fmaf(e[1], xe.y, p0);
-        p1 = __builtin_fmaf(o[1], xo.y, p1);
-        p0 = __builtin_fmaf(e[2], xe.z, p0);
-        p1 = __builtin_fmaf(o[2], xo.z, p1);
-        p0 = __builtin_fmaf(e[3], xe.w, p0);
-        p1 = __builtin_fmaf(o[3], xo.w, p1);
-    }
-    return p0 + p1;
-}
-
 
 // ---------------------------------------------------------------------------
 // Integer-dot form of the 4-bit chunk product.
@@ -403,9 +294,9 @@ __device__ __forceinline__ void fwht256_item(float v[8], int lane)
 
 // Stages S activation vectors of I columns (I % 32 == 0) in the fixed-point
 // layout above.  Thread f of the workgroup takes item f: the eight columns
-// 8f .. 8f + 7 (two float4 loads), so a chunk is four consecutive lanes.  As
-// with XStageN, each workgroup starts at its own aligned offset and wraps
-// around.  load() issues the thread's first NPRE items (those that exist)
+// 8f .. 8f + 7 (two float4 loads), so a chunk is four consecutive lanes.
+// Each workgroup starts at its own aligned offset and wraps around, as
+// stage_rot describes.  load() issues the thread's first NPRE items (those that exist)
 // and store() converts them, then any further items one at a time.  Items
 // past the end belong to whole lane groups (items is a multiple of 32 with
 // ROT, of 4 otherwise; NT a multiple of 64), which skip both.  NT is the
@@ -603,8 +494,6 @@ __device__ __forceinline__ float sub_reduce(float v)
     if (LPR >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
     return v;
 }
-
-__device__ __forceinline__ float sub_reduce8(float v) { return sub_reduce<8>(v); }
 
 // ---------------------------------------------------------------------------
 // floor(u / d) via a 64-bit reciprocal multiply, exact whenever u * d < 2^40
