@@ -10,6 +10,9 @@ A step is one pass of the hot path over one batch of synthetic input:
       the same step on 2 or 4 activation vectors per call (multi-token decode)
   fp8b128_O7168_I16384:
       one qgemv_fp8b128 call
+  fp8ue8m0_O7168_I16384:
+      one qgemv_fp8b128_ue8m0 call (the same weights with power-of-two
+      UE8M0 block scale bytes)
   mq4v2_O8192_I8192:
       one qgemv_mq4v2_rot call (the FWHT-256 rotation of x fused into the
       GEMV; the same result as qgemv_fwht256 followed by qgemv_mq4v2), also
@@ -153,6 +156,49 @@ class FP8(Case):
             raise SystemExit(f"qgemv_fp8b128: {self.q.strerror(st)}")
 
 
+class FP8E8(Case):
+    """fp8-e4m3 with UE8M0 (one power-of-two byte per 128x128 block) scales."""
+    kernel = "fp8_gemv_stream"
+
+    def __init__(self, O, I, torch, q, o, S=1):
+        import workloads as W
+        self.name = f"fp8ue8m0_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = "fp8 e4m3, UE8M0 scale byte per 128x128 block" + (f", {S} vectors per call" if S > 1 else "")
+        self.O, self.I, self.S = O, I, S
+        nbo, nbi = W.fp8_nblocks(O, I)
+        self.weight_bytes = O * I + nbo * nbi
+        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4)
+        self.bytes_per_weight = self.weight_bytes / (O * I)
+        dev = torch.device("cuda:0")
+        d = W.gen_fp8ue8m0(O, I, S=S, seed=0)
+        self.n = n_copies(self.weight_bytes)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        self.ws = [torch.from_numpy(d["w"]).to(dev)]
+        self.ss = [torch.from_numpy(d["scale_e8m0"]).to(dev)]
+        for _ in range(1, self.n):
+            v = torch.randint(0, 254, (O, I), dtype=torch.uint8, device=dev, generator=g)
+            self.ws.append(v + (v >= 0x7F).to(torch.uint8))
+            self.ss.append(torch.randint(114, 121, (nbo, nbi), dtype=torch.uint8, device=dev,
+                                         generator=g))
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
+        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
+        self.step(0)
+        ref = o.fp8ue8m0_gemv(d["w"], d["scale_e8m0"], d["x"], O, I)
+        self.rel = _rel(self.y.cpu().numpy(), ref)
+        _check(self.rel, self.name)
+        self.cpu = lambda: o.fp8ue8m0_gemv(d["w"], d["scale_e8m0"], d["x"], O, I)
+
+    def step(self, i):
+        wp, spp = self.ptrs[i % self.n]
+        st = self.q.qgemv_fp8b128_ue8m0(wp, spp, self.x.data_ptr(), self.y.data_ptr(), self.S,
+                                        self.I, self.O, self.sp)
+        if st:
+            raise SystemExit(f"qgemv_fp8b128_ue8m0: {self.q.strerror(st)}")
+
+
 class MQ4(Case):
     kernel = "mq4v2_gemv_stream"
 
@@ -284,6 +330,7 @@ def build_case(name, torch, q, o):
         "fp8b128_O7168_I16384_S4": lambda: FP8(7168, 16384, torch, q, o, S=4),
         "mq4v2_O8192_I8192_S2": lambda: MQ4(8192, 8192, torch, q, o, S=2),
         "mq4v2_O8192_I8192_S4": lambda: MQ4(8192, 8192, torch, q, o, S=4),
+        "fp8ue8m0_O7168_I16384": lambda: FP8E8(7168, 16384, torch, q, o),
     }
     return table[name]()
 
@@ -292,7 +339,7 @@ CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_
               "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64",
               "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4",
               "fp8b128_O7168_I16384_S2", "fp8b128_O7168_I16384_S4",
-              "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4"]
+              "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4", "fp8ue8m0_O7168_I16384"]
 
 
 KERNEL_SOURCES = {

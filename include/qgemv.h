@@ -78,6 +78,19 @@ int qgemv_fp8b128(const void *w, const float *scale_inv, const float *x,
                   float *y, int S, int I, int O, void *stream);
 
 /*
+ * fp8-e4m3 with UE8M0 block scales: the same weight geometry as
+ * qgemv_fp8b128 with one scale byte per 128x128 block holding a power-of-two
+ * exponent (colibri PR #528, section "Design": dtype F8_E8M0, one byte per
+ * block).  The page names the dtype without its decode; the reading taken is
+ * the dtype's definition: scale = 2^(e - 127), e = 255 is NaN.
+ *   scale_e8m0  u8 [ceil(O/128)][ceil(I/128)] row-major block order;
+ *               weight (o,i) = e4m3(w[o][i]) * 2^(scale_e8m0[o/128][i/128] - 127)
+ *   w, x, y     as qgemv_fp8b128
+ */
+int qgemv_fp8b128_ue8m0(const void *w, const uint8_t *scale_e8m0, const float *x, float *y,
+                        int S, int I, int O, void *stream);
+
+/*
  * MQ4-v2: hipfire "MQ4 V2" page, sections 2 and 4.
  *   w      u8 [O][I/256][136]; per 256-weight group, little-endian:
  *          bytes 0..3  dword: fp16 scale (low 16 bits), fp16 zero (high 16)
@@ -161,6 +174,8 @@ int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I,
                       int O, int gs, void *stream);
 int qgemv_dequant_fp8b128(const void *w, const float *scale_inv, float *W,
                           int I, int O, void *stream);
+int qgemv_dequant_fp8b128_ue8m0(const void *w, const uint8_t *scale_e8m0, float *W, int I,
+                                int O, void *stream);
 int qgemv_dequant_mq4v2(const void *w, float *W, int I, int O, void *stream);
 
 #ifdef __cplusplus

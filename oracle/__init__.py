@@ -53,6 +53,8 @@ class Oracle:
         self.path = path
         L.qref_e4m3.restype = C.c_double
         L.qref_e4m3.argtypes = [C.c_uint8]
+        L.qref_e8m0.restype = C.c_double
+        L.qref_e8m0.argtypes = [C.c_uint8]
         L.qref_f16.restype = C.c_double
         L.qref_f16.argtypes = [C.c_uint16]
         L.qref_set_threads.argtypes = [C.c_int]
@@ -63,19 +65,25 @@ class Oracle:
         L.qref_i4g_gemv.argtypes = [_u8p, _f32p, _f32p, _f32p, I, I, I, I, _rowsp, I]
         L.qref_fp8b128_dequant.argtypes = [_u8p, _f32p, I, I, _f32p]
         L.qref_fp8b128_gemv.argtypes = [_u8p, _f32p, _f32p, _f32p, I, I, I, _rowsp, I]
+        L.qref_fp8ue8m0_dequant.argtypes = [_u8p, _u8p, I, I, _f32p]
+        L.qref_fp8ue8m0_gemv.argtypes = [_u8p, _u8p, _f32p, _f32p, I, I, I, _rowsp, I]
         L.qref_mq4v2_dequant.argtypes = [_u8p, I, I, _f32p]
         L.qref_mq4v2_gemv.argtypes = [_u8p, _f32p, _f32p, I, I, I, _rowsp, I]
         L.qref_fwht256.argtypes = [_f32p, _i8p, _f32p, I, I]
         L.qref_moe_i4g.argtypes = [_u8p, _f32p, C.c_longlong, C.c_longlong, I, _i32p,
                                    _f32p, I, I, _f32p, _f32p, I, I, I, _rowsp, I]
         for f in (L.qref_i4g_dequant, L.qref_i4g_gemv, L.qref_fp8b128_dequant,
-                  L.qref_fp8b128_gemv, L.qref_mq4v2_dequant, L.qref_mq4v2_gemv,
+                  L.qref_fp8b128_gemv, L.qref_fp8ue8m0_dequant, L.qref_fp8ue8m0_gemv,
+                  L.qref_mq4v2_dequant, L.qref_mq4v2_gemv,
                   L.qref_fwht256, L.qref_moe_i4g, L.qref_set_threads):
             f.restype = None
 
     # -- scalars ---------------------------------------------------------
     def e4m3(self, b: int) -> float:
         return self.lib.qref_e4m3(b)
+
+    def e8m0(self, e: int) -> float:
+        return self.lib.qref_e8m0(e)
 
     def f16(self, h: int) -> float:
         return self.lib.qref_f16(h)
@@ -132,6 +140,20 @@ class Oracle:
         return y
 
     # -- MQ4-v2 ----------------------------------------------------------
+    # -- fp8 with UE8M0 block scales ----------------------------------------
+    def fp8ue8m0_dequant(self, w, se, O, I):
+        W = np.empty((O, I), np.float32)
+        self.lib.qref_fp8ue8m0_dequant(self._c(w, np.uint8), self._c(se, np.uint8), O, I, W)
+        return W
+
+    def fp8ue8m0_gemv(self, w, se, x, O, I, rows=None):
+        x = self._c(x, np.float32).reshape(-1, I)
+        r, rp, n = self._rows(rows)
+        y = np.empty((x.shape[0], n if rows is not None else O), np.float32)
+        self.lib.qref_fp8ue8m0_gemv(self._c(w, np.uint8), self._c(se, np.uint8), x, y,
+                                    x.shape[0], I, O, rp, n)
+        return y
+
     def mq4v2_dequant(self, w, O, I):
         W = np.empty((O, I), np.float32)
         self.lib.qref_mq4v2_dequant(self._c(w, np.uint8), O, I, W)

@@ -201,6 +201,60 @@ void qref_fp8b128_gemv(const uint8_t *w, const float *sc, const float *x,
     }
 }
 
+/*
+ * UE8M0 block scale byte -> value.  "fmt=7: fp8-e4m3-b128 passthrough weight
+ * format", section "Design": the same weight geometry also ships with one
+ * byte per 128x128 block holding a power-of-two exponent (dtype F8_E8M0).
+ * The page names the dtype without its decode; the reading taken is that
+ * dtype's usual definition: unsigned, no sign or mantissa bits, value
+ * 2^(e - 127), and e = 255 is NaN (no zero, no infinity).
+ */
+double qref_e8m0(uint8_t e)
+{
+    if (e == 255)
+        return NAN;
+#if QREF_MUTATE == 11 /* planted: exponent bias 128 */
+    return ldexp(1.0, (int)e - 128);
+#else
+    return ldexp(1.0, (int)e - 127);
+#endif
+}
+
+/* Exact value of weight (o, i) with UE8M0 block scales (layout as fmt=7). */
+static double fp8e8_weight(const uint8_t *w, const uint8_t *se, int O, int I,
+                           int o, int i)
+{
+    int nbi = (I + 127) / 128;
+    (void)O;
+    return qref_e4m3(w[(size_t)o * I + i]) * qref_e8m0(se[(size_t)(o / 128) * nbi + i / 128]);
+}
+
+void qref_fp8ue8m0_dequant(const uint8_t *w, const uint8_t *se, int O, int I,
+                           float *W)
+{
+    for (int o = 0; o < O; o++)
+        for (int i = 0; i < I; i++)
+            W[(size_t)o * I + i] = (float)fp8e8_weight(w, se, O, I, o, i);
+}
+
+void qref_fp8ue8m0_gemv(const uint8_t *w, const uint8_t *se, const float *x,
+                        float *y, int S, int I, int O, const int *rows,
+                        int nrows)
+{
+    int n = rows ? nrows : O;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int r = 0; r < n; r++) {
+        int o = rows ? rows[r] : r;
+        for (int t = 0; t < S; t++) {
+            double acc = 0.0;
+            for (int i = 0; i < I; i++)
+                acc += fp8e8_weight(w, se, O, I, o, i) * (double)x[(size_t)t * I + i];
+            y[(size_t)t * n + r] = (float)acc;
+        }
+    }
+}
+
+
 /* ------------------------------------------------------------------------ */
 /* MQ4-v2: 136 bytes per 256 weights                                         */
 /* ------------------------------------------------------------------------ */

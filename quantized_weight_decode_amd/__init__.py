@@ -30,6 +30,8 @@ _SIGS = {
                             C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_fp8b128": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_fp8b128_ue8m0": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_mq4v2_rot": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -46,6 +48,8 @@ _SIGS = {
                                     C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_dequant_fp8b128": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_dequant_fp8b128_ue8m0": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                                              C.c_int, C.c_int, C.c_void_p]),
     "qgemv_dequant_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p,
                                       C.c_int, C.c_int, C.c_void_p]),
 }
@@ -109,6 +113,10 @@ def qgemv_fp8b128(w, scale_inv, x, y, S, I, O, stream):
     return lib().qgemv_fp8b128(w, scale_inv, x, y, S, I, O, stream)
 
 
+def qgemv_fp8b128_ue8m0(w, scale_e8m0, x, y, S, I, O, stream):
+    return lib().qgemv_fp8b128_ue8m0(w, scale_e8m0, x, y, S, I, O, stream)
+
+
 def qgemv_mq4v2(w, x_rot, y, S, I, O, stream):
     return lib().qgemv_mq4v2(w, x_rot, y, S, I, O, stream)
 
@@ -137,6 +145,10 @@ def qgemv_dequant_i4g(w, scales, W, I, O, gs, stream):
 
 def qgemv_dequant_fp8b128(w, scale_inv, W, I, O, stream):
     return lib().qgemv_dequant_fp8b128(w, scale_inv, W, I, O, stream)
+
+
+def qgemv_dequant_fp8b128_ue8m0(w, scale_e8m0, W, I, O, stream):
+    return lib().qgemv_dequant_fp8b128_ue8m0(w, scale_e8m0, W, I, O, stream)
 
 
 def qgemv_dequant_mq4v2(w, W, I, O, stream):
@@ -191,6 +203,18 @@ def fp8b128(w, scale_inv, x, out=None):
     y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
     _call("qgemv_fp8b128", _dev(w, "w", torch.uint8), _dev(scale_inv, "scale_inv", torch.float32),
           _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, _stream())
+    return y
+
+
+def fp8b128_ue8m0(w, scale_e8m0, x, out=None):
+    """fp8-e4m3 GEMV with UE8M0 (power-of-two byte) block scales."""
+    torch = _torch()
+    O, I = w.shape[0], x.shape[-1]
+    S = _vecs(x, I)
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _call("qgemv_fp8b128_ue8m0", _dev(w, "w", torch.uint8),
+          _dev(scale_e8m0, "scale_e8m0", torch.uint8), _dev(x, "x", torch.float32),
+          _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
 
 
@@ -268,6 +292,15 @@ def dequant_fp8b128(w, scale_inv):
     W = torch.empty((O, I), dtype=torch.float32, device=w.device)
     _call("qgemv_dequant_fp8b128", _dev(w, "w", torch.uint8),
           _dev(scale_inv, "scale_inv", torch.float32), _dev(W, "W"), I, O, _stream())
+    return W
+
+
+def dequant_fp8b128_ue8m0(w, scale_e8m0):
+    torch = _torch()
+    O, I = w.shape
+    W = torch.empty((O, I), dtype=torch.float32, device=w.device)
+    _call("qgemv_dequant_fp8b128_ue8m0", _dev(w, "w", torch.uint8),
+          _dev(scale_e8m0, "scale_e8m0", torch.uint8), _dev(W, "W"), I, O, _stream())
     return W
 
 

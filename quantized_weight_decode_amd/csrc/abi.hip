@@ -140,6 +140,24 @@ int qgemv_dequant_fp8b128(const void *w, const float *scale_inv, float *W, int I
     return launched(qg::launch_fp8b128_dequant(w, scale_inv, W, I, O, (hipStream_t)stream));
 }
 
+int qgemv_fp8b128_ue8m0(const void *w, const uint8_t *scale_e8m0, const float *x, float *y,
+                        int S, int I, int O, void *stream)
+{
+    if (!w || !scale_e8m0 || !x || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_fp8ue8m0_gemv(w, scale_e8m0, x, y, S, I, O, (hipStream_t)stream));
+}
+
+int qgemv_dequant_fp8b128_ue8m0(const void *w, const uint8_t *scale_e8m0, float *W, int I, int O,
+                                void *stream)
+{
+    if (!w || !scale_e8m0 || !W) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (mis4(W)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_fp8ue8m0_dequant(w, scale_e8m0, W, I, O, (hipStream_t)stream));
+}
+
 int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I, int O, void *stream)
 {
     if (!w || !x_rot || !y) return QGEMV_E_NULL;

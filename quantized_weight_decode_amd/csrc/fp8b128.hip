@@ -91,6 +91,15 @@ struct XStageF8 {
     }
 };
 
+// Block scale value: an f32 as stored, or a UE8M0 byte read as 2^(e - 127)
+// (e = 0 is the f32 subnormal 2^-127, e = 255 is NaN).
+__device__ __forceinline__ float scale_value(float s) { return s; }
+__device__ __forceinline__ float scale_value(uint8_t e)
+{
+    const float v = __builtin_bit_cast(float, (uint32_t)e << 23);
+    return e == 0 ? __builtin_bit_cast(float, 0x00400000u) : (e == 255 ? __builtin_nanf("") : v);
+}
+
 // sum over the 16 columns of one lane chunk of e4m3(w) * x
 __device__ __forceinline__ float fp8_chunk_dot(const u32x4 wv, const f32x4 *__restrict__ xl,
                                                int NU, int u)
@@ -109,9 +118,9 @@ __device__ __forceinline__ float fp8_chunk_dot(const u32x4 wv, const f32x4 *__re
     return p0 + p1;
 }
 
-template <int S, int LPR, int R, int PF, int WPB>
+template <typename ST, int S, int LPR, int R, int PF, int WPB>
 __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
-    const uint8_t *__restrict__ w, const float *__restrict__ sc, const float *__restrict__ x,
+    const uint8_t *__restrict__ w, const ST *__restrict__ sc, const float *__restrict__ x,
     float *__restrict__ y, int I, int O, int nbi, int ntiles)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
     const int nit = (NU + LPR - 1) / LPR;
     const int nit_pad = (nit + PF - 1) / PF * PF;
-    const float *scrow = sc + (size_t)(min(row0, O - 1) / 128) * nbi;
+    const ST *scrow = sc + (size_t)(min(row0, O - 1) / 128) * nbi;
 
     const uint8_t *wr[R];
 #pragma unroll
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
 #pragma unroll
         for (int r = 0; r < R; r++)
             wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
-        sb[j] = ld_stream(&scrow[u >> 3]);
+        sb[j] = scale_value(ld_stream(&scrow[u >> 3]));
     };
 #pragma unroll
     for (int j = 0; j < PF0; j++) fetch(j, j);
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
 #pragma unroll
             for (int r = 0; r < R; r++)
                 wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (uint32_t)un * 16u));
-            sb[j] = ld_stream(&scrow[un >> 3]);
+            sb[j] = scale_value(ld_stream(&scrow[un >> 3]));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -223,8 +232,9 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
 // General kernel: any I >= 1, any alignment, S <= QGEMV_MAX_S.  One wave per
 // row; each weight decoded to f32 and multiplied by its block scale (one
 // rounding), then multiplied into x in f32.
+template <typename ST>
 __global__ __launch_bounds__(256) void fp8_gemv_general(
-    const uint8_t *__restrict__ w, const float *__restrict__ sc, const float *__restrict__ x,
+    const uint8_t *__restrict__ w, const ST *__restrict__ sc, const float *__restrict__ x,
     float *__restrict__ y, int S, int I, int O)
 {
     const int lane = threadIdx.x & 63;
@@ -232,14 +242,14 @@ __global__ __launch_bounds__(256) void fp8_gemv_general(
     if (row >= O) return;
     const int nbi = (I + 127) / 128;
     const uint8_t *wr = w + (size_t)row * I;
-    const float *scr = sc + (size_t)(row / 128) * nbi;
+    const ST *scr = sc + (size_t)(row / 128) * nbi;
     float acc[QGEMV_MAX_S];
 #pragma unroll
     for (int t = 0; t < QGEMV_MAX_S; t++) acc[t] = 0.0f;
     for (int i = lane; i < I; i += WAVE) {
         float v[4];
         e4m3x4((uint32_t)wr[i], v);
-        const float wv = v[0] * scr[i / 128];
+        const float wv = v[0] * scale_value(scr[i / 128]);
 #pragma unroll
         for (int t = 0; t < QGEMV_MAX_S; t++)
             if (t < S) acc[t] = __builtin_fmaf(wv, x[(size_t)t * I + i], acc[t]);
@@ -254,8 +264,9 @@ __global__ __launch_bounds__(256) void fp8_gemv_general(
 }
 
 // Decode-only: W[o][i] = e4m3(w[o][i]) * scale[o/128][i/128] as f32.
+template <typename ST>
 __global__ __launch_bounds__(256) void fp8_dequant(const uint8_t *__restrict__ w,
-                                                   const float *__restrict__ sc,
+                                                   const ST *__restrict__ sc,
                                                    float *__restrict__ W, int I, int O)
 {
     const int nbi = (I + 127) / 128;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(256) void fp8_dequant(const uint8_t *__restrict__ w
         const int i = (int)(idx - o * I);
         float v[4];
         e4m3x4((uint32_t)w[idx], v);
-        W[idx] = v[0] * sc[(o / 128) * nbi + i / 128];
+        W[idx] = v[0] * scale_value(sc[(o / 128) * nbi + i / 128]);
     }
 }
 
@@ -278,15 +289,15 @@ size_t fp8_lds_bytes(int S, int I)
     return ((size_t)S * 4 * seg_stride(I / 16) + 1) * sizeof(f32x4);
 }
 
-template <int S, int LPR, int R, int PF, int WPB>
-hipError_t launch_t(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
+template <typename ST, int S, int LPR, int R, int PF, int WPB>
+hipError_t launch_t(const uint8_t *w, const ST *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
     const int blocks = (ntiles + WPB - 1) / WPB;
     const size_t lds = fp8_lds_bytes(S, I);
-    auto kern = fp8_gemv_stream<S, LPR, R, PF, WPB>;
+    auto kern = fp8_gemv_stream<ST, S, LPR, R, PF, WPB>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, sc, x, y, I, O,
@@ -294,8 +305,8 @@ hipError_t launch_t(const uint8_t *w, const float *sc, const float *x, float *y,
     return hipGetLastError();
 }
 
-template <int S, int R>
-hipError_t launch_r(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
+template <typename ST, int S, int R>
+hipError_t launch_r(const uint8_t *w, const ST *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
 {
     constexpr int WPB = S == 1 ? QG_FP8_WPB : QG_FP8_WPB_MULTI;
@@ -303,28 +314,28 @@ hipError_t launch_r(const uint8_t *w, const float *sc, const float *x, float *y,
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_FP8_PF : 2;
     switch (pick_lpr(I / 16)) {
-    case 64: return launch_t<S, 64, R, PF, WPB>(w, sc, x, y, I, O, st);
-    case 32: return launch_t<S, 32, R, PF, WPB>(w, sc, x, y, I, O, st);
-    case 16: return launch_t<S, 16, R, PF, WPB>(w, sc, x, y, I, O, st);
-    case 8: return launch_t<S, 8, R, PF, WPB>(w, sc, x, y, I, O, st);
-    default: return launch_t<S, 4, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 64: return launch_t<ST, S, 64, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 32: return launch_t<ST, S, 32, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 16: return launch_t<ST, S, 16, R, PF, WPB>(w, sc, x, y, I, O, st);
+    case 8: return launch_t<ST, S, 8, R, PF, WPB>(w, sc, x, y, I, O, st);
+    default: return launch_t<ST, S, 4, R, PF, WPB>(w, sc, x, y, I, O, st);
     }
 }
 
-template <int S>
-hipError_t launch_s(const uint8_t *w, const float *sc, const float *x, float *y, int I, int O,
+template <typename ST, int S>
+hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
 {
     if constexpr (S == 1) {
-        return launch_r<S, QG_FP8_R>(w, sc, x, y, I, O, st);
+        return launch_r<ST, S, QG_FP8_R>(w, sc, x, y, I, O, st);
     } else {
         // several vectors: R keeps every workgroup resident at once (the rows
         // of a lane group must share a 128-row band, so R divides 128)
         static const int cand[] = {1, 2};
         switch (pick_rows_per_group(O, pick_lpr(I / 16), QG_FP8_WPB_MULTI, fp8_lds_bytes(S, I),
                                     cand, 2)) {
-        case 1: return launch_r<S, 1>(w, sc, x, y, I, O, st);
-        default: return launch_r<S, 2>(w, sc, x, y, I, O, st);
+        case 1: return launch_r<ST, S, 1>(w, sc, x, y, I, O, st);
+        default: return launch_r<ST, S, 2>(w, sc, x, y, I, O, st);
         }
     }
 }
@@ -338,10 +349,9 @@ int fp8_stream_vectors(const void *w, const float *x, int S, int I)
     return n;
 }
 
-}  // namespace
-
-hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const float *x, float *y,
-                               int S, int I, int O, hipStream_t st)
+template <typename ST>
+hipError_t launch_gemv(const void *w, const ST *sc, const float *x, float *y, int S, int I,
+                       int O, hipStream_t st)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     // more vectors than one launch takes (S > 4, or their activations do not
@@ -354,30 +364,56 @@ hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const floa
             float *ys = y + (size_t)s0 * O;
             hipError_t e;
             switch (n) {
-            case 1: e = launch_s<1>(wb, scale_inv, xs, ys, I, O, st); break;
-            case 2: e = launch_s<2>(wb, scale_inv, xs, ys, I, O, st); break;
-            case 3: e = launch_s<3>(wb, scale_inv, xs, ys, I, O, st); break;
-            default: e = launch_s<4>(wb, scale_inv, xs, ys, I, O, st); break;
+            case 1: e = launch_s<ST, 1>(wb, sc, xs, ys, I, O, st); break;
+            case 2: e = launch_s<ST, 2>(wb, sc, xs, ys, I, O, st); break;
+            case 3: e = launch_s<ST, 3>(wb, sc, xs, ys, I, O, st); break;
+            default: e = launch_s<ST, 4>(wb, sc, xs, ys, I, O, st); break;
             }
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
     const int wpb = 4;
-    hipLaunchKernelGGL(fp8_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
-                       scale_inv, x, y, S, I, O);
+    hipLaunchKernelGGL(fp8_gemv_general<ST>, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st,
+                       wb, sc, x, y, S, I, O);
     return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_dequant(const void *w, const ST *sc, float *W, int I, int O, hipStream_t st)
+{
+    const size_t n = (size_t)O * I;
+    const size_t want = (n + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(fp8_dequant<ST>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(w), sc, W, I, O);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const float *x, float *y,
+                               int S, int I, int O, hipStream_t st)
+{
+    return launch_gemv(w, scale_inv, x, y, S, I, O, st);
+}
+
+hipError_t launch_fp8ue8m0_gemv(const void *w, const uint8_t *scale_e8m0, const float *x,
+                                float *y, int S, int I, int O, hipStream_t st)
+{
+    return launch_gemv(w, scale_e8m0, x, y, S, I, O, st);
 }
 
 hipError_t launch_fp8b128_dequant(const void *w, const float *scale_inv, float *W, int I, int O,
                                   hipStream_t st)
 {
-    const size_t n = (size_t)O * I;
-    const size_t want = (n + 255) / 256;
-    const int blocks = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(fp8_dequant, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const uint8_t *>(w), scale_inv, W, I, O);
-    return hipGetLastError();
+    return launch_dequant(w, scale_inv, W, I, O, st);
+}
+
+hipError_t launch_fp8ue8m0_dequant(const void *w, const uint8_t *scale_e8m0, float *W, int I,
+                                   int O, hipStream_t st)
+{
+    return launch_dequant(w, scale_e8m0, W, I, O, st);
 }
 
 }  // namespace qg

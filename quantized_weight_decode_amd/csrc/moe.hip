@@ -44,7 +44,7 @@
 #define QG_MOE_WGS 256
 #endif
 #ifndef QG_MOE_PF
-#define QG_MOE_PF 2
+#define QG_MOE_PF 3
 #endif
 
 namespace qg {

@@ -54,6 +54,11 @@ hipError_t launch_fp8b128_gemv(const void *w, const float *scale_inv, const floa
                                int S, int I, int O, hipStream_t st);
 hipError_t launch_fp8b128_dequant(const void *w, const float *scale_inv, float *W, int I, int O,
                                   hipStream_t st);
+// fp8-e4m3 with UE8M0 (power-of-two byte) 128x128 block scales
+hipError_t launch_fp8ue8m0_gemv(const void *w, const uint8_t *scale_e8m0, const float *x,
+                                float *y, int S, int I, int O, hipStream_t st);
+hipError_t launch_fp8ue8m0_dequant(const void *w, const uint8_t *scale_e8m0, float *W, int I,
+                                   int O, hipStream_t st);
 
 // MQ4-v2 and the FWHT-256 rotation
 hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int I, int O,

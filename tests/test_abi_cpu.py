@@ -74,3 +74,11 @@ def test_fp8_refusals(q):
     assert f(0, BAD, BAD, BAD, 1, 64, 8, 0) == 1
     assert f(BAD, BAD, BAD, BAD, 1, 64, 0, 0) == 2
     assert f(BAD, BAD + 1, BAD, BAD, 1, 64, 8, 0) == 4
+
+
+def test_fp8_ue8m0_refusals(q):
+    f = q.qgemv_fp8b128_ue8m0
+    assert f(BAD, 0, BAD, BAD, 1, 64, 8, 0) == 1
+    assert f(BAD, BAD, BAD, BAD, 0, 64, 8, 0) == 2
+    assert f(BAD, BAD + 1, BAD + 2, BAD, 1, 64, 8, 0) == 4                 # x misaligned
+    assert q.qgemv_dequant_fp8b128_ue8m0(BAD, BAD, BAD + 2, 64, 8, 0) == 4

@@ -100,6 +100,24 @@ def gen_fp8b128(O: int, I: int, S: int = 1, seed: int = 0,
             "w": w, "scale_inv": scale, "x": x}
 
 
+def gen_fp8ue8m0(O: int, I: int, S: int = 1, seed: int = 0,
+                 e_lo: int = 114, e_hi: int = 120) -> dict:
+    """fp8-e4m3 GEMV inputs with UE8M0 (power-of-two) 128x128 block scales.
+
+    Draw order: weight codes as gen_fp8b128, u8[O][I]; block scale exponent
+    bytes uniform over [e_lo, e_hi] (2^-13 .. 2^-7, the powers of two inside
+    the f32-scale range 1e-4 .. 1e-2) as u8[ceil(O/128)][ceil(I/128)];
+    x ~ N(0,1) f32[S][I].
+    """
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E4M3_NON_NAN_CODES.size, (O, I), dtype=np.uint8)
+    w = E4M3_NON_NAN_CODES[idx]
+    nbo, nbi = fp8_nblocks(O, I)
+    se = rng.integers(e_lo, e_hi + 1, (nbo, nbi)).astype(np.uint8)
+    x = rng.standard_normal((S, I), dtype=np.float32)
+    return {"fmt": "fp8ue8m0", "O": O, "I": I, "S": S, "w": w, "scale_e8m0": se, "x": x}
+
+
 def gen_fwht_signs(I: int, seed: int = 42) -> np.ndarray:
     """Per-element +-1 rotation signs, int8[I], from default_rng(seed)."""
     rng = np.random.default_rng(seed)
