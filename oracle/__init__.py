@@ -70,12 +70,21 @@ class Oracle:
         L.qref_mq4v2_dequant.argtypes = [_u8p, I, I, _f32p]
         L.qref_mq4v2_gemv.argtypes = [_u8p, _f32p, _f32p, I, I, I, _rowsp, I]
         L.qref_fwht256.argtypes = [_f32p, _i8p, _f32p, I, I]
+        L.qref_mq4v1_dequant.argtypes = [_u8p, I, I, _f32p]
+        L.qref_mq4c_dequant.argtypes = [_u8p, I, I, _f32p]
+        L.qref_mq4v1_gemv.argtypes = [_u8p, _f32p, _f32p, I, I, I, _rowsp, I]
+        L.qref_mq4c_gemv.argtypes = [_u8p, _f32p, _f32p, I, I, I, _rowsp, I]
+        L.qref_mq4v2_encode.argtypes = [_f32p, I, I, _u8p]
+        L.qref_f32_to_f16.restype = C.c_uint16
+        L.qref_f32_to_f16.argtypes = [C.c_float]
         L.qref_moe_i4g.argtypes = [_u8p, _f32p, C.c_longlong, C.c_longlong, I, _i32p,
                                    _f32p, I, I, _f32p, _f32p, I, I, I, _rowsp, I]
         for f in (L.qref_i4g_dequant, L.qref_i4g_gemv, L.qref_fp8b128_dequant,
                   L.qref_fp8b128_gemv, L.qref_fp8ue8m0_dequant, L.qref_fp8ue8m0_gemv,
                   L.qref_mq4v2_dequant, L.qref_mq4v2_gemv,
-                  L.qref_fwht256, L.qref_moe_i4g, L.qref_set_threads):
+                  L.qref_fwht256, L.qref_moe_i4g, L.qref_set_threads,
+                  L.qref_mq4v1_dequant, L.qref_mq4c_dequant, L.qref_mq4v1_gemv,
+                  L.qref_mq4c_gemv, L.qref_mq4v2_encode):
             f.restype = None
 
     # -- scalars ---------------------------------------------------------
@@ -165,6 +174,39 @@ class Oracle:
         y = np.empty((x.shape[0], n if rows is not None else O), np.float32)
         self.lib.qref_mq4v2_gemv(self._c(w, np.uint8), x, y, x.shape[0], I, O, rp, n)
         return y
+
+    # -- MQ4 v1 (f32 header per 256) and MQ4C (fp16 pair per 256 + pad) ---
+    def _mq4g_dequant(self, fn, w, O, I):
+        W = np.empty((O, I), np.float32)
+        fn(self._c(w, np.uint8), O, I, W)
+        return W
+
+    def _mq4g_gemv(self, fn, w, x, O, I, rows):
+        x = self._c(x, np.float32).reshape(-1, I)
+        keep, rp, n = self._rows(rows)
+        y = np.empty((x.shape[0], n if rows is not None else O), np.float32)
+        fn(self._c(w, np.uint8), x, y, x.shape[0], I, O, rp, n)
+        return y
+
+    def mq4v1_dequant(self, w, O, I):
+        return self._mq4g_dequant(self.lib.qref_mq4v1_dequant, w, O, I)
+
+    def mq4c_dequant(self, w, O, I):
+        return self._mq4g_dequant(self.lib.qref_mq4c_dequant, w, O, I)
+
+    def mq4v1_gemv(self, w, x, O, I, rows=None):
+        return self._mq4g_gemv(self.lib.qref_mq4v1_gemv, w, x, O, I, rows)
+
+    def mq4c_gemv(self, w, x, O, I, rows=None):
+        return self._mq4g_gemv(self.lib.qref_mq4c_gemv, w, x, O, I, rows)
+
+    def mq4v2_encode(self, W, O, I):
+        out = np.empty(O * (I // 256) * 136, np.uint8)
+        self.lib.qref_mq4v2_encode(self._c(W, np.float32), O, I, out)
+        return out.reshape(O, (I // 256) * 136)
+
+    def f32_to_f16(self, f: float) -> int:
+        return self.lib.qref_f32_to_f16(f)
 
     def fwht256(self, x, signs, I):
         x = self._c(x, np.float32).reshape(-1, I)

@@ -315,6 +315,175 @@ void qref_mq4v2_gemv(const uint8_t *w, const float *x, float *y, int S, int I,
     }
 }
 
+/*
+ * MQ4 v1 (qt=13) and the padded-compat form MQ4C (qt=45), hipfire "MQ4 V2",
+ * sections 1b and 1e: the same 136-byte groups with the same 128 payload
+ * bytes at [8..136) (weight j = nibble j, low nibble first), one header for
+ * all 256 weights.  v1: f32 scale at byte 0, f32 zero at byte 4 ("v1 reads
+ * two f32 fields").  MQ4C: one packed pair at byte 0, fp16 scale in the low
+ * half and fp16 zero in the high half, as v2 packs its pairs; bytes 4..7 are
+ * the required zero pad and are not read.  w = q*scale + zero.
+ */
+static uint32_t le32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
+           ((uint32_t)p[3] << 24);
+}
+
+static double f32_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double mq4_group_weight(const uint8_t *w, int I, int o, int i, int fmt)
+{
+    size_t G = (size_t)I / 256;
+    const uint8_t *p = w + ((size_t)o * G + (size_t)i / 256) * 136;
+    int j = i % 256;
+    double sc, zp;
+    if (fmt == 1) {           /* v1 */
+#if QREF_MUTATE == 13 /* planted: v1 fields swapped */
+        sc = f32_bits(le32(p + 4));
+        zp = f32_bits(le32(p));
+#else
+        sc = f32_bits(le32(p));
+        zp = f32_bits(le32(p + 4));
+#endif
+    } else {                  /* MQ4C */
+        uint32_t hd = le32(p);
+        sc = qref_f16((uint16_t)(hd & 0xFFFF));
+        zp = qref_f16((uint16_t)(hd >> 16));
+    }
+    uint8_t b = p[8 + j / 2];
+    int q = (j & 1) ? (b >> 4) : (b & 0xF);
+    return (double)q * sc + zp;
+}
+
+static void mq4_group_dequant(const uint8_t *w, int O, int I, float *W, int fmt)
+{
+    for (int o = 0; o < O; o++)
+        for (int i = 0; i < I; i++)
+            W[(size_t)o * I + i] = (float)mq4_group_weight(w, I, o, i, fmt);
+}
+
+static void mq4_group_gemv(const uint8_t *w, const float *x, float *y, int S, int I, int O,
+                           const int *rows, int nrows, int fmt)
+{
+    int n = rows ? nrows : O;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int r = 0; r < n; r++) {
+        int o = rows ? rows[r] : r;
+        for (int t = 0; t < S; t++) {
+            double acc = 0.0;
+            for (int i = 0; i < I; i++)
+                acc += mq4_group_weight(w, I, o, i, fmt) * (double)x[(size_t)t * I + i];
+            y[(size_t)t * n + r] = (float)acc;
+        }
+    }
+}
+
+void qref_mq4v1_dequant(const uint8_t *w, int O, int I, float *W) { mq4_group_dequant(w, O, I, W, 1); }
+void qref_mq4c_dequant(const uint8_t *w, int O, int I, float *W) { mq4_group_dequant(w, O, I, W, 2); }
+void qref_mq4v1_gemv(const uint8_t *w, const float *x, float *y, int S, int I, int O,
+                     const int *rows, int nrows)
+{
+    mq4_group_gemv(w, x, y, S, I, O, rows, nrows, 1);
+}
+void qref_mq4c_gemv(const uint8_t *w, const float *x, float *y, int S, int I, int O,
+                    const int *rows, int nrows)
+{
+    mq4_group_gemv(w, x, y, S, I, O, rows, nrows, 2);
+}
+
+/*
+ * f32 -> IEEE binary16 bits, round to nearest even (overflow to infinity,
+ * subnormals kept, NaN stays NaN).  Every f32 is exact in double, so the
+ * scaled value below is exact and one nearbyint() is the whole rounding.
+ */
+uint16_t qref_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000);
+    double v = fabs((double)f);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7E00);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7C00);
+    if (v == 0.0)
+        return sign;
+    int k;
+    (void)frexp(v, &k);               /* v = m * 2^k, m in [0.5, 1) */
+    int E = k - 1;                     /* v in [2^E, 2^(E+1)) */
+    if (E < -14) {                     /* subnormal range: units of 2^-24 */
+        double q = nearbyint(ldexp(v, 24));
+        return (uint16_t)(sign | (uint16_t)q);   /* q = 1024 is the least normal */
+    }
+    double q = nearbyint(ldexp(v, 10 - E));       /* in [1024, 2048] */
+    if (q == 2048.0) {
+        q = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | ((E + 15) << 10) | ((int)q - 1024));
+}
+
+/*
+ * MQ4-v2 encoder, hipfire "MQ4 V2", section 3, for weights already in the
+ * rotated space (W f32 [O][I], I % 256 == 0) -> 136-byte groups.  Per group
+ * and half h (weights 128h .. 128h+127): lo and hi are the half's min and
+ * max; step = (hi - lo) / 15 in f32; the stored scale and zero are the fp16
+ * roundings of step and lo; each code is chosen against the stored (f16
+ * round-tripped) values, q = clamp(rint((w - z) / s), 0, 15) in f32, so the
+ * decoder reproduces the encoder's reconstruction.  A half whose stored
+ * scale is 0 -- the constant half of the page, and (our reading) a step too
+ * small for fp16 -- gets q = 0: it decodes to the stored zero.  Weights must
+ * be finite.
+ */
+void qref_mq4v2_encode(const float *W, int O, int I, uint8_t *out)
+{
+    int G = I / 256;
+    for (int o = 0; o < O; o++)
+        for (int g = 0; g < G; g++) {
+            const float *wg = W + (size_t)o * I + (size_t)g * 256;
+            uint8_t *p = out + ((size_t)o * G + g) * 136;
+            memset(p, 0, 136);
+            for (int h = 0; h < 2; h++) {
+                const float *wh = wg + 128 * h;
+                float lo = wh[0], hi = wh[0];
+                for (int i = 1; i < 128; i++) {
+                    if (wh[i] < lo) lo = wh[i];
+                    if (wh[i] > hi) hi = wh[i];
+                }
+                volatile float step = (hi - lo) / 15.0f;
+                uint16_t sc16 = qref_f32_to_f16(step);
+                uint16_t zp16 = qref_f32_to_f16(lo);
+#if QREF_MUTATE == 12 /* planted: codes chosen against the unrounded step */
+                float st = step, z = (float)qref_f16(zp16);
+#else
+                float st = (float)qref_f16(sc16), z = (float)qref_f16(zp16);
+#endif
+                uint32_t hd = (uint32_t)sc16 | ((uint32_t)zp16 << 16);
+                for (int b = 0; b < 4; b++)
+                    p[4 * h + b] = (uint8_t)(hd >> (8 * b));
+                for (int i = 0; i < 128; i++) {
+                    int q = 0;
+                    if (st != 0.0f) {
+                        volatile float d = wh[i] - z;
+                        volatile float r = d / st;
+                        float qf = rintf(r);
+                        q = qf < 0.0f ? 0 : (qf > 15.0f ? 15 : (int)qf);
+                    }
+                    int j = 128 * h + i;
+                    p[8 + j / 2] |= (uint8_t)(q << (4 * (j & 1)));
+                }
+            }
+        }
+}
+
 /* ------------------------------------------------------------------------ */
 /* FWHT-256 pre-rotation                                                     */
 /* ------------------------------------------------------------------------ */

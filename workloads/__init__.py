@@ -17,6 +17,9 @@ Formats (byte layouts as the pages define them):
 * MQ4-v2 (hipfire "MQ4 V2" page, sections 2 and 4): 136 bytes per 256
   weights; bytes 0..3 hold the fp16 scale and fp16 zero of weights 0..127,
   bytes 4..7 those of weights 128..255, bytes 8..135 the 128 payload bytes.
+  MQ4 v1 (sections 1b, 1e) keeps the geometry with an f32 scale at byte 0 and
+  an f32 zero at byte 4 for all 256 weights; MQ4C pad one fp16 pair at byte 0
+  and a zero pad at bytes 4..7.
 
 Random numbers are drawn with ``numpy.random.default_rng(seed)`` in the order
 each function lists; the recipes follow the workload descriptions (uniform
@@ -30,7 +33,8 @@ import numpy as np
 
 __all__ = [
     "i4g_rowbytes", "i4g_ngroups", "fp8_nblocks",
-    "random_bytes", "gen_i4g", "gen_fp8b128", "gen_mq4v2", "gen_fwht_signs",
+    "random_bytes", "gen_i4g", "gen_fp8b128", "gen_fp8ue8m0", "gen_mq4v2", "gen_mq4v1",
+    "gen_mq4c", "gen_rotated_weights", "gen_fwht_signs",
     "gen_moe", "gen_moe_routing", "E4M3_NON_NAN_CODES",
     "WORKLOADS",
 ]
@@ -159,6 +163,64 @@ def gen_mq4v2(O: int, I: int, S: int = 1, seed: int = 0, sign_seed: int = 42,
     return {"fmt": "mq4v2", "O": O, "I": I, "S": S, "w": w,
             "sc16": sc16, "zp16": zp16, "x": x,
             "signs": gen_fwht_signs(I, sign_seed)}
+
+
+def gen_mq4v1(O: int, I: int, S: int = 1, seed: int = 0, sign_seed: int = 42,
+              sc_lo: float = 1e-3, sc_hi: float = 1e-2,
+              zp_lo: float = -0.08, zp_hi: float = 0.0) -> dict:
+    """MQ4 v1 (qt=13) GEMV inputs: one f32 scale and f32 zero per 256 weights.
+
+    Draw order: f32 scales U[sc_lo, sc_hi] per (row, group), f32 zeros
+    U[zp_lo, zp_hi] per (row, group), payload bytes u8[O][I/256][128], x ~
+    N(0,1) f32[S][I].  Bytes 0..3 of a group hold the scale, 4..7 the zero
+    (little-endian f32), 8..135 the payload.
+    """
+    if I % 256:
+        raise ValueError("MQ4 needs I % 256 == 0")
+    G = I // 256
+    rng = np.random.default_rng(seed)
+    sc = rng.uniform(sc_lo, sc_hi, (O, G)).astype(np.float32)
+    zp = rng.uniform(zp_lo, zp_hi, (O, G)).astype(np.float32)
+    payload = random_bytes(rng, (O, G, 128))
+    x = rng.standard_normal((S, I), dtype=np.float32)
+    w = np.empty((O, G, 136), dtype=np.uint8)
+    w[:, :, 0:4] = np.ascontiguousarray(sc).astype("<f4").view(np.uint8).reshape(O, G, 4)
+    w[:, :, 4:8] = np.ascontiguousarray(zp).astype("<f4").view(np.uint8).reshape(O, G, 4)
+    w[:, :, 8:136] = payload
+    return {"fmt": "mq4v1", "O": O, "I": I, "S": S, "w": w, "sc": sc, "zp": zp, "x": x,
+            "signs": gen_fwht_signs(I, sign_seed)}
+
+
+def gen_mq4c(O: int, I: int, S: int = 1, seed: int = 0, sign_seed: int = 42,
+             sc_lo: float = 1e-3, sc_hi: float = 1e-2,
+             zp_lo: float = -0.08, zp_hi: float = 0.0) -> dict:
+    """MQ4C pad (qt=45) GEMV inputs: one fp16 scale/zero pair per 256 weights.
+
+    Draw order: fp16 scales and zeros as gen_mq4v2 but per (row, group),
+    payload bytes, x.  Bytes 0..1 hold the fp16 scale, 2..3 the fp16 zero,
+    4..7 the zero pad, 8..135 the payload.
+    """
+    if I % 256:
+        raise ValueError("MQ4 needs I % 256 == 0")
+    G = I // 256
+    rng = np.random.default_rng(seed)
+    sc16 = rng.uniform(sc_lo, sc_hi, (O, G)).astype(np.float16)
+    zp16 = rng.uniform(zp_lo, zp_hi, (O, G)).astype(np.float16)
+    payload = random_bytes(rng, (O, G, 128))
+    x = rng.standard_normal((S, I), dtype=np.float32)
+    w = np.zeros((O, G, 136), dtype=np.uint8)
+    w[:, :, 0:2] = np.ascontiguousarray(sc16).astype("<f2").view(np.uint8).reshape(O, G, 2)
+    w[:, :, 2:4] = np.ascontiguousarray(zp16).astype("<f2").view(np.uint8).reshape(O, G, 2)
+    w[:, :, 8:136] = payload
+    return {"fmt": "mq4c", "O": O, "I": I, "S": S, "w": w, "sc16": sc16, "zp16": zp16,
+            "x": x, "signs": gen_fwht_signs(I, sign_seed)}
+
+
+def gen_rotated_weights(O: int, I: int, seed: int = 0, sigma: float = 0.02) -> np.ndarray:
+    """Dense f32 weights [O][I] ~ N(0, sigma^2), standing in for weights already
+    in the rotated space (the input of the MQ4-v2 encoder)."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((O, I)) * sigma).astype(np.float32)
 
 
 def gen_moe_routing(E: int, T: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
