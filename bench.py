@@ -10,6 +10,9 @@ A step is one pass of the hot path over one batch of synthetic input:
       the same step on 2 or 4 activation vectors per call (multi-token decode)
   fp8b128_O7168_I16384:
       one qgemv_fp8b128 call
+  mq4v1_O8192_I8192, mq4c_O8192_I8192:
+      qgemv_fwht256 then qgemv_mq4v1 / qgemv_mq4c (MQ4 v1 and the MQ4C pad
+      form on the same shape)
   fp8ue8m0_O7168_I16384:
       one qgemv_fp8b128_ue8m0 call (the same weights with power-of-two
       UE8M0 block scale bytes)
@@ -202,10 +205,18 @@ class FP8E8(Case):
 class MQ4(Case):
     kernel = "mq4v2_gemv_stream"
 
-    def __init__(self, O, I, torch, q, o, S=1):
+    FORMATS = {
+        "v2": ("mq4v2", "MQ4-v2 136 B / 256 weights (fp16 scale+zero per 128)"),
+        "v1": ("mq4v1", "MQ4 v1 136 B / 256 weights (f32 scale+zero per 256)"),
+        "c": ("mq4c", "MQ4C pad 136 B / 256 weights (fp16 scale+zero per 256)"),
+    }
+
+    def __init__(self, O, I, torch, q, o, S=1, fmt="v2"):
         import workloads as W
-        self.name = f"mq4v2_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = "MQ4-v2 136 B / 256 weights, FWHT-256 rotated activations" + (f", {S} vectors per call" if S > 1 else "")
+        self.fmt = fmt
+        tag, desc = self.FORMATS[fmt]
+        self.name = f"{tag}_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = desc + ", FWHT-256 rotated activations" + (f", {S} vectors per call" if S > 1 else "")
         self.O, self.I, self.S = O, I, S
         self.weight_bytes = O * (I // 256) * 136
         # up to two vectors: one fused launch (weights, x, signs in; y out),
@@ -214,11 +225,11 @@ class MQ4(Case):
         # y out) -- every workgroup of the fused kernel rotates all S
         # vectors, which at S = 4 costs more than the extra launch
         self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4) + I
-        if S > 2:
+        if S > 2 or fmt != "v2":
             self.alg_bytes += S * I * 8
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
-        d = W.gen_mq4v2(O, I, S=S, seed=0)
+        d = {"v2": W.gen_mq4v2, "v1": W.gen_mq4v1, "c": W.gen_mq4c}[fmt](O, I, S=S, seed=0)
         self.n = n_copies(self.weight_bytes)
         g = torch.Generator(device=dev)
         g.manual_seed(1)
@@ -241,22 +252,24 @@ class MQ4(Case):
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [w.data_ptr() for w in self.ws]
         self.step(0)
-        ref = o.mq4v2_gemv(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
+        ref_fn = {"v2": o.mq4v2_gemv, "v1": o.mq4v1_gemv, "c": o.mq4c_gemv}[fmt]
+        ref = ref_fn(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
         self.rel = _rel(self.y.cpu().numpy(), ref)
         _check(self.rel, self.name)
-        self.cpu = lambda: o.mq4v2_gemv(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
+        self.cpu = lambda: ref_fn(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
 
     def step(self, i):
         q = self.q
-        if self.S <= 2:
+        if self.S <= 2 and self.fmt == "v2":
             st = q.qgemv_mq4v2_rot(self.ptrs[i % self.n], self.x.data_ptr(),
                                    self.signs.data_ptr(), self.y.data_ptr(), self.S, self.I,
                                    self.O, self.sp)
         else:
             st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(),
                                  self.S, self.I, self.sp)
-            st = st or q.qgemv_mq4v2(self.ptrs[i % self.n], self.xr.data_ptr(),
-                                     self.y.data_ptr(), self.S, self.I, self.O, self.sp)
+            gemv = {"v2": q.qgemv_mq4v2, "v1": q.qgemv_mq4v1, "c": q.qgemv_mq4c}[self.fmt]
+            st = st or gemv(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), self.S,
+                            self.I, self.O, self.sp)
         if st:
             raise SystemExit(f"mq4v2 step: {q.strerror(st)}")
 
@@ -331,6 +344,8 @@ def build_case(name, torch, q, o):
         "mq4v2_O8192_I8192_S2": lambda: MQ4(8192, 8192, torch, q, o, S=2),
         "mq4v2_O8192_I8192_S4": lambda: MQ4(8192, 8192, torch, q, o, S=4),
         "fp8ue8m0_O7168_I16384": lambda: FP8E8(7168, 16384, torch, q, o),
+        "mq4v1_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o, fmt="v1"),
+        "mq4c_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o, fmt="c"),
     }
     return table[name]()
 
@@ -339,7 +354,8 @@ CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_
               "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64",
               "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4",
               "fp8b128_O7168_I16384_S2", "fp8b128_O7168_I16384_S4",
-              "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4", "fp8ue8m0_O7168_I16384"]
+              "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4", "fp8ue8m0_O7168_I16384",
+              "mq4v1_O8192_I8192", "mq4c_O8192_I8192"]
 
 
 KERNEL_SOURCES = {

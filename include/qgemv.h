@@ -105,6 +105,35 @@ int qgemv_mq4v2(const void *w, const float *x_rot, float *y, int S, int I,
                 int O, void *stream);
 
 /*
+ * MQ4 v1 (qt=13) and MQ4C pad (qt=45): hipfire "MQ4 V2", sections 1b and 1e.
+ * The same 136-byte groups and payload as qgemv_mq4v2 (128 nibble bytes at
+ * [8..136), weight j = nibble j, low nibble first; w = q * scale + zero),
+ * with one header for all 256 weights of a group:
+ *   v1    f32 scale at byte 0, f32 zero at byte 4
+ *   MQ4C  fp16 scale (low half) and fp16 zero (high half) of the dword at
+ *         byte 0; bytes 4..7 are the zero pad and are not read
+ * x_rot, y, S, I, O and refusals as qgemv_mq4v2.
+ */
+int qgemv_mq4v1(const void *w, const float *x_rot, float *y, int S, int I, int O,
+                void *stream);
+int qgemv_mq4c(const void *w, const float *x_rot, float *y, int S, int I, int O,
+               void *stream);
+
+/*
+ * MQ4-v2 encoder: hipfire "MQ4 V2", section 3.  W f32 [O][I] holds weights
+ * already in the rotated space (I % 256 == 0, 16-byte aligned); w_out
+ * receives O * (I/256) * 136 bytes (8-byte aligned) in the qgemv_mq4v2
+ * layout.  Per 128-weight half: lo, hi = min, max; step = (hi - lo) / 15 in
+ * f32; the stored scale and zero are the fp16 (nearest even) roundings of
+ * step and lo; each code is q = clamp(rint((w - z) / s), 0, 15) against the
+ * stored, f16-rounded s and z (so decoding reproduces the encoder's own
+ * reconstruction).  A stored scale of 0 (a constant half, or a step below
+ * fp16's range) gives q = 0; an extreme of -0 counts as +0.  W must be
+ * finite.
+ */
+int qgemv_mq4v2_encode(const float *W, void *w_out, int I, int O, void *stream);
+
+/*
  * MQ4-v2 GEMV on unrotated activations: the FWHT-256 pre-rotation below
  * (hipfire "MQ4 V2", section 1) fused into the GEMV (sections 2 and 4),
  *     y = W . x_rot,  x_rot = (1/16) H256 (signs (.) x) per 256-column block,
@@ -177,6 +206,8 @@ int qgemv_dequant_fp8b128(const void *w, const float *scale_inv, float *W,
 int qgemv_dequant_fp8b128_ue8m0(const void *w, const uint8_t *scale_e8m0, float *W, int I,
                                 int O, void *stream);
 int qgemv_dequant_mq4v2(const void *w, float *W, int I, int O, void *stream);
+int qgemv_dequant_mq4v1(const void *w, float *W, int I, int O, void *stream);
+int qgemv_dequant_mq4c(const void *w, float *W, int I, int O, void *stream);
 
 #ifdef __cplusplus
 }

@@ -440,8 +440,9 @@ uint16_t qref_f32_to_f16(float f)
  * round-tripped) values, q = clamp(rint((w - z) / s), 0, 15) in f32, so the
  * decoder reproduces the encoder's reconstruction.  A half whose stored
  * scale is 0 -- the constant half of the page, and (our reading) a step too
- * small for fp16 -- gets q = 0: it decodes to the stored zero.  Weights must
- * be finite.
+ * small for fp16 -- gets q = 0: it decodes to the stored zero.  An extreme
+ * of -0 counts as +0 (the two compare equal; this fixes the bits of the
+ * stored values whichever zero comes first).  Weights must be finite.
  */
 void qref_mq4v2_encode(const float *W, int O, int I, uint8_t *out)
 {
@@ -458,6 +459,8 @@ void qref_mq4v2_encode(const float *W, int O, int I, uint8_t *out)
                     if (wh[i] < lo) lo = wh[i];
                     if (wh[i] > hi) hi = wh[i];
                 }
+                lo = lo + 0.0f;      /* a -0 extreme counts as +0 */
+                hi = hi + 0.0f;
                 volatile float step = (hi - lo) / 15.0f;
                 uint16_t sc16 = qref_f32_to_f16(step);
                 uint16_t zp16 = qref_f32_to_f16(lo);

@@ -34,6 +34,11 @@ _SIGS = {
                                       C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_mq4v1": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_mq4c": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
+                             C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_mq4v2_encode": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_mq4v2_rot": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_fwht256": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
@@ -52,6 +57,8 @@ _SIGS = {
                                               C.c_int, C.c_int, C.c_void_p]),
     "qgemv_dequant_mq4v2": (C.c_int, [C.c_void_p, C.c_void_p,
                                       C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_dequant_mq4v1": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_dequant_mq4c": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]),
 }
 
 ENTRY_POINTS = tuple(_SIGS)
@@ -121,6 +128,18 @@ def qgemv_mq4v2(w, x_rot, y, S, I, O, stream):
     return lib().qgemv_mq4v2(w, x_rot, y, S, I, O, stream)
 
 
+def qgemv_mq4v1(w, x_rot, y, S, I, O, stream):
+    return lib().qgemv_mq4v1(w, x_rot, y, S, I, O, stream)
+
+
+def qgemv_mq4c(w, x_rot, y, S, I, O, stream):
+    return lib().qgemv_mq4c(w, x_rot, y, S, I, O, stream)
+
+
+def qgemv_mq4v2_encode(W, w_out, I, O, stream):
+    return lib().qgemv_mq4v2_encode(W, w_out, I, O, stream)
+
+
 def qgemv_mq4v2_rot(w, x, signs, y, S, I, O, stream):
     return lib().qgemv_mq4v2_rot(w, x, signs, y, S, I, O, stream)
 
@@ -153,6 +172,14 @@ def qgemv_dequant_fp8b128_ue8m0(w, scale_e8m0, W, I, O, stream):
 
 def qgemv_dequant_mq4v2(w, W, I, O, stream):
     return lib().qgemv_dequant_mq4v2(w, W, I, O, stream)
+
+
+def qgemv_dequant_mq4v1(w, W, I, O, stream):
+    return lib().qgemv_dequant_mq4v1(w, W, I, O, stream)
+
+
+def qgemv_dequant_mq4c(w, W, I, O, stream):
+    return lib().qgemv_dequant_mq4c(w, W, I, O, stream)
 
 
 # -- torch-tensor layer ----------------------------------------------------
@@ -226,6 +253,37 @@ def mq4v2(w, x_rot, out=None):
     _call("qgemv_mq4v2", _dev(w, "w", torch.uint8), _dev(x_rot, "x_rot", torch.float32),
           _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
+
+
+def _mq4_any(fn, w, x_rot, out):
+    torch = _torch()
+    O, I = w.shape[0], x_rot.shape[-1]
+    S = _vecs(x_rot, I, "x_rot")
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x_rot.device)
+    _call(fn, _dev(w, "w", torch.uint8), _dev(x_rot, "x_rot", torch.float32),
+          _dev(y, "y", torch.float32), S, I, O, _stream())
+    return y
+
+
+def mq4v1(w, x_rot, out=None):
+    """MQ4 v1 (f32 scale and zero per 256 weights) GEMV on rotated x."""
+    return _mq4_any("qgemv_mq4v1", w, x_rot, out)
+
+
+def mq4c(w, x_rot, out=None):
+    """MQ4C pad (one fp16 scale/zero pair per 256 weights) GEMV on rotated x."""
+    return _mq4_any("qgemv_mq4c", w, x_rot, out)
+
+
+def mq4v2_encode(W, out=None):
+    """MQ4-v2 groups [O][I/256*136] u8 from rotated-space weights W f32 [O][I]."""
+    torch = _torch()
+    O, I = W.shape
+    w = out if out is not None else torch.empty((O, (I // 256) * 136), dtype=torch.uint8,
+                                                 device=W.device)
+    _call("qgemv_mq4v2_encode", _dev(W, "W", torch.float32), _dev(w, "w_out", torch.uint8),
+          I, O, _stream())
+    return w
 
 
 def mq4v2_rot(w, x, signs, out=None):
@@ -302,6 +360,22 @@ def dequant_fp8b128_ue8m0(w, scale_e8m0):
     _call("qgemv_dequant_fp8b128_ue8m0", _dev(w, "w", torch.uint8),
           _dev(scale_e8m0, "scale_e8m0", torch.uint8), _dev(W, "W"), I, O, _stream())
     return W
+
+
+def _dequant_mq4_any(fn, w, I):
+    torch = _torch()
+    O = w.shape[0]
+    W = torch.empty((O, I), dtype=torch.float32, device=w.device)
+    _call(fn, _dev(w, "w", torch.uint8), _dev(W, "W"), I, O, _stream())
+    return W
+
+
+def dequant_mq4v1(w, I):
+    return _dequant_mq4_any("qgemv_dequant_mq4v1", w, I)
+
+
+def dequant_mq4c(w, I):
+    return _dequant_mq4_any("qgemv_dequant_mq4c", w, I)
 
 
 def dequant_mq4v2(w, I):

@@ -178,6 +178,51 @@ int qgemv_mq4v2_rot(const void *w, const float *x, const int8_t *signs, float *y
     return launched(qg::launch_mq4v2_rot_gemv(w, x, signs, y, S, I, O, (hipStream_t)stream));
 }
 
+int qgemv_mq4v1(const void *w, const float *x_rot, float *y, int S, int I, int O, void *stream)
+{
+    if (!w || !x_rot || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(x_rot) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4v1_gemv(w, x_rot, y, S, I, O, (hipStream_t)stream));
+}
+
+int qgemv_mq4c(const void *w, const float *x_rot, float *y, int S, int I, int O, void *stream)
+{
+    if (!w || !x_rot || !y) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(S, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(x_rot) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4c_gemv(w, x_rot, y, S, I, O, (hipStream_t)stream));
+}
+
+int qgemv_dequant_mq4v1(const void *w, float *W, int I, int O, void *stream)
+{
+    if (!w || !W) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(W)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4v1_dequant(w, W, I, O, (hipStream_t)stream));
+}
+
+int qgemv_dequant_mq4c(const void *w, float *W, int I, int O, void *stream)
+{
+    if (!w || !W) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (mis4(W)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4c_dequant(w, W, I, O, (hipStream_t)stream));
+}
+
+int qgemv_mq4v2_encode(const float *W, void *w_out, int I, int O, void *stream)
+{
+    if (!W || !w_out) return QGEMV_E_NULL;
+    if (int e = check_gemv_dims(1, I, O)) return e;
+    if (I % 256) return QGEMV_E_K256;
+    if (((uintptr_t)W & 15) || ((uintptr_t)w_out & 7)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_mq4v2_encode(W, w_out, I, O, (hipStream_t)stream));
+}
+
 int qgemv_dequant_mq4v2(const void *w, float *W, int I, int O, void *stream)
 {
     if (!w || !W) return QGEMV_E_NULL;

@@ -73,9 +73,67 @@ __device__ __forceinline__ float mq4_chunk_plain(const u32x4 wv, float scl, floa
     return acc;
 }
 
+// The group header formats that share the 136-byte geometry and the payload
+// at bytes 8..135 (hipfire "MQ4 V2", sections 1b, 1e and 2):
+//   MQ4_V2  fp16 {scale, zero} pair at +0 for weights 0..127, at +4 for 128..255
+//   MQ4_V1  f32 scale at +0, f32 zero at +4, for all 256 weights (qt=13)
+//   MQ4_C   one fp16 {scale, zero} pair at +0 for all 256 weights, zero pad at
+//           +4 (MQ4C pad, qt=45)
+// A fp16 pair holds the scale in its low half and the zero in its high half.
+enum : int { MQ4_V2 = 0, MQ4_V1 = 1, MQ4_C = 2 };
+
+template <int HF>
+struct Mq4Hdr {
+    typedef uint32_t T;
+    // header of payload chunk p (16 bytes at +8 + 16p) of group gp
+    __device__ __forceinline__ static T load(const uint8_t *gp, int p)
+    {
+        return ld_stream(reinterpret_cast<const uint32_t *>(gp + (HF == MQ4_V2 && p >= 4 ? 4 : 0)));
+    }
+    __device__ __forceinline__ static void decode(T h, float &sc, float &zp)
+    {
+        sc = f16_to_f32(h & 0xFFFFu);
+        zp = f16_to_f32(h >> 16);
+    }
+};
+template <>
+struct Mq4Hdr<MQ4_V1> {
+    typedef u32x2 T;
+    __device__ __forceinline__ static T load(const uint8_t *gp, int)
+    {
+        return ld_stream(reinterpret_cast<const u32x2 *>(gp));
+    }
+    __device__ __forceinline__ static void decode(T h, float &sc, float &zp)
+    {
+        // through scalars: __builtin_bit_cast of a vector element (h.y) is
+        // compiled as a cast of element 0 by this compiler
+        const uint32_t a = h[0], b = h[1];
+        sc = __builtin_bit_cast(float, a);
+        zp = __builtin_bit_cast(float, b);
+    }
+};
+
+// The same header read byte by byte (any alignment), for weight j of the group.
+template <int HF>
+__device__ __forceinline__ void mq4_hdr_bytes(const uint8_t *gp, int j, float &sc, float &zp)
+{
+    auto le32 = [&](int off) {
+        return (uint32_t)gp[off] | ((uint32_t)gp[off + 1] << 8) | ((uint32_t)gp[off + 2] << 16) |
+               ((uint32_t)gp[off + 3] << 24);
+    };
+    if constexpr (HF == MQ4_V1) {
+        sc = __builtin_bit_cast(float, le32(0));
+        zp = __builtin_bit_cast(float, le32(4));
+    } else {
+        const uint32_t hd = le32(HF == MQ4_V2 && j >= 128 ? 4 : 0);
+        sc = f16_to_f32(hd & 0xFFFFu);
+        zp = f16_to_f32(hd >> 16);
+    }
+}
+
 // Rows row0 .. row0 + R - 1 (those below O) of one lane group with the plain
 // per-element arithmetic (x read from global memory).
-template <int S, int LPR, int R>
+template <int HF, int S, int LPR, int R>
 __device__ __noinline__ void mq4_rows_plain(const uint8_t *__restrict__ w,
                                             const float *__restrict__ x, float *__restrict__ y,
                                             int I, int O, int row0, int sl)
@@ -92,8 +150,8 @@ __device__ __noinline__ void mq4_rows_plain(const uint8_t *__restrict__ w,
             const int g = u >> 3, p = u & 7;
             const uint8_t *gp = wr + (size_t)g * MQ4_GROUP_BYTES;
             const u32x4 wv = load16_a8(gp + 8 + 16 * p);
-            const uint32_t hd = *reinterpret_cast<const uint32_t *>(gp + (p >= 4 ? 4 : 0));
-            const float scl = f16_to_f32(hd & 0xFFFFu), zro = f16_to_f32(hd >> 16);
+            float scl, zro;
+            Mq4Hdr<HF>::decode(Mq4Hdr<HF>::load(gp, p), scl, zro);
 #pragma unroll
             for (int t = 0; t < S; t++)
                 acc[t] += mq4_chunk_plain(wv, scl, zro, x + (size_t)t * I + (size_t)u * 32);
@@ -109,7 +167,7 @@ __device__ __noinline__ void mq4_rows_plain(const uint8_t *__restrict__ w,
 // ROT: x is unrotated and the workgroup applies the FWHT-256 pre-rotation
 // (signs, then H256 / 16 per block) while staging it; the rotated values are
 // bit-identical to the stand-alone rotation kernel's.
-template <int S, int LPR, int R, int PF, int WPB, bool ROT>
+template <int HF, int S, int LPR, int R, int PF, int WPB, bool ROT>
 __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ x, const int8_t *__restrict__ signs,
     float *__restrict__ y, int I, int O, int ntiles)
@@ -144,18 +202,19 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     xst.load(x, items, signs, NU * 4);
 
     // payload chunk u: group u/8, bytes 8 + 16 (u%8); header dword +0 / +4
-    auto fetch = [&](int u, u32x4 *wv, uint32_t *hv) {
+    typedef typename Mq4Hdr<HF>::T HdrT;
+    auto fetch = [&](int u, u32x4 *wv, HdrT *hv) {
         const int g = u >> 3, p = u & 7;
         const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
 #pragma unroll
         for (int r = 0; r < R; r++) {
             wv[r] = load16_a8(wr[r] + goff + 8 + 16 * p);
-            hv[r] = ld_stream(reinterpret_cast<const uint32_t *>(wr[r] + goff + (p >= 4 ? 4 : 0)));
+            hv[r] = Mq4Hdr<HF>::load(wr[r] + goff, p);
         }
     };
 
     u32x4 wb[PF][R];
-    uint32_t hb[PF][R];
+    HdrT hb[PF][R];
     // the weight stream starts once the activations are staged: a flood of
     // streaming weight requests is served ahead of the activation reads
     const uint32_t bad =
@@ -175,7 +234,7 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
             xst.store_rotated_f32(x, items, NU, signs, xf);
             __syncthreads();
         }
-        if (tile < ntiles) mq4_rows_plain<S, LPR, R>(w, ROT ? xf : x, y, I, O, row0, sl);
+        if (tile < ntiles) mq4_rows_plain<HF, S, LPR, R>(w, ROT ? xf : x, y, I, O, row0, sl);
         return;
     }
     if (tile >= ntiles) return;
@@ -202,10 +261,7 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
         const int uu = valid ? u : 0;
         float scl[R], zro[R];
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            scl[r] = f16_to_f32(hb[j][r] & 0xFFFFu);
-            zro[r] = f16_to_f32(hb[j][r] >> 16);
-        }
+        for (int r = 0; r < R; r++) Mq4Hdr<HF>::decode(hb[j][r], scl[r], zro[r]);
         uint32_t wx[R][4];
 #pragma unroll
         for (int r = 0; r < R; r++)
@@ -259,6 +315,7 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
 
 // General kernel: any alignment of w, S <= QGEMV_MAX_S.  One wave per row;
 // lane takes payload bytes; each weight decoded to f32 as fma(q, scale, zero).
+template <int HF>
 __global__ __launch_bounds__(256) void mq4v2_gemv_general(const uint8_t *__restrict__ w,
                                                           const float *__restrict__ x,
                                                           float *__restrict__ y, int S, int I,
@@ -275,10 +332,8 @@ __global__ __launch_bounds__(256) void mq4v2_gemv_general(const uint8_t *__restr
     for (int k = lane; k < G * 128; k += WAVE) {     // payload byte k of the row
         const int g = k >> 7, b = k & 127;
         const uint8_t *gp = wr + (size_t)g * MQ4_GROUP_BYTES;
-        const int h = b >= 64 ? 4 : 0;
-        const uint32_t hd = (uint32_t)gp[h] | ((uint32_t)gp[h + 1] << 8) |
-                            ((uint32_t)gp[h + 2] << 16) | ((uint32_t)gp[h + 3] << 24);
-        const float scl = f16_to_f32(hd & 0xFFFFu), zro = f16_to_f32(hd >> 16);
+        float scl, zro;
+        mq4_hdr_bytes<HF>(gp, 2 * b, scl, zro);
         float e[4], o[4];
         nib8((uint32_t)gp[8 + b], e, o);
         const float w0 = __builtin_fmaf(e[0] * NIB_XSCALE, scl, zro);
@@ -301,7 +356,8 @@ __global__ __launch_bounds__(256) void mq4v2_gemv_general(const uint8_t *__restr
     }
 }
 
-// Decode-only: W[o][i] = fma(q, scale, zero) (exact q*scale, one rounding).
+// Decode-only: W[o][i] = fma(q, scale, zero) (one rounding), header format HF.
+template <int HF>
 __global__ __launch_bounds__(256) void mq4v2_dequant(const uint8_t *__restrict__ w,
                                                      float *__restrict__ W, int I, int O)
 {
@@ -312,10 +368,8 @@ __global__ __launch_bounds__(256) void mq4v2_dequant(const uint8_t *__restrict__
         const size_t og = idx >> 7;             // row * G + g
         const int b = (int)(idx & 127);
         const uint8_t *gp = w + og * MQ4_GROUP_BYTES;
-        const int h = b >= 64 ? 4 : 0;
-        const uint32_t hd = (uint32_t)gp[h] | ((uint32_t)gp[h + 1] << 8) |
-                            ((uint32_t)gp[h + 2] << 16) | ((uint32_t)gp[h + 3] << 24);
-        const float scl = f16_to_f32(hd & 0xFFFFu), zro = f16_to_f32(hd >> 16);
+        float scl, zro;
+        mq4_hdr_bytes<HF>(gp, 2 * b, scl, zro);
         float e[4], o[4];
         nib8((uint32_t)gp[8 + b], e, o);
         const size_t o_row = og / G;
@@ -323,6 +377,60 @@ __global__ __launch_bounds__(256) void mq4v2_dequant(const uint8_t *__restrict__
         float *dst = W + o_row * I + (size_t)g * 256 + 2 * b;
         dst[0] = __builtin_fmaf(e[0] * NIB_XSCALE, scl, zro);
         dst[1] = __builtin_fmaf(o[0] * NIB_XSCALE, scl, zro);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MQ4-v2 encoder (hipfire "MQ4 V2", section 3) for weights already in the
+// rotated space.  One wave per 256-weight group; lane l holds weights
+// 4l .. 4l+3, so lanes 0..31 hold half 0 and lanes 32..63 half 1.  Per half:
+// lo and hi are the min and max over its 32 lanes; step = (hi - lo) / 15 in
+// f32 (correctly rounded); the stored scale and zero are the fp16 (nearest
+// even) values of step and lo; every code is chosen against the stored
+// values, q = clamp(rint((w - z) / s), 0, 15), so the decoder reproduces the
+// encoder's reconstruction.  A stored scale of 0 (a constant half, or a step
+// too small for fp16) gives q = 0.  An extreme of -0 counts as +0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mq4v2_encode_kernel(const float *__restrict__ W,
+                                                           uint8_t *__restrict__ out, int I,
+                                                           int O)
+{
+    const int lane = threadIdx.x & 63;
+    const int G = I / 256;
+    const int grp = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (grp >= O * G) return;                    // whole waves
+    const int row = grp / G, g = grp - row * G;
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(W + (size_t)row * I + (size_t)g * 256 +
+                                                      4 * lane);
+    float lo = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
+    float hi = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {           // within each 32-lane half
+        lo = fminf(lo, __shfl_xor(lo, m, WAVE));
+        hi = fmaxf(hi, __shfl_xor(hi, m, WAVE));
+    }
+    lo = lo + 0.0f;                              // a -0 extreme counts as +0
+    hi = hi + 0.0f;
+    const float step = __fdiv_rn(hi - lo, 15.0f);
+    const _Float16 s16 = (_Float16)step, z16 = (_Float16)lo;
+    const float st = (float)s16, z = (float)z16;
+    const float wv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        uint32_t q = 0;
+        if (st != 0.0f) {
+            const float qf = __builtin_rintf(__fdiv_rn(wv[k] - z, st));
+            q = qf < 0.0f ? 0u : (qf > 15.0f ? 15u : (uint32_t)qf);
+        }
+        packed |= q << (4 * k);
+    }
+    uint8_t *gp = out + (size_t)grp * MQ4_GROUP_BYTES;
+    *reinterpret_cast<uint16_t *>(gp + 8 + 2 * lane) = (uint16_t)packed;
+    if ((lane & 31) == 0) {
+        const uint32_t hd = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+        *reinterpret_cast<uint32_t *>(gp + (lane >> 3)) = hd;   // +0 / +4
     }
 }
 
@@ -379,7 +487,7 @@ size_t mq4_lds_bytes(int S, int I, bool rot)
     return stage > fallback ? stage : fallback;
 }
 
-template <int S, int LPR, int R, int PF, int WPB, bool ROT>
+template <int HF, int S, int LPR, int R, int PF, int WPB, bool ROT>
 hipError_t launch_t(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
                     hipStream_t st)
 {
@@ -387,14 +495,14 @@ hipError_t launch_t(const uint8_t *w, const float *x, const int8_t *sg, float *y
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
     const int blocks = (ntiles + WPB - 1) / WPB;
     const size_t lds = mq4_lds_bytes(S, I, ROT);
-    auto kern = mq4v2_gemv_stream<S, LPR, R, PF, WPB, ROT>;
+    auto kern = mq4v2_gemv_stream<HF, S, LPR, R, PF, WPB, ROT>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, x, sg, y, I, O, ntiles);
     return hipGetLastError();
 }
 
-template <int S, int R, bool ROT>
+template <int HF, int S, int R, bool ROT>
 hipError_t launch_r(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
                     hipStream_t st)
 {
@@ -403,19 +511,19 @@ hipError_t launch_r(const uint8_t *w, const float *x, const int8_t *sg, float *y
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_MQ4_PF : 2;
     switch (pick_lpr(I / 32)) {
-    case 64: return launch_t<S, 64, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
-    case 32: return launch_t<S, 32, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
-    case 16: return launch_t<S, 16, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
-    default: return launch_t<S, 8, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    case 64: return launch_t<HF, S, 64, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    case 32: return launch_t<HF, S, 32, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    case 16: return launch_t<HF, S, 16, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
+    default: return launch_t<HF, S, 8, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
     }
 }
 
-template <int S, bool ROT>
+template <int HF, int S, bool ROT>
 hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
                     hipStream_t st)
 {
     if constexpr (S == 1) {
-        return launch_r<S, QG_MQ4_R, ROT>(w, x, sg, y, I, O, st);
+        return launch_r<HF, S, QG_MQ4_R, ROT>(w, x, sg, y, I, O, st);
     } else {
         // several vectors: R keeps every workgroup resident at once.  With the
         // rotation every workgroup rotates all S vectors, so ties go to the
@@ -424,9 +532,9 @@ hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y
         static const int cand_rot[] = {3, 2, 1};
         switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_MQ4_WPB_MULTI,
                                     mq4_lds_bytes(S, I, ROT), ROT ? cand_rot : cand, 3)) {
-        case 1: return launch_r<S, 1, ROT>(w, x, sg, y, I, O, st);
-        case 2: return launch_r<S, 2, ROT>(w, x, sg, y, I, O, st);
-        default: return launch_r<S, 3, ROT>(w, x, sg, y, I, O, st);
+        case 1: return launch_r<HF, S, 1, ROT>(w, x, sg, y, I, O, st);
+        case 2: return launch_r<HF, S, 2, ROT>(w, x, sg, y, I, O, st);
+        default: return launch_r<HF, S, 3, ROT>(w, x, sg, y, I, O, st);
         }
     }
 }
@@ -442,7 +550,7 @@ int mq4_stream_vectors(const void *w, const float *x, const int8_t *sg, int S, i
 }
 
 // Streaming launches in groups of at most nmax vectors.
-template <bool ROT>
+template <int HF, bool ROT>
 hipError_t launch_groups(const uint8_t *w, const float *x, const int8_t *sg, float *y, int S,
                          int I, int O, int nmax, hipStream_t st)
 {
@@ -452,14 +560,40 @@ hipError_t launch_groups(const uint8_t *w, const float *x, const int8_t *sg, flo
         float *ys = y + (size_t)s0 * O;
         hipError_t e;
         switch (n) {
-        case 1: e = launch_s<1, ROT>(w, xs, sg, ys, I, O, st); break;
-        case 2: e = launch_s<2, ROT>(w, xs, sg, ys, I, O, st); break;
-        case 3: e = launch_s<3, ROT>(w, xs, sg, ys, I, O, st); break;
-        default: e = launch_s<4, ROT>(w, xs, sg, ys, I, O, st); break;
+        case 1: e = launch_s<HF, 1, ROT>(w, xs, sg, ys, I, O, st); break;
+        case 2: e = launch_s<HF, 2, ROT>(w, xs, sg, ys, I, O, st); break;
+        case 3: e = launch_s<HF, 3, ROT>(w, xs, sg, ys, I, O, st); break;
+        default: e = launch_s<HF, 4, ROT>(w, xs, sg, ys, I, O, st); break;
         }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+template <int HF>
+hipError_t launch_gemv_hf(const void *w, const float *x, float *y, int S, int I, int O,
+                          hipStream_t st)
+{
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    // more vectors than one launch takes run in groups, each streaming the
+    // weights once
+    const int nmax = mq4_stream_vectors(w, x, nullptr, S, I, false);
+    if (nmax > 0) return launch_groups<HF, false>(wb, x, nullptr, y, S, I, O, nmax, st);
+    const int wpb = 4;
+    hipLaunchKernelGGL(mq4v2_gemv_general<HF>, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st,
+                       wb, x, y, S, I, O);
+    return hipGetLastError();
+}
+
+template <int HF>
+hipError_t launch_dequant_hf(const void *w, float *W, int I, int O, hipStream_t st)
+{
+    const size_t n = (size_t)O * (I / 256) * 128;
+    const size_t want = (n + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(mq4v2_dequant<HF>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(w), W, I, O);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -467,15 +601,19 @@ hipError_t launch_groups(const uint8_t *w, const float *x, const int8_t *sg, flo
 hipError_t launch_mq4v2_gemv(const void *w, const float *x, float *y, int S, int I, int O,
                              hipStream_t st)
 {
-    const uint8_t *wb = static_cast<const uint8_t *>(w);
-    // more vectors than one launch takes run in groups, each streaming the
-    // weights once
-    const int nmax = mq4_stream_vectors(w, x, nullptr, S, I, false);
-    if (nmax > 0) return launch_groups<false>(wb, x, nullptr, y, S, I, O, nmax, st);
-    const int wpb = 4;
-    hipLaunchKernelGGL(mq4v2_gemv_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
-                       x, y, S, I, O);
-    return hipGetLastError();
+    return launch_gemv_hf<MQ4_V2>(w, x, y, S, I, O, st);
+}
+
+hipError_t launch_mq4v1_gemv(const void *w, const float *x, float *y, int S, int I, int O,
+                             hipStream_t st)
+{
+    return launch_gemv_hf<MQ4_V1>(w, x, y, S, I, O, st);
+}
+
+hipError_t launch_mq4c_gemv(const void *w, const float *x, float *y, int S, int I, int O,
+                            hipStream_t st)
+{
+    return launch_gemv_hf<MQ4_C>(w, x, y, S, I, O, st);
 }
 
 int mq4v2_rot_check(const void *w, const float *x, const int8_t *signs, int I)
@@ -491,16 +629,30 @@ hipError_t launch_mq4v2_rot_gemv(const void *w, const float *x, const int8_t *si
 {
     const int nmax = mq4_stream_vectors(w, x, signs, S, I, true);
     if (nmax <= 0) return hipErrorInvalidValue;   // callers check mq4v2_rot_check first
-    return launch_groups<true>(static_cast<const uint8_t *>(w), x, signs, y, S, I, O, nmax, st);
+    return launch_groups<MQ4_V2, true>(static_cast<const uint8_t *>(w), x, signs, y, S, I, O,
+                                       nmax, st);
 }
 
 hipError_t launch_mq4v2_dequant(const void *w, float *W, int I, int O, hipStream_t st)
 {
-    const size_t n = (size_t)O * (I / 256) * 128;
-    const size_t want = (n + 255) / 256;
-    const int blocks = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(mq4v2_dequant, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const uint8_t *>(w), W, I, O);
+    return launch_dequant_hf<MQ4_V2>(w, W, I, O, st);
+}
+
+hipError_t launch_mq4v1_dequant(const void *w, float *W, int I, int O, hipStream_t st)
+{
+    return launch_dequant_hf<MQ4_V1>(w, W, I, O, st);
+}
+
+hipError_t launch_mq4c_dequant(const void *w, float *W, int I, int O, hipStream_t st)
+{
+    return launch_dequant_hf<MQ4_C>(w, W, I, O, st);
+}
+
+hipError_t launch_mq4v2_encode(const float *W, void *out, int I, int O, hipStream_t st)
+{
+    const long groups = (long)O * (I / 256);
+    hipLaunchKernelGGL(mq4v2_encode_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, st,
+                       W, static_cast<uint8_t *>(out), I, O);
     return hipGetLastError();
 }
 

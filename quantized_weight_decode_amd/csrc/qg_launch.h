@@ -70,6 +70,15 @@ int mq4v2_rot_check(const void *w, const float *x, const int8_t *signs, int I);
 hipError_t launch_mq4v2_rot_gemv(const void *w, const float *x, const int8_t *signs, float *y,
                                  int S, int I, int O, hipStream_t st);
 hipError_t launch_mq4v2_dequant(const void *w, float *W, int I, int O, hipStream_t st);
+// MQ4 v1 (f32 header per 256) and MQ4C pad (fp16 pair per 256 + zero pad)
+hipError_t launch_mq4v1_gemv(const void *w, const float *x, float *y, int S, int I, int O,
+                             hipStream_t st);
+hipError_t launch_mq4c_gemv(const void *w, const float *x, float *y, int S, int I, int O,
+                            hipStream_t st);
+hipError_t launch_mq4v1_dequant(const void *w, float *W, int I, int O, hipStream_t st);
+hipError_t launch_mq4c_dequant(const void *w, float *W, int I, int O, hipStream_t st);
+// MQ4-v2 encoder: W f32 [O][I] (rotated space, 16-byte aligned) -> 136-byte groups
+hipError_t launch_mq4v2_encode(const float *W, void *out, int I, int O, hipStream_t st);
 hipError_t launch_fwht256(const float *x, const int8_t *signs, float *xr, int S, int I,
                           hipStream_t st);
 

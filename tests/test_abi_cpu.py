@@ -82,3 +82,17 @@ def test_fp8_ue8m0_refusals(q):
     assert f(BAD, BAD, BAD, BAD, 0, 64, 8, 0) == 2
     assert f(BAD, BAD + 1, BAD + 2, BAD, 1, 64, 8, 0) == 4                 # x misaligned
     assert q.qgemv_dequant_fp8b128_ue8m0(BAD, BAD, BAD + 2, 64, 8, 0) == 4
+
+
+def test_mq4_family_refusals(q):
+    assert q.qgemv_mq4v1(BAD, BAD, BAD, 1, 300, 8, 0) == 5
+    assert q.qgemv_mq4c(0, BAD, BAD, 1, 256, 8, 0) == 1
+    assert q.qgemv_mq4c(BAD, BAD + 2, BAD, 1, 256, 8, 0) == 4
+    assert q.qgemv_dequant_mq4v1(BAD, BAD, 300, 8, 0) == 5
+    assert q.qgemv_dequant_mq4c(BAD, BAD + 1, 256, 8, 0) == 4
+    e = q.qgemv_mq4v2_encode
+    assert e(0, BAD, 256, 8, 0) == 1
+    assert e(BAD, BAD, 300, 8, 0) == 5
+    assert e(BAD + 4, BAD, 256, 8, 0) == 4                                   # W not 16-B aligned
+    assert e(BAD, BAD + 4, 256, 8, 0) == 4                                   # out not 8-B aligned
+    assert e(BAD, BAD, 256, 0, 0) == 2
