@@ -75,6 +75,7 @@ class Oracle:
         L.qref_mq4v1_gemv.argtypes = [_u8p, _f32p, _f32p, I, I, I, _rowsp, I]
         L.qref_mq4c_gemv.argtypes = [_u8p, _f32p, _f32p, I, I, I, _rowsp, I]
         L.qref_mq4v2_encode.argtypes = [_f32p, I, I, _u8p]
+        L.qref_router_topk.argtypes = [_f32p, I, I, I, I, _i32p, _f32p]
         L.qref_f32_to_f16.restype = C.c_uint16
         L.qref_f32_to_f16.argtypes = [C.c_float]
         L.qref_moe_i4g.argtypes = [_u8p, _f32p, C.c_longlong, C.c_longlong, I, _i32p,
@@ -84,7 +85,7 @@ class Oracle:
                   L.qref_mq4v2_dequant, L.qref_mq4v2_gemv,
                   L.qref_fwht256, L.qref_moe_i4g, L.qref_set_threads,
                   L.qref_mq4v1_dequant, L.qref_mq4c_dequant, L.qref_mq4v1_gemv,
-                  L.qref_mq4c_gemv, L.qref_mq4v2_encode):
+                  L.qref_mq4c_gemv, L.qref_mq4v2_encode, L.qref_router_topk):
             f.restype = None
 
     # -- scalars ---------------------------------------------------------
@@ -204,6 +205,15 @@ class Oracle:
         out = np.empty(O * (I // 256) * 136, np.uint8)
         self.lib.qref_mq4v2_encode(self._c(W, np.float32), O, I, out)
         return out.reshape(O, (I // 256) * 136)
+
+    def router_topk(self, logits, E, K):
+        """logits f32 [T][ld] (ld >= E) -> ids int32 [T][K], gates f32 [T][K]."""
+        lg = self._c(logits, np.float32)
+        T, ld = lg.shape
+        ids = np.empty((T, K), np.int32)
+        gates = np.empty((T, K), np.float32)
+        self.lib.qref_router_topk(lg, T, E, ld, K, ids, gates)
+        return ids, gates
 
     def f32_to_f16(self, f: float) -> int:
         return self.lib.qref_f32_to_f16(f)

@@ -571,3 +571,52 @@ void qref_moe_i4g(const uint8_t *w, const float *s, long long w_stride,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Router top-k                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Top-K routing of T tokens over E experts, regolith audit "phase 0 + phase
+ * 2 m5 air validation", sections 2.1 and 2.2: the logits of the valid
+ * experts (columns 0..E-1 of rows of stride ld; columns >= E are masked out)
+ * go through a softmax; the K most probable experts are picked in rank
+ * order; each picked expert's gate is its probability renormalised over the
+ * K picked ones.  Equal probabilities rank by the lower expert index (our
+ * reading: the pages do not break ties).  The probability order is the
+ * logit order, so picks compare logits; gates are formed in double,
+ *     g_k = exp(l_k - m) / sum over picked j of exp(l_j - m),
+ * with m the largest logit (the softmax's full normaliser cancels).  Logits
+ * must be finite.
+ */
+void qref_router_topk(const float *logits, int T, int E, int ld, int K,
+                      int32_t *ids, float *gates)
+{
+    for (int t = 0; t < T; t++) {
+        const float *l = logits + (size_t)t * ld;
+        int32_t *id = ids + (size_t)t * K;
+        for (int k = 0; k < K; k++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                int taken = 0;
+                for (int j = 0; j < k; j++)
+                    taken |= id[j] == e;
+                if (taken)
+                    continue;
+                if (best < 0 || l[e] > l[best])
+                    best = e;   /* strict: the lower index wins a tie */
+            }
+            id[k] = best;
+        }
+        double m = (double)l[id[0]], sum = 0.0;
+#if QREF_MUTATE == 14 /* planted: gates normalised over all experts, not the picked */
+        for (int e = 0; e < E; e++)
+            sum += exp((double)l[e] - m);
+#else
+        for (int k = 0; k < K; k++)
+            sum += exp((double)l[id[k]] - m);
+#endif
+        for (int k = 0; k < K; k++)
+            gates[(size_t)t * K + k] = (float)(exp((double)l[id[k]] - m) / sum);
+    }
+}
