@@ -163,6 +163,21 @@ int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S,
                   int I, void *stream);
 
 /*
+ * Router top-k that feeds qgemv_moe_topk: regolith audit "phase 0 + phase 2
+ * m5 air validation", section 2.1 (columns at or past the expert count are
+ * masked out of the softmax; the logits row stride may exceed it) and
+ * section 2.2 (the gates are the picked experts' probabilities renormalised
+ * over the picked set).
+ *   logits  f32 [T][ld], experts 0..E-1 of each row valid (ld >= E); finite
+ *   ids     int32 [T][K]: the K most probable experts, most probable first;
+ *           equal probabilities rank by the lower expert index
+ *   gates   f32 [T][K]: g_k = exp(l_k - m) / sum over picks j of exp(l_j - m)
+ *   1 <= E <= 1024, 1 <= K <= min(E, 64)
+ */
+int qgemv_router_topk(const float *logits, int T, int E, int ld, int K, int32_t *ids,
+                      float *gates, void *stream);
+
+/*
  * Routed experts over grouped-int4 matrices: regolith audit "phase 0 +
  * phase 2 m5 air validation", section 2.2 (the gates are the selection
  * probabilities renormalised over the selected experts) and colibri PR #457,

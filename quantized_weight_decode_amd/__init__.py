@@ -43,6 +43,8 @@ _SIGS = {
                                   C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_fwht256": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_router_topk": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int,
+                                    C.c_void_p, C.c_void_p, C.c_void_p]),
     "qgemv_moe_topk_workspace": (C.c_size_t, [C.c_int, C.c_int, C.c_int]),
     "qgemv_moe_topk": (C.c_int, [C.c_void_p, C.c_void_p, C.c_longlong, C.c_longlong,
                                  C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
@@ -146,6 +148,10 @@ def qgemv_mq4v2_rot(w, x, signs, y, S, I, O, stream):
 
 def qgemv_fwht256(x, signs, x_rot, S, I, stream):
     return lib().qgemv_fwht256(x, signs, x_rot, S, I, stream)
+
+
+def qgemv_router_topk(logits, T, E, ld, K, ids, gates, stream):
+    return lib().qgemv_router_topk(logits, T, E, ld, K, ids, gates, stream)
 
 
 def qgemv_moe_topk_workspace(T, K, O):
@@ -305,6 +311,17 @@ def fwht256(x, signs, out=None):
     _call("qgemv_fwht256", _dev(x, "x", torch.float32), _dev(signs, "signs", torch.int8),
           _dev(y, "x_rot", torch.float32), S, I, _stream())
     return y
+
+
+def router_topk(logits, E, K):
+    """logits f32 [T][ld] (experts 0..E-1 valid) -> (ids int32 [T][K], gates f32 [T][K])."""
+    torch = _torch()
+    T, ld = logits.shape
+    ids = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    gates = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _call("qgemv_router_topk", _dev(logits, "logits", torch.float32), T, E, ld, K,
+          _dev(ids, "ids", torch.int32), _dev(gates, "gates", torch.float32), _stream())
+    return ids, gates
 
 
 def moe_topk_workspace(T, K, O, device):

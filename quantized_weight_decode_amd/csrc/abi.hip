@@ -242,6 +242,16 @@ int qgemv_fwht256(const float *x, const int8_t *signs, float *x_rot, int S, int 
     return launched(qg::launch_fwht256(x, signs, x_rot, S, I, (hipStream_t)stream));
 }
 
+int qgemv_router_topk(const float *logits, int T, int E, int ld, int K, int32_t *ids,
+                      float *gates, void *stream)
+{
+    if (!logits || !ids || !gates) return QGEMV_E_NULL;
+    if (T < 1 || T > MAX_DIM || E < 1 || E > 1024 || ld < E || K < 1 || K > 64 || K > E)
+        return QGEMV_E_DIMS;
+    if (mis4(logits) || mis4(ids) || mis4(gates)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_router_topk(logits, T, E, ld, K, ids, gates, (hipStream_t)stream));
+}
+
 size_t qgemv_moe_topk_workspace(int T, int K, int O)
 {
     (void)T; (void)K; (void)O;

@@ -321,6 +321,76 @@ __global__ __launch_bounds__(256) void moe_i4g_general(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Router top-k (regolith audit, sections 2.1 and 2.2): softmax over the valid
+// experts (columns 0..E-1 of rows of stride ld), the K most probable picked
+// in rank order, gates renormalised over the picked ones.  One wave per
+// token; lane l holds the logits of experts l, l + 64, ... (E <= 1024).  Each
+// of the K rounds takes the wave-wide largest not-yet-picked logit (the lower
+// expert index on a tie) by a butterfly reduction over (value, index) pairs;
+// probability order is logit order, so no exponential is needed to pick.
+// Lane k keeps pick k; g_k = exp(l_k - m) / sum over picks, m = the largest.
+// ---------------------------------------------------------------------------
+constexpr int ROUTER_MAX_E = 1024;
+constexpr int ROUTER_MAX_K = 64;
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T,
+                                                          int E, int ld, int K,
+                                                          int32_t *__restrict__ ids,
+                                                          float *__restrict__ gates)
+{
+    constexpr int PER = ROUTER_MAX_E / WAVE;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;                           // whole waves
+    const float *l = logits + (size_t)t * ld;
+    float v[PER];
+    uint32_t taken = 0;                           // bit j: entry j picked or not an expert
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        const int e = lane + WAVE * j;
+        v[j] = e < E ? l[e] : 0.0f;
+        if (e >= E) taken |= 1u << j;
+    }
+    float pick_l = 0.0f;
+    int pick_e = 0;
+    for (int k = 0; k < K; k++) {
+        float bv = 0.0f;
+        int be = 0x7FFFFFFF;                      // none
+#pragma unroll
+        for (int j = 0; j < PER; j++) {
+            const int e = lane + WAVE * j;
+            if (!((taken >> j) & 1u) && (be == 0x7FFFFFFF || v[j] > bv)) {
+                bv = v[j];
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, WAVE);
+            const int oe = __shfl_xor(be, m, WAVE);
+            const bool better = oe != 0x7FFFFFFF &&
+                                (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
+            if (better) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if (lane == k) {
+            pick_l = bv;
+            pick_e = be;
+        }
+    }
+    const float m = __shfl(pick_l, 0, WAVE);
+    const float ex = lane < K ? expf(pick_l - m) : 0.0f;
+    const float sum = __shfl(sub_reduce<64>(ex), 63, WAVE);
+    if (lane < K) {
+        ids[(size_t)t * K + lane] = pick_e;
+        gates[(size_t)t * K + lane] = ex / sum;
+    }
+}
+
 namespace {
 
 size_t moe_lds_bytes(int K, int I, int RT)
@@ -381,6 +451,14 @@ hipError_t launch_moe_topk(const void *w, const float *scales, long long w_strid
     const int wpb = 4;
     hipLaunchKernelGGL(moe_i4g_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,
                        scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, err_flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float *logits, int T, int E, int ld, int K, int32_t *ids,
+                              float *gates, hipStream_t st)
+{
+    hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, ld,
+                       K, ids, gates);
     return hipGetLastError();
 }
 

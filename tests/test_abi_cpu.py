@@ -96,3 +96,13 @@ def test_mq4_family_refusals(q):
     assert e(BAD + 4, BAD, 256, 8, 0) == 4                                   # W not 16-B aligned
     assert e(BAD, BAD + 4, 256, 8, 0) == 4                                   # out not 8-B aligned
     assert e(BAD, BAD, 256, 0, 0) == 2
+
+
+def test_router_refusals(q):
+    f = q.qgemv_router_topk
+    assert f(0, 4, 256, 256, 8, BAD, BAD, 0) == 1
+    assert f(BAD, 4, 2048, 2048, 8, BAD, BAD, 0) == 2                         # E > 1024
+    assert f(BAD, 4, 256, 200, 8, BAD, BAD, 0) == 2                           # ld < E
+    assert f(BAD, 4, 256, 256, 65, BAD, BAD, 0) == 2                          # K > 64
+    assert f(BAD, 4, 4, 4, 5, BAD, BAD, 0) == 2                               # K > E
+    assert f(BAD + 2, 4, 256, 256, 8, BAD, BAD, 0) == 4
