@@ -22,6 +22,9 @@ A step is one pass of the hot path over one batch of synthetic input:
       for _S2; the _S4 step calls qgemv_fwht256 then qgemv_mq4v2
   moe_E256_O2048_I7168_gs64_T4_K8:
       one qgemv_moe_topk call (4 tokens, top-8 of 256 experts)
+  i4g_prefill_O12288_I6144_gs64_S256, _S2048:
+      one qgemv_i4g_prefill call (256 or 2048 prompt tokens through the
+      grouped-int4 matrix on f32 MFMA; its roofline is the matrix cores')
 
 Dense steps rotate through distinct weight copies totalling over 1 GiB, and
 the routed-expert step cycles through 16 seeded routings over one resident
@@ -49,6 +52,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F32_PEAK_TFS = 157.3   # dense f32 matrix-core peak
 DENSE_27B = 27e9   # weights of the dense decode fixture the tok/s figure is scaled to
 ROTATE_BYTES = 1 << 30
 METRIC = "achieved HBM GB/s (% of MI355X peak) + equiv decode tok/s, batch-1 qGEMV"
@@ -115,6 +119,44 @@ class I4G(Case):
                               self.O, self.gs, self.sp)
         if st:
             raise SystemExit(f"qgemv_i4g: {self.q.strerror(st)}")
+
+
+class Prefill(Case):
+    """Many tokens through one grouped-int4 matrix: a dense contraction on MFMA."""
+    kernel = "i4g_gemm_mfma"
+    bound = "mfma"
+
+    def __init__(self, O, I, gs, S, torch, q, o):
+        import workloads as W
+        self.name = f"i4g_prefill_O{O}_I{I}_gs{gs}_S{S}"
+        self.fmt_desc = f"grouped int4, f32 scale per group, {S} tokens (f32 MFMA)"
+        self.O, self.I, self.gs, self.S = O, I, gs, S
+        rb, ng = (I + 1) // 2, (I + gs - 1) // gs
+        self.weight_bytes = O * rb + O * ng * 4
+        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4)
+        self.alg_flops = 2.0 * S * O * I
+        self.bytes_per_weight = self.weight_bytes / (O * I)
+        dev = torch.device("cuda:0")
+        d = W.gen_i4g(O, I, gs, S=S, seed=0)
+        self.n = 1
+        self.w = torch.from_numpy(d["w"]).to(dev)
+        self.s = torch.from_numpy(d["scales"]).to(dev)
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
+        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.step(0)
+        rows = np.arange(0, O, 97)
+        self.rel = _rel(self.y.cpu().numpy()[:, rows],
+                        o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs, rows=rows))
+        _check(self.rel, self.name)
+        self.cpu_frac = len(rows) / O
+        self.cpu = lambda: o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs, rows=rows)
+
+    def step(self, i):
+        st = self.q.qgemv_i4g_prefill(self.w.data_ptr(), self.s.data_ptr(), self.x.data_ptr(),
+                                      self.y.data_ptr(), self.S, self.I, self.O, self.gs, self.sp)
+        if st:
+            raise SystemExit(f"qgemv_i4g_prefill: {self.q.strerror(st)}")
 
 
 class FP8(Case):
@@ -338,6 +380,9 @@ def build_case(name, torch, q, o):
         "moe_E256_O2048_I7168_gs64_T4_K8": lambda: MoE(256, 2048, 7168, 64, 4, 8, torch, q, o),
         "i4g_O256_I512_gs64": lambda: I4G(256, 512, 64, torch, q, o),
         "i4g_O12288_I6144_gs64_S2": lambda: I4G(12288, 6144, 64, torch, q, o, S=2),
+        "i4g_prefill_O12288_I6144_gs64_S256": lambda: Prefill(12288, 6144, 64, 256, torch, q, o),
+        "i4g_prefill_O12288_I6144_gs64_S2048": lambda: Prefill(12288, 6144, 64, 2048, torch, q,
+                                                               o),
         "i4g_O12288_I6144_gs64_S4": lambda: I4G(12288, 6144, 64, torch, q, o, S=4),
         "fp8b128_O7168_I16384_S2": lambda: FP8(7168, 16384, torch, q, o, S=2),
         "fp8b128_O7168_I16384_S4": lambda: FP8(7168, 16384, torch, q, o, S=4),
@@ -355,7 +400,8 @@ CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_
               "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4",
               "fp8b128_O7168_I16384_S2", "fp8b128_O7168_I16384_S4",
               "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4", "fp8ue8m0_O7168_I16384",
-              "mq4v1_O8192_I8192", "mq4c_O8192_I8192"]
+              "mq4v1_O8192_I8192", "mq4c_O8192_I8192", "i4g_prefill_O12288_I6144_gs64_S256",
+              "i4g_prefill_O12288_I6144_gs64_S2048"]
 
 
 KERNEL_SOURCES = {
@@ -363,6 +409,7 @@ KERNEL_SOURCES = {
     "fp8_gemv_stream": "fp8b128.hip",
     "mq4v2_gemv_stream": "mq4v2.hip",
     "moe_i4g_stream": "moe.hip",
+    "i4g_gemm_mfma": "prefill.hip",
 }
 
 
@@ -430,8 +477,10 @@ def cpu_baseline(case, budget_s=12.0):
         sample = (f"{n} routed-expert calls restricted to {len(case.cpu_rows)} of {case.O} output "
                   f"rows (routing seed 0) in {el:.1f} s")
     else:
-        per_call = case.alg_bytes
-        sample = f"{n} full GEMVs of {case.name} in {el:.1f} s ({el / n * 1e3:.1f} ms each)"
+        frac = getattr(case, "cpu_frac", 1.0)
+        per_call = case.alg_bytes * frac
+        part = "full GEMVs" if frac == 1.0 else f"calls on {frac:.2%} of the output rows"
+        sample = f"{n} {part} of {case.name} in {el:.1f} s ({el / n * 1e3:.1f} ms each)"
     return {"value": round(per_call * n / el / 1e9, 3), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "sample": sample + ", f64 accumulate"}
 
@@ -504,6 +553,12 @@ def main():
                      "traffic": profiled_traffic(case.kernel, case.name)},
         "parity_rel_l2": case.rel,
     }
+    if getattr(case, "bound", "hbm") == "mfma":
+        tf = case.alg_flops / (kms * 1e-3) / 1e12
+        out["roofline"].update({"bound": "mfma", "achieved": round(tf, 2),
+                                "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
+                                "frac": round(tf / MFMA_F32_PEAK_TFS, 4),
+                                "alg_flops_per_launch": case.alg_flops})
     if isinstance(case, MoE):
         out["config"]["distinct_experts_per_routing"] = case.uniq
         out["tokens_per_s"] = round(case.T / (ms_step * 1e-3), 1)

@@ -65,6 +65,20 @@ int qgemv_i4g(const void *w, const float *scales, const float *x, float *y,
               int S, int I, int O, int gs, void *stream);
 
 /*
+ * Grouped int4 for many tokens at once (prompt prefill): the same product as
+ * qgemv_i4g, Y[S][O] = X[S][I] . W^T, for any S >= 1, on the matrix cores
+ * (f32 MFMA: weights decoded to f32 as (q - 8) * s, products and sums in
+ * f32).  colibri PR #457 "metal: grouped-int4 (fmt=4) GEMV support",
+ * sections 1 and 3 (format); the pages route many-token products to a
+ * separate matrix-unit GEMM path from a token-count threshold.
+ *   w, scales, gs  as qgemv_i4g;  x f32 [S][I], y f32 [S][O] (overwritten)
+ * Fast path: I % 32 == 0, gs % 32 == 0, w 4-byte and x 16-byte aligned;
+ * other shapes run the GEMV eight tokens per launch.
+ */
+int qgemv_i4g_prefill(const void *w, const float *scales, const float *x, float *y, int S,
+                      int I, int O, int gs, void *stream);
+
+/*
  * fp8-e4m3 with 128x128 block scales ("fmt=7"): colibri PR #528 "fmt=7:
  * fp8-e4m3-b128 passthrough weight format", section "Design".
  *   w          u8  [O][I]    OCP E4M3-FN codes (bias 7, subnormals, +-0;

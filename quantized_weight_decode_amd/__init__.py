@@ -28,6 +28,8 @@ _SIGS = {
     "qgemv_version": (C.c_char_p, []),
     "qgemv_i4g": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                             C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p]),
+    "qgemv_i4g_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_fp8b128": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_fp8b128_ue8m0": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -116,6 +118,10 @@ def _call(name, *args):
 # -- raw C ABI, same names -------------------------------------------------
 def qgemv_i4g(w, scales, x, y, S, I, O, gs, stream):
     return lib().qgemv_i4g(w, scales, x, y, S, I, O, gs, stream)
+
+
+def qgemv_i4g_prefill(w, scales, x, y, S, I, O, gs, stream):
+    return lib().qgemv_i4g_prefill(w, scales, x, y, S, I, O, gs, stream)
 
 
 def qgemv_fp8b128(w, scale_inv, x, y, S, I, O, stream):
@@ -225,6 +231,17 @@ def i4g(w, scales, x, gs, out=None):
     S = _vecs(x, I)
     y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
     _call("qgemv_i4g", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
+          _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, gs, _stream())
+    return y
+
+
+def i4g_prefill(w, scales, x, gs, out=None):
+    """Grouped-int4 product for many tokens (MFMA): x f32 [S][I] -> y f32 [S][O]."""
+    torch = _torch()
+    O, I = w.shape[0], x.shape[-1]
+    S = x.reshape(-1, I).shape[0]
+    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _call("qgemv_i4g_prefill", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
           _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, gs, _stream())
     return y
 

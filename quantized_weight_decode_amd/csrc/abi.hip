@@ -112,6 +112,17 @@ int qgemv_i4g(const void *w, const float *scales, const float *x, float *y, int 
     return launched(qg::launch_i4g_gemv(w, scales, x, y, S, I, O, gs, (hipStream_t)stream));
 }
 
+int qgemv_i4g_prefill(const void *w, const float *scales, const float *x, float *y, int S,
+                      int I, int O, int gs, void *stream)
+{
+    if (!w || !scales || !x || !y) return QGEMV_E_NULL;
+    if (S < 1 || S > MAX_DIM || I < 1 || O < 1 || I > MAX_DIM || O > MAX_DIM) return QGEMV_E_DIMS;
+    if ((long long)((S + 63) / 64) * ((O + 63) / 64) > 0x7FFFFFFFLL) return QGEMV_E_DIMS;
+    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (mis4(scales) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
+    return launched(qg::launch_i4g_prefill(w, scales, x, y, S, I, O, gs, (hipStream_t)stream));
+}
+
 int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I, int O, int gs,
                       void *stream)
 {

@@ -89,6 +89,10 @@ hipError_t launch_moe_topk(const void *w, const float *scales, long long w_strid
                            int T, int K, const float *x, float *y, int I, int O, int gs,
                            int *err_flag, hipStream_t st);
 
+// many-token grouped-int4 product on MFMA (any S >= 1)
+hipError_t launch_i4g_prefill(const void *w, const float *scales, const float *x, float *y,
+                              int S, int I, int O, int gs, hipStream_t st);
+
 // router top-k (E <= 1024, K <= min(E, 64))
 hipError_t launch_router_topk(const float *logits, int T, int E, int ld, int K, int32_t *ids,
                               float *gates, hipStream_t st);

@@ -106,3 +106,11 @@ def test_router_refusals(q):
     assert f(BAD, 4, 256, 256, 65, BAD, BAD, 0) == 2                          # K > 64
     assert f(BAD, 4, 4, 4, 5, BAD, BAD, 0) == 2                               # K > E
     assert f(BAD + 2, 4, 256, 256, 8, BAD, BAD, 0) == 4
+
+
+def test_prefill_refusals(q):
+    f = q.qgemv_i4g_prefill
+    assert f(0, BAD, BAD, BAD, 64, 512, 8, 64, 0) == 1
+    assert f(BAD, BAD, BAD, BAD, 0, 512, 8, 64, 0) == 2
+    assert f(BAD, BAD, BAD, BAD, 64, 512, 8, 63, 0) == 3
+    assert f(BAD, BAD + 2, BAD, BAD, 64, 512, 8, 64, 0) == 4
