@@ -25,15 +25,28 @@
 
 namespace qg {
 
-// Tile shape of the streaming kernel for one vector: rows per lane group and
-// waves per workgroup.  Measured on the 12288 x 6144 workload: 2 rows x 12
-// waves (512 workgroups, two per CU) beat 4 x 4, 3 x 8, 2 x 8, 4 x 12 and
-// 3 x 16 by 0.1-0.5 us.
+// Tile shape of the streaming kernel for one vector: rows per lane group,
+// waves per workgroup, at most QG_I4G_LPR lanes per row and a ring of
+// QG_I4G_PF chunk-sweeps, the first issued before the activations are
+// converted.  Measured on the 12288 x 6144 workload (mean of six
+// interleaved runs of 300 calls): 32 lanes x 3 rows x 8 waves (256
+// workgroups of 48 rows, one per CU, six sweeps per row through a ring of
+// two) 8.8 us; the same without the early sweep 9.6 us; 64 lanes x 2 rows x
+// 12 waves with all three sweeps in one burst 9.4 us; 32 x 2 x 12 with a
+// ring of three, two sweeps early, 8.9 us; 32 x 4 x 6 9.1 us; 16 lanes per
+// row 9.8-10.0 us.  The early sweep also helps several vectors per call:
+// 15.1 -> 14.1 us at S = 2, 23.6 -> 21.9 us at S = 4.
 #ifndef QG_I4G_R
-#define QG_I4G_R 2
+#define QG_I4G_R 3
 #endif
 #ifndef QG_I4G_WPB
-#define QG_I4G_WPB 12
+#define QG_I4G_WPB 8
+#endif
+#ifndef QG_I4G_LPR
+#define QG_I4G_LPR 32
+#endif
+#ifndef QG_I4G_PF
+#define QG_I4G_PF 2
 #endif
 // Waves per workgroup for several vectors: the staged activations take S
 // times the LDS, so fewer workgroups fit a CU and each must hold more waves.
@@ -96,7 +109,7 @@ __device__ __noinline__ void i4g_rows_plain(const uint8_t *__restrict__ w,
     }
 }
 
-template <int S, int LPR, int R, int PF, int WPB>
+template <int S, int LPR, int R, int PF, int WPB, int EARLY>
 __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ scales,
     const float *__restrict__ x, float *__restrict__ y, int I, int O, int ng,
@@ -142,9 +155,11 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. weight and scale loads of one chunk-sweep into ring slot j.  The
-    //    first round goes out only once the activations are staged: issued
-    //    earlier (before the activation loads return, or between their return
-    //    and the conversion) it measured slower.
+    //    first EARLY sweeps go out right after the activation loads, before
+    //    they are converted, the rest of the ring once the activations are
+    //    staged.  One early sweep measured best: issuing the whole first round
+    //    early (every wave of the chip at once) delays the activation loads
+    //    of later workgroups behind the weight traffic.
     u32x4 wb[PF][R];
     float sb[PF][R];
     auto fetch = [&](int c, int j) {
@@ -156,6 +171,9 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
             sb[j][r] = ld_stream(&sr[r][g]);
         }
     };
+#pragma unroll
+    for (int j = 0; j < EARLY; j++) fetch(j, j);
+    __builtin_amdgcn_sched_barrier(0);
     // 3. activations into LDS as fixed-point digits
     const uint32_t bad = xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, nullptr);
     const bool wbad = __ballot(bad != 0) != 0;
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
         return;
     }
 #pragma unroll
-    for (int j = 0; j < PF; j++) fetch(j, j);
+    for (int j = EARLY; j < PF; j++) fetch(j, j);
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
@@ -316,7 +334,6 @@ template <int S, int LPR, int R, int PF>
 hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, float *y,
                            int I, int O, int gs, hipStream_t st)
 {
-    const int NU = I / 32;
     const int ng = (I + gs - 1) / gs;
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
@@ -324,7 +341,7 @@ hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, flo
     const int waves_per_block = WPB;
     const int blocks = (ntiles + waves_per_block - 1) / waves_per_block;
     const size_t lds = i4g_stream_lds_bytes(S, I);
-    auto kern = i4g_gemv_stream<S, LPR, R, PF, WPB>;
+    auto kern = i4g_gemv_stream<S, LPR, R, PF, WPB, 1>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves_per_block), lds, st, w, s, x, y,
@@ -332,40 +349,22 @@ hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, flo
     return hipGetLastError();
 }
 
-// chunk sweeps in flight per lane: the depth in {2, 3, 4} that leaves the
-// fewest padded sweeps (ties go to the deeper ring)
-inline int pick_pf(int nit)
-{
-    int best = 4, best_pad = 1 << 30;
-    for (int pf : {4, 3, 2}) {
-        const int pad = (nit + pf - 1) / pf * pf - nit;
-        if (pad < best_pad) { best_pad = pad; best = pf; }
-    }
-    return best;
-}
-
 template <int S, int LPR, int R>
 hipError_t launch_stream_pf(const uint8_t *w, const float *s, const float *x, float *y, int I,
                             int O, int gs, hipStream_t st)
 {
     // several vectors: 16-wave workgroups leave 128 registers per lane, so
-    // two sweeps in flight
-    if constexpr (S > 1) {
-        return launch_stream_t<S, LPR, R, 2>(w, s, x, y, I, O, gs, st);
-    } else {
-        switch (pick_pf((I / 32 + LPR - 1) / LPR)) {
-        case 2: return launch_stream_t<S, LPR, R, 2>(w, s, x, y, I, O, gs, st);
-        case 3: return launch_stream_t<S, LPR, R, 3>(w, s, x, y, I, O, gs, st);
-        default: return launch_stream_t<S, LPR, R, 4>(w, s, x, y, I, O, gs, st);
-        }
-    }
+    // two sweeps in flight; one vector: a ring of QG_I4G_PF sweeps
+    return launch_stream_t<S, LPR, R, (S > 1 ? 2 : QG_I4G_PF)>(w, s, x, y, I, O, gs, st);
 }
 
 template <int S, int R>
 hipError_t launch_stream_r(const uint8_t *w, const float *s, const float *x, float *y, int I,
                            int O, int gs, hipStream_t st)
 {
-    switch (pick_lpr(I / 32)) {
+    int lpr = pick_lpr(I / 32);
+    if (S == 1 && lpr > QG_I4G_LPR) lpr = QG_I4G_LPR;
+    switch (lpr) {
     case 64: return launch_stream_pf<S, 64, R>(w, s, x, y, I, O, gs, st);
     case 32: return launch_stream_pf<S, 32, R>(w, s, x, y, I, O, gs, st);
     case 16: return launch_stream_pf<S, 16, R>(w, s, x, y, I, O, gs, st);
