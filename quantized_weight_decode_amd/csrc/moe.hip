@@ -46,6 +46,12 @@
 #ifndef QG_MOE_PF
 #define QG_MOE_PF 3
 #endif
+// ring slots filled before the activations are converted.  Measured at 256
+// experts of 2048 x 7168, 4 tokens, top-8 (mean of five interleaved runs of
+// 300 calls): none 45.9 us, one 45.7, two 45.6, three 45.8.
+#ifndef QG_MOE_EARLY
+#define QG_MOE_EARLY 2
+#endif
 
 namespace qg {
 
@@ -69,6 +75,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     Div20 div_cpg, int RT, int NB, int *__restrict__ err_flag)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    constexpr int MOE_EARLY = QG_MOE_EARLY < PF ? QG_MOE_EARLY : PF;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
     u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                      // [6][NU]
@@ -182,8 +189,11 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         }
     };
 
-    // the weight stream starts once the activations are staged: a flood of
-    // streaming weight requests is served ahead of the activation reads
+    // the first QG_MOE_EARLY sweeps go out before the activations are
+    // converted, the rest of the ring once they are staged
+#pragma unroll
+    for (int j = 0; j < MOE_EARLY; j++) fetch(j);
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t xbad = xst.store(xt, items, NU, reinterpret_cast<uint32_t *>(xq), xc, nullptr);
     const bool wbad = __ballot(xbad != 0) != 0;
     if (lane == 0) wflag[wave] = wbad;
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     for (int k = 0; k < QG_MOE_WPB; k++) xnan |= wflag[k];
     xnan = __builtin_amdgcn_readfirstlane(xnan);
 #pragma unroll
-    for (int j = 0; j < PF; j++) fetch(j);
+    for (int j = MOE_EARLY; j < PF; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[R];

@@ -21,14 +21,30 @@
 #include "qg_device.h"
 #include "qg_launch.h"
 
+// Tile shape for one vector: R rows per lane group, a ring of PF
+// chunk-sweeps per lane, WPB waves per workgroup, the first EARLY sweeps
+// issued before the activations are converted.  Measured on the 8192 x 8192
+// workload with the fused rotation (mean of six interleaved runs of 300
+// calls): 64 lanes x 2 rows x 16 waves with a ring of two and one early
+// sweep 9.2 us; the same with a ring of four 9.4 us, and without the early
+// sweep 10.3 us; two early sweeps 9.4 us; 32 lanes per row 10.1-10.2 us;
+// 4 rows x 8 waves 10.1 us.
 #ifndef QG_MQ4_R
 #define QG_MQ4_R 2
 #endif
 #ifndef QG_MQ4_PF
-#define QG_MQ4_PF 4
+#define QG_MQ4_PF 2
 #endif
 #ifndef QG_MQ4_WPB
 #define QG_MQ4_WPB 16
+#endif
+// at most this many lanes per row for one vector
+#ifndef QG_MQ4_LPR
+#define QG_MQ4_LPR 64
+#endif
+// chunk-sweeps of weights issued before the activations are converted
+#ifndef QG_MQ4_EARLY
+#define QG_MQ4_EARLY 1
 #endif
 // waves per workgroup for several vectors (S times the LDS per workgroup)
 #ifndef QG_MQ4_WPB_MULTI
@@ -167,7 +183,7 @@ __device__ __noinline__ void mq4_rows_plain(const uint8_t *__restrict__ w,
 // ROT: x is unrotated and the workgroup applies the FWHT-256 pre-rotation
 // (signs, then H256 / 16 per block) while staging it; the rotated values are
 // bit-identical to the stand-alone rotation kernel's.
-template <int HF, int S, int LPR, int R, int PF, int WPB, bool ROT>
+template <int HF, int S, int LPR, int R, int PF, int WPB, bool ROT, int EARLY>
 __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ x, const int8_t *__restrict__ signs,
     float *__restrict__ y, int I, int O, int ntiles)
@@ -203,6 +219,8 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
 
     // payload chunk u: group u/8, bytes 8 + 16 (u%8); header dword +0 / +4
     typedef typename Mq4Hdr<HF>::T HdrT;
+    u32x4 wb[PF][R];
+    HdrT hb[PF][R];
     auto fetch = [&](int u, u32x4 *wv, HdrT *hv) {
         const int g = u >> 3, p = u & 7;
         const size_t goff = (size_t)g * MQ4_GROUP_BYTES;
@@ -213,10 +231,12 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
         }
     };
 
-    u32x4 wb[PF][R];
-    HdrT hb[PF][R];
-    // the weight stream starts once the activations are staged: a flood of
-    // streaming weight requests is served ahead of the activation reads
+    // the first EARLY sweeps go out before the activations are converted, the
+    // rest once they are staged: a flood of weight requests from every wave
+    // at once is served ahead of later workgroups' activation reads
+#pragma unroll
+    for (int j = 0; j < EARLY; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t bad =
         xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, xsm, signs);
     const bool wbad = __ballot(bad != 0) != 0;
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     }
     if (tile >= ntiles) return;
 #pragma unroll
-    for (int j = 0; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
+    for (int j = EARLY; j < PF; j++) fetch(min(j * LPR + sl, NU - 1), wb[j], hb[j]);
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
@@ -495,7 +515,8 @@ hipError_t launch_t(const uint8_t *w, const float *x, const int8_t *sg, float *y
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
     const int blocks = (ntiles + WPB - 1) / WPB;
     const size_t lds = mq4_lds_bytes(S, I, ROT);
-    auto kern = mq4v2_gemv_stream<HF, S, LPR, R, PF, WPB, ROT>;
+    constexpr int EARLY = QG_MQ4_EARLY < PF ? QG_MQ4_EARLY : PF;
+    auto kern = mq4v2_gemv_stream<HF, S, LPR, R, PF, WPB, ROT, EARLY>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, x, sg, y, I, O, ntiles);
@@ -510,7 +531,9 @@ hipError_t launch_r(const uint8_t *w, const float *x, const int8_t *sg, float *y
     // several vectors: 16-wave workgroups leave 128 registers per lane, so
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_MQ4_PF : 2;
-    switch (pick_lpr(I / 32)) {
+    int lpr = pick_lpr(I / 32);
+    if (S == 1 && lpr > QG_MQ4_LPR) lpr = QG_MQ4_LPR;
+    switch (lpr) {
     case 64: return launch_t<HF, S, 64, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
     case 32: return launch_t<HF, S, 32, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
     case 16: return launch_t<HF, S, 16, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
