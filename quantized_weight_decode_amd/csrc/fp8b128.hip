@@ -47,18 +47,34 @@ constexpr int FP8_FAST_MAX_S = 4;
 // Stages up to 8 vectors into the fp8 LDS layout with coalesced float4 loads
 // (thread f reads float4 number f, from the offset stage_rot picks); the
 // first NPRE float4s per thread are loaded unconditionally (indices clamped)
-// so later waits count exactly.
+// so later waits count exactly.  The staged columns are the NU chunks from
+// float4 off4 of each vector (vectors xs4 float4s apart): a column phase of
+// a row too long to stage at once, or the whole row.
 template <int NPRE, int NT>
 struct XStageF8 {
     f32x4 v[NPRE];
     int rot;
 
-    __device__ __forceinline__ void load(const float *__restrict__ x, int total)
+    // global float4 index of the g-th staged float4 (PH: a column phase;
+    // otherwise whole rows, where it is g itself)
+    template <bool PH>
+    __device__ __forceinline__ static uint32_t src(int g, int NU, int xs4, int off4)
+    {
+        if constexpr (!PH) return (uint32_t)g;
+        int t, rem;
+        split_f<8>(g, NU * 4, t, rem);
+        return (uint32_t)(t * xs4 + off4 + rem);
+    }
+
+    template <bool PH>
+    __device__ __forceinline__ void load(const float *__restrict__ x, int total, int NU, int xs4,
+                                         int off4)
     {
         rot = stage_rot(total);
 #pragma unroll
         for (int j = 0; j < NPRE; j++)
-            v[j] = ldx4(x, (uint32_t)stage_index((int)threadIdx.x + j * NT, total, rot));
+            v[j] = ldx4(x, src<PH>(stage_index((int)threadIdx.x + j * NT, total, rot), NU, xs4,
+                                   off4));
     }
 
     // g is the float4 index read for the workgroup's f-th read.  Out-of-range
@@ -75,8 +91,9 @@ struct XStageF8 {
         xl[idx] = a;
     }
 
+    template <bool PH>
     __device__ __forceinline__ void store(const float *__restrict__ x, int total, int NU,
-                                          f32x4 *__restrict__ xl)
+                                          int xs4, int off4, f32x4 *__restrict__ xl)
     {
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
@@ -86,7 +103,7 @@ struct XStageF8 {
         const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
         for (int f = (int)threadIdx.x + NPRE * NT; f < total; f += NT) {
             const int g = stage_index(f, total, rot);
-            put(x4[g], f, g, total, NU, xl);
+            put(x4[src<PH>(g, NU, xs4, off4)], f, g, total, NU, xl);
         }
     }
 };
@@ -118,16 +135,16 @@ __device__ __forceinline__ float fp8_chunk_dot(const u32x4 wv, const f32x4 *__re
     return p0 + p1;
 }
 
-template <typename ST, int S, int LPR, int R, int PF, int WPB>
+template <typename ST, int S, int LPR, int R, int PF, int WPB, bool PH>
 __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
     const uint8_t *__restrict__ w, const ST *__restrict__ sc, const float *__restrict__ x,
-    float *__restrict__ y, int I, int O, int nbi, int ntiles)
+    float *__restrict__ y, int I, int O, int nbi, int ntiles, int NUP)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     constexpr int PF0 = QG_FP8_PF0 < PF ? QG_FP8_PF0 : PF;
     static_assert(128 % R == 0, "a lane group's rows must share one 128-row band");
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    const int NU = I / 16;
+    const int NUA = I / 16;                            // lane chunks per row
     f32x4 *xl = reinterpret_cast<f32x4 *>(lds_raw);   // [S][4][NS] + 1 spare
 
     const int lane = threadIdx.x & 63;
@@ -136,46 +153,11 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
     const int sl = lane % LPR;
     const int tile = blockIdx.x * WPB + wave;
     const int row0 = tile * ROWS_PER_WAVE + sub * R;
-    const int nit = (NU + LPR - 1) / LPR;
-    const int nit_pad = (nit + PF - 1) / PF * PF;
     const ST *scrow = sc + (size_t)(min(row0, O - 1) / 128) * nbi;
-
     const uint8_t *wr[R];
 #pragma unroll
     for (int r = 0; r < R; r++)
         wr[r] = w + (size_t)min(row0 + r, O - 1) * I;
-
-    // activations first; every load unconditional
-    XStageF8<8, 64 * WPB> xst;
-    const int total4 = S * NU * 4;
-    xst.load(x, total4);
-    // every wave of the workgroup has issued its activation loads before any
-    // wave issues weight loads (raw barrier: no drain)
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-
-    // only PF0 sweeps go out before the activations are staged: a flood of
-    // streaming weight requests is served ahead of the activation reads
-    u32x4 wb[PF][R];
-    float sb[PF];
-    auto fetch = [&](int c, int j) {
-        const int u = min(c * LPR + sl, NU - 1);
-#pragma unroll
-        for (int r = 0; r < R; r++)
-            wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
-        sb[j] = scale_value(ld_stream(&scrow[u >> 3]));
-    };
-#pragma unroll
-    for (int j = 0; j < PF0; j++) fetch(j, j);
-
-    __builtin_amdgcn_sched_barrier(0);
-    xst.store(x, total4, NU, xl);
-    __syncthreads();
-    if (tile >= ntiles) return;
-#pragma unroll
-    for (int j = PF0; j < PF; j++) fetch(j, j);
-    __builtin_amdgcn_sched_barrier(0);
 
     float acc[S][R];
 #pragma unroll
@@ -183,41 +165,88 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
 
-    auto consume = [&](int c, int j) {
-        const int u = c * LPR + sl;
-        const bool valid = u < NU;
-        const int uu = valid ? u : 0;
-        const float s = valid ? sb[j] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < S; t++) {
-            const f32x4 *xt = xl + (size_t)t * 4 * seg_stride(NU);
-#pragma unroll
-            for (int r = 0; r < R; r++) {
-                const float p = fp8_chunk_dot(wb[j][r], xt, NU, uu);
-                // lanes past the row end add nothing (not even a NaN)
-                acc[t][r] = valid ? __builtin_fmaf(s, p, acc[t][r]) : acc[t][r];
-            }
-        }
-    };
-    // rounds of PF sweeps; refills unconditional and pinned; last round none
-    const int nrounds = nit_pad / PF;
-    for (int rd = 0; rd + 1 < nrounds; rd++) {
-#pragma unroll
-        for (int j = 0; j < PF; j++) {
-            const int c = rd * PF + j;
-            consume(c, j);
-            const int un = min((c + PF) * LPR + sl, NU - 1);
+    // PH: column phases of NUP chunks, each staging its columns of every
+    // vector, then streaming them for the workgroup's rows; the sums run on
+    // across phases, so every weight byte is still read once.  Otherwise
+    // one phase of whole rows.
+    auto phase = [&](int c0, int NU) {
+        const int nit = (NU + LPR - 1) / LPR;
+        const int nit_pad = (nit + PF - 1) / PF * PF;
+        if (PH && c0 > 0) __syncthreads();   // every wave is done with the previous phase
+
+        // activations first; every load unconditional
+        XStageF8<8, 64 * WPB> xst;
+        const int total4 = S * NU * 4;
+        xst.template load<PH>(x, total4, NU, I / 4, c0 * 4);
+        // every wave of the workgroup has issued its activation loads before
+        // any wave issues weight loads (raw barrier: no drain)
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+
+        // only PF0 sweeps go out before the activations are staged: a flood
+        // of streaming weight requests is served ahead of the activation reads
+        u32x4 wb[PF][R];
+        float sb[PF];
+        auto fetch = [&](int c, int j) {
+            const int u = c0 + min(c * LPR + sl, NU - 1);
 #pragma unroll
             for (int r = 0; r < R; r++)
-                wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (uint32_t)un * 16u));
-            sb[j] = scale_value(ld_stream(&scrow[un >> 3]));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+                wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(wr[r] + (size_t)u * 16));
+            sb[j] = scale_value(ld_stream(&scrow[u >> 3]));
+        };
 #pragma unroll
-    for (int j = 0; j < PF; j++) {
-        consume((nrounds - 1) * PF + j, j);
-        __builtin_amdgcn_sched_barrier(0);   // one slot at a time, as in the loop
+        for (int j = 0; j < PF0; j++) fetch(j, j);
+
+        __builtin_amdgcn_sched_barrier(0);
+        xst.template store<PH>(x, total4, NU, I / 4, c0 * 4, xl);
+        __syncthreads();
+        // waves past the last row helped stage; with one phase they are done,
+        // with several they run every phase (clamped rows, nothing stored) to
+        // reach each phase's barriers
+        if (!PH && tile >= ntiles) return false;
+#pragma unroll
+        for (int j = PF0; j < PF; j++) fetch(j, j);
+        __builtin_amdgcn_sched_barrier(0);
+
+        auto consume = [&](int c, int j) {
+            const int u = c * LPR + sl;
+            const bool valid = u < NU;
+            const int uu = valid ? u : 0;
+            const float s = valid ? sb[j] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < S; t++) {
+                const f32x4 *xt = xl + (size_t)t * 4 * seg_stride(NU);
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const float p = fp8_chunk_dot(wb[j][r], xt, NU, uu);
+                    // lanes past the row end add nothing (not even a NaN)
+                    acc[t][r] = valid ? __builtin_fmaf(s, p, acc[t][r]) : acc[t][r];
+                }
+            }
+        };
+        // rounds of PF sweeps; refills unconditional and pinned; last round none
+        const int nrounds = nit_pad / PF;
+        for (int rd = 0; rd + 1 < nrounds; rd++) {
+#pragma unroll
+            for (int j = 0; j < PF; j++) {
+                const int c = rd * PF + j;
+                consume(c, j);
+                fetch(c + PF, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < PF; j++) {
+            consume((nrounds - 1) * PF + j, j);
+            __builtin_amdgcn_sched_barrier(0);   // one slot at a time, as in the loop
+        }
+        return true;
+    };
+    if constexpr (PH) {
+        for (int c0 = 0; c0 < NUA; c0 += NUP) phase(c0, min(NUP, NUA - c0));
+    } else {
+        if (!phase(0, NUA)) return;
     }
 
 #pragma unroll
@@ -289,6 +318,19 @@ size_t fp8_lds_bytes(int S, int I)
     return ((size_t)S * 4 * seg_stride(I / 16) + 1) * sizeof(f32x4);
 }
 
+// Lane chunks per column phase: the whole row when S vectors of it fit the
+// LDS, else the fewest equal phases (multiples of 64 chunks, 1024 columns)
+// that do.
+int fp8_phase_chunks(int S, int I)
+{
+    const int NUA = I / 16;
+    for (int nph = 1;; nph++) {
+        int nup = (NUA + nph - 1) / nph;
+        if (nph > 1) nup = (nup + 63) / 64 * 64;
+        if (fp8_lds_bytes(S, nup * 16) <= LDS_BUDGET) return nup;
+    }
+}
+
 template <typename ST, int S, int LPR, int R, int PF, int WPB>
 hipError_t launch_t(const uint8_t *w, const ST *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
@@ -296,12 +338,14 @@ hipError_t launch_t(const uint8_t *w, const ST *sc, const float *x, float *y, in
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     const int ntiles = (O + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
     const int blocks = (ntiles + WPB - 1) / WPB;
-    const size_t lds = fp8_lds_bytes(S, I);
-    auto kern = fp8_gemv_stream<ST, S, LPR, R, PF, WPB>;
+    const int nup = fp8_phase_chunks(S, I);
+    const size_t lds = fp8_lds_bytes(S, nup * 16);
+    auto kern = nup < I / 16 ? fp8_gemv_stream<ST, S, LPR, R, PF, WPB, true>
+                             : fp8_gemv_stream<ST, S, LPR, R, PF, WPB, false>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), lds, st, w, sc, x, y, I, O,
-                       (I + 127) / 128, ntiles);
+                       (I + 127) / 128, ntiles, nup);
     return hipGetLastError();
 }
 
@@ -332,8 +376,8 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
         // several vectors: R keeps every workgroup resident at once (the rows
         // of a lane group must share a 128-row band, so R divides 128)
         static const int cand[] = {1, 2};
-        switch (pick_rows_per_group(O, pick_lpr(I / 16), QG_FP8_WPB_MULTI, fp8_lds_bytes(S, I),
-                                    cand, 2)) {
+        switch (pick_rows_per_group(O, pick_lpr(I / 16), QG_FP8_WPB_MULTI,
+                                    fp8_lds_bytes(S, fp8_phase_chunks(S, I) * 16), cand, 2)) {
         case 1: return launch_r<ST, S, 1>(w, sc, x, y, I, O, st);
         default: return launch_r<ST, S, 2>(w, sc, x, y, I, O, st);
         }
@@ -341,12 +385,11 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
 }
 
 // Vectors one streaming launch takes for this shape (0: not applicable).
+// Activations too long for the LDS are staged in column phases.
 int fp8_stream_vectors(const void *w, const float *x, int S, int I)
 {
     if (I % 16 != 0 || ((uintptr_t)w & 15) != 0 || ((uintptr_t)x & 15) != 0) return 0;
-    int n = S < FP8_FAST_MAX_S ? S : FP8_FAST_MAX_S;
-    while (n > 0 && fp8_lds_bytes(n, I) > LDS_BUDGET) --n;
-    return n;
+    return S < FP8_FAST_MAX_S ? S : FP8_FAST_MAX_S;
 }
 
 template <typename ST>
@@ -354,8 +397,8 @@ hipError_t launch_gemv(const void *w, const ST *sc, const float *x, float *y, in
                        int O, hipStream_t st)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
-    // more vectors than one launch takes (S > 4, or their activations do not
-    // fit the LDS) run in groups, each streaming the weights once
+    // more vectors than one launch takes (S > 4) run in groups, each
+    // streaming the weights once
     const int nmax = fp8_stream_vectors(w, x, S, I);
     if (nmax > 0) {
         for (int s0 = 0; s0 < S; s0 += nmax) {

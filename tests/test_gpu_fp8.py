@@ -41,7 +41,7 @@ def test_dequant_bit_exact(q, qref, O, I):
     (2048, 6144, 1), (2048, 6144, 4), (6144, 2048, 1), (384, 6144, 3),
     (130, 200, 2), (129, 128, 1), (128, 129, 1), (1, 1, 1), (300, 2048, 2),
     (77, 16, 1), (64, 4096, 8),
-    # several vectors whose activations do not all fit the LDS: groups of launches
+    # several vectors whose activations do not all fit the LDS: column phases
     (300, 16384, 4), (7168, 16384, 2),
 ])
 def test_gemv_matches_oracle(q, qref, O, I, S):

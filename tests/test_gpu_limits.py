@@ -4,9 +4,9 @@ A streaming launch stages each activation vector of the call in LDS, whose
 size per workgroup bounds the row length (and, for several vectors, how
 many vectors share one launch).  These cases sit at those bounds on both
 sides: the last length that streams, the first that takes the general
-kernel or more launches, each against the oracle to the same bar as every
-other GEMV test (relative L2 1e-5), plus the fused rotation's largest
-accepted length and its first refusal.  colibri PR #457 "metal: grouped-int4
+kernel, more launches or (fp8) several column phases, each against the
+oracle to the same bar as every other GEMV test (relative L2 1e-5), plus
+the fused rotation's largest accepted length and its first refusal.  colibri PR #457 "metal: grouped-int4
 (fmt=4) GEMV support", sections 1 and 3 (i4g); the fp8 block-scale and
 MQ4-v2 layouts as in the format-specific tests.
 """
@@ -37,10 +37,11 @@ def test_i4g_long_rows(q, qref, O, I, S):
     assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, 64))
 
 
-# fp8 stages 4 B per column and vector: 36864 columns stream, 40960 (160 KiB
-# plus padding) take the general kernel; three vectors of 16384 run as
-# launches of fewer vectors
-@pytest.mark.parametrize("O,I,S", [(130, 36864, 1), (130, 40960, 1), (130, 16384, 3)])
+# fp8 stages 4 B per column and vector: 36864 columns stream in one phase,
+# 40960 (160 KiB plus padding) in two column phases, as do three or four
+# vectors of 16384; 100000 columns take three phases of one vector
+@pytest.mark.parametrize("O,I,S", [(130, 36864, 1), (130, 40960, 1), (130, 16384, 3),
+                                   (200, 16384, 4), (65, 100000, 1), (129, 49152, 2)])
 def test_fp8_long_rows(q, qref, O, I, S):
     d = W.gen_fp8b128(O, I, S=S, seed=I + S)
     y = host(q.fp8b128(dev(d["w"]), dev(d["scale_inv"]), dev(d["x"])))
