@@ -39,6 +39,9 @@ def test_dequant_bit_exact(q, qref, O, I, gs):
     (1, 32, 32, 1), (1, 1, 2, 1),
     # several vectors: 16-wave workgroups; S > 4 runs as groups of streaming launches
     (12288, 6144, 64, 2), (4000, 6144, 64, 4), (300, 1024, 64, 6), (65, 6144, 64, 7),
+    # four vectors on the int8 matrix cores: scale groups of one, two and three
+    # 64-column blocks, ragged row blocks
+    (1000, 6144, 128, 4), (96, 4096, 192, 4), (17, 64, 64, 4), (12288, 6144, 64, 4),
 ])
 def test_gemv_matches_oracle(q, qref, O, I, gs, S):
     d = W.gen_i4g(O, I, gs, S=S, seed=7 * O + I)
@@ -72,7 +75,8 @@ def test_nan_activation_poisons_all_rows(q):
     assert np.isnan(y).all()
 
 
-@pytest.mark.parametrize("O,I,S", [(300, 512, 1), (12288, 6144, 1), (200, 6144, 2)])
+@pytest.mark.parametrize("O,I,S", [(300, 512, 1), (12288, 6144, 1), (200, 6144, 2),
+                                   (200, 6144, 4)])
 def test_infinite_activations_propagate(q, qref, O, I, S):
     # an infinity makes its rows +-inf, or NaN where a zero weight meets it or
     # two infinities of opposite sign meet, exactly as in the plain definition
@@ -85,7 +89,7 @@ def test_infinite_activations_propagate(q, qref, O, I, S):
     assert_y_close(y, ref)
 
 
-@pytest.mark.parametrize("O,I,S", [(512, 6144, 1), (256, 2048, 2)])
+@pytest.mark.parametrize("O,I,S", [(512, 6144, 1), (256, 2048, 2), (256, 2048, 4)])
 def test_wide_dynamic_range_activations(q, qref, O, I, S):
     # magnitudes spread over twelve decades, zeros, subnormals and one chunk
     # holding a value 1e4 times its neighbours
