@@ -339,20 +339,29 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
     const int row0 = (blockIdx.x * MV_RB + rbl) * 16;
     const int g = lane >> 4, j = lane & 15;
 
-    // 1. activations: item f is 8 columns 64 kb + 8 m of vector t
-    //    (kb = f / 32, t = f / 8 % 4, m = f % 8); vectors past S are zeros
+    // 1. activations: item f is 8 columns 64 kb + 8 m of vector t (t = f /
+    //    (8 NKB), kb = f / 8 % NKB, m = f % 8): vector-major, so whole waves
+    //    of items past S only write zeros
     const int items = NKB * 32;
+    const int ipv = NKB * 8;   // items per vector
+    auto item_t = [&](int f) { return (f >= ipv) + (f >= 2 * ipv) + (f >= 3 * ipv); };
     f32x4 xa[MV_NPRE], xb[MV_NPRE];
 #pragma unroll
     for (int p = 0; p < MV_NPRE; p++) {
         // unconditional loads (clamped index; unused items are zeroed after
         // the loads) so that the waits for them count exactly
         const int f = min((int)threadIdx.x + p * NT, items - 1);
-        const int kb = f >> 5, t = min((f >> 3) & 3, S - 1), m = f & 7;
+        const int t = min(item_t(f), S - 1), kb = (f - item_t(f) * ipv) >> 3, m = f & 7;
         const float *src = x + (size_t)t * I + kb * 64 + m * 8;
         xa[p] = *reinterpret_cast<const f32x4 *>(src);
         xb[p] = *reinterpret_cast<const f32x4 *>(src + 4);
     }
+    // every wave of the workgroup has issued its activation loads before any
+    // wave issues weight loads (raw barrier: no drain); without it the last
+    // activation loads arrived up to 5 us into the call, behind weight misses
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     // 2. this wave's column range of its 16 rows.  A load step is MV_SS
     //    blocks: lane l reads 32 bytes (one block) of row l / 4, so each row's
     //    128 bytes come in one piece, and its group scale; the step goes
@@ -378,18 +387,35 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
     const int nst = (nk + MV_SS - 1) / MV_SS;
 #pragma unroll
     for (int slot = 0; slot < MV_PF; slot++) fetch(slot, slot);   // in flight while x converts
+    // the activations count as redefined here: the compiler can neither
+    // reload them later (behind the weight loads) nor wait for more than them
+#pragma unroll
+    for (int p = 0; p < MV_NPRE; p++) asm volatile("" : "+v"(xa[p]), "+v"(xb[p]));
 
     uint32_t bad = 0;
 #pragma unroll
     for (int p = 0; p < MV_NPRE; p++) {
         const int f = (int)threadIdx.x + p * NT;
         if (f >= items) continue;   // whole 8-lane groups (items and NT are multiples of 8)
-        const int kb = f >> 5, t = (f >> 3) & 3, m = f & 7;
-        const bool live = t < S;   // vectors past S are zeros
-        const float v[8] = {live ? xa[p].x : 0.0f, live ? xa[p].y : 0.0f,
-                            live ? xa[p].z : 0.0f, live ? xa[p].w : 0.0f,
-                            live ? xb[p].x : 0.0f, live ? xb[p].y : 0.0f,
-                            live ? xb[p].z : 0.0f, live ? xb[p].w : 0.0f};
+        const int t = item_t(f), kb = (f - t * ipv) >> 3, m = f & 7;
+        // B bytes: digit d of columns 16 (m / 2) + 8 (m % 2) + {0,2,4,6} then
+        // {1,3,5,7}, in B slot 16 g + j (g = m / 2, j = 4 t + d) stored at
+        // 16 g + (j ^ swz): the slots a wave writes for one (t, d) would all
+        // fall on the same LDS banks unswizzled
+        const int swz = (kb * 4 + (m >> 1)) & 15;
+        uint2 *dst0 = reinterpret_cast<uint2 *>(bl + (size_t)kb * 64 + 16 * (m >> 1)) + (m & 1);
+        auto dst = [&](int d) { return dst0 + 2 * ((4 * t + d) ^ swz); };
+        int2 *mm = ml + (size_t)kb * 16 + 4 * t;
+        if (t >= S) {   // a vector slot past S: zeros
+#pragma unroll
+            for (int d = 0; d < 4; d++) *dst(d) = uint2{0u, 0u};
+            if (m == 0)
+#pragma unroll
+                for (int d = 0; d < 4; d++) mm[d] = int2{0, 0x3F800000};
+            continue;
+        }
+        const float v[8] = {xa[p].x, xa[p].y, xa[p].z, xa[p].w,
+                            xb[p].x, xb[p].y, xb[p].z, xb[p].w};
         uint32_t mx = 0;
 #pragma unroll
         for (int k = 0; k < 8; k++) mx = max(mx, __builtin_bit_cast(uint32_t, v[k]) & 0x7FFFFFFFu);
@@ -404,19 +430,6 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
         for (int k = 0; k < 8; k++)
             sd[k] = (__builtin_bit_cast(uint32_t, __builtin_fmaf(v[k], sin, 12582912.0f)) -
                      0x4ABF7F80u) ^ 0x808080u;
-        int ds[3];
-#pragma unroll
-        for (int d = 0; d < 3; d++) {
-            int sum = 0;
-#pragma unroll
-            for (int k = 0; k < 8; k++) sum += (int)(int8_t)(uint8_t)(sd[k] >> (8 * d));
-            sum = quad_sum_i32(sum);
-            sum += __builtin_amdgcn_update_dpp(0, sum, 0x141, 0xF, 0xF, false);
-            ds[d] = sum;
-        }
-        // B bytes: digit d of columns 16 (m / 2) + 8 (m % 2) + {0,2,4,6} then {1,3,5,7}
-        uint2 *dst = reinterpret_cast<uint2 *>(bl + (size_t)kb * 64 + 16 * (m >> 1) + 4 * t) +
-                     (m & 1);
 #pragma unroll
         for (int d = 0; d < 3; d++) {
             const uint32_t sel = (uint32_t)d | ((uint32_t)(4 + d) << 8) | 0x0C0C0000u;
@@ -424,17 +437,19 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
             const uint32_t e1 = __builtin_amdgcn_perm(sd[6], sd[4], sel);
             const uint32_t o0 = __builtin_amdgcn_perm(sd[3], sd[1], sel);
             const uint32_t o1 = __builtin_amdgcn_perm(sd[7], sd[5], sel);
-            dst[2 * d] = uint2{__builtin_amdgcn_perm(e1, e0, 0x05040100u),
-                               __builtin_amdgcn_perm(o1, o0, 0x05040100u)};
+            const uint32_t ev = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+            const uint32_t od = __builtin_amdgcn_perm(o1, o0, 0x05040100u);
+            *dst(d) = uint2{ev, od};
+            // the block's digit sum: four signed bytes per dot, then 8 lanes
+            int sum = __builtin_amdgcn_sdot4((int)ev, 0x01010101, 0, false);
+            sum = __builtin_amdgcn_sdot4((int)od, 0x01010101, sum, false);
+            sum = quad_sum_i32(sum);
+            sum += __builtin_amdgcn_update_dpp(0, sum, 0x141, 0xF, 0xF, false);
+            if (m == 0)
+                mm[d] = int2{8 * sum, (int)((e - 21u + 8u * (uint32_t)d) << 23)};   // 2^(E-22) 256^d
         }
-        dst[6] = uint2{0u, 0u};   // column 4t + 3
-        if (m == 0) {
-            int2 *mm = ml + (size_t)kb * 16 + 4 * t;
-#pragma unroll
-            for (int d = 0; d < 3; d++)
-                mm[d] = int2{8 * ds[d], (int)((e - 21u + 8u * (uint32_t)d) << 23)};   // 2^(E-22) 256^d
-            mm[3] = int2{0, 0};
-        }
+        *dst(3) = uint2{0u, 0u};   // column 4t + 3
+        if (m == 0) mm[3] = int2{0, 0x3F800000};
     }
     const bool wbad = __ballot(bad != 0) != 0;
     if (lane == 0) wflag[wave] = wbad;
@@ -471,7 +486,7 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
                                                                           8 * g);
                         const i32x4 a = {(int)(wv.x & 0x0F0F0F0Fu), (int)((wv.x >> 4) & 0x0F0F0F0Fu),
                                          (int)(wv.y & 0x0F0F0F0Fu), (int)((wv.y >> 4) & 0x0F0F0F0Fu)};
-                        const u32x4 bu = bl[(size_t)kb * 64 + lane];
+                        const u32x4 bu = bl[(size_t)kb * 64 + 16 * g + (j ^ ((kb * 4 + g) & 15))];
                         const i32x4 b = {(int)bu.x, (int)bu.y, (int)bu.z, (int)bu.w};
                         const int2 mm = ml[(size_t)kb * 16 + j];
                         const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(wsc + p * 16 + 4 * g);
@@ -675,10 +690,10 @@ hipError_t launch_mv_s(const uint8_t *w, const float *s, const float *x, float *
 
 // the matrix-core kernel takes four vectors of rows in whole 64-column
 // blocks, scale groups of whole blocks, 8-byte aligned weights and 16-byte
-// aligned activations that its staging holds.  Its staging always converts
-// four vector slots, so its time barely depends on S: at 12288 x 6144 it
-// measured 18.3 us for two and for four vectors, against 14.6 and 22.8 us
-// for the streaming kernel, which therefore keeps two and three.
+// aligned activations that its staging holds.  Its time barely depends on
+// S: at 12288 x 6144 it measured 17.2 us for four vectors and 16.9 us for
+// two, against 22.9 and 14.6 us for the streaming kernel, which therefore
+// keeps two and three.
 bool i4g_mv_fits(const void *w, const float *x, int S, int I, int gs)
 {
     return QG_I4G_MV && S == 4 && I % 64 == 0 && gs % 64 == 0 &&
