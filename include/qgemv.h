@@ -58,8 +58,11 @@ const char *qgemv_version(void);
  *   gs      even, >= 2; any I >= 1 (a last partial group is allowed)
  * Rows whose bytes are 16-byte aligned (I % 32 == 0, w and x 16-byte
  * aligned) with gs % 32 == 0 take the streaming kernel (S > 4 runs in groups
- * of up to 4 vectors, each group streaming the weights once); every other
- * valid shape takes a slower general kernel with the same result definition.
+ * of up to 4 vectors, each group streaming the weights once); a group of
+ * exactly four vectors with I % 64 == 0, gs % 64 == 0 and I up to 8896 runs
+ * on the int8 matrix cores instead (activations in a 22-bit fixed point per
+ * 64 columns, integer block sums exact).  Every other valid shape takes a
+ * slower general kernel with the same result definition.
  */
 int qgemv_i4g(const void *w, const float *scales, const float *x, float *y,
               int S, int I, int O, int gs, void *stream);
@@ -87,6 +90,9 @@ int qgemv_i4g_prefill(const void *w, const float *scales, const float *x, float 
  *              weight (o,i) = e4m3(w[o][i]) * scale_inv[o/128][i/128]
  *              (a multiply, whatever the name says)
  *   x          f32 [S][I],  y f32 [S][O]
+ * Rows with I % 16 == 0 and 16-byte aligned w and x take the streaming
+ * kernel (vectors that do not fit its LDS staging together are staged in
+ * column phases inside the launch); other shapes a general kernel.
  */
 int qgemv_fp8b128(const void *w, const float *scale_inv, const float *x,
                   float *y, int S, int I, int O, void *stream);

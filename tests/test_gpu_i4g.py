@@ -3,7 +3,11 @@
 Shapes follow colibri PR #457, section 5 (I a multiple of gs, I = 200 / 201,
 I <= gs, S = 1..4, an activation forced to 50.0 in group 0) plus the
 workload shapes O=256 x I=512 and O=12288 x I=6144 at gs = 64 and 128.
-Decoded weights must match bit for bit; y to relative L2 <= 1e-5.
+Decoded weights must match bit for bit; y to relative L2 <= 1e-5.  Four
+vectors of rows in whole 64-column blocks run on the int8 matrix cores
+(activations in a 22-bit fixed point per 64 columns): their cases include
+scale groups of one, two and three blocks, infinities and a twelve-decade
+dynamic range.
 """
 import numpy as np
 import pytest
