@@ -689,15 +689,15 @@ hipError_t launch_mv_s(const uint8_t *w, const float *s, const float *x, float *
 }
 
 // the matrix-core kernel takes four vectors of rows in whole 64-column
-// blocks, scale groups of whole blocks, 8-byte aligned weights and 16-byte
-// aligned activations that its staging holds.  Its time barely depends on
+// blocks, scale groups of whole blocks, 16-byte aligned weights and
+// activations that its staging holds.  Its time barely depends on
 // S: at 12288 x 6144 it measured 17.2 us for four vectors and 16.9 us for
 // two, against 22.9 and 14.6 us for the streaming kernel, which therefore
 // keeps two and three.
 bool i4g_mv_fits(const void *w, const float *x, int S, int I, int gs)
 {
     return QG_I4G_MV && S == 4 && I % 64 == 0 && gs % 64 == 0 &&
-           ((uintptr_t)w & 7) == 0 && ((uintptr_t)x & 15) == 0 &&
+           ((uintptr_t)w & 15) == 0 && ((uintptr_t)x & 15) == 0 &&
            i4g_mv_lds_bytes(I) <= LDS_BUDGET && (I / 64) * 32 <= MV_NPRE * 64 * MV_WPB;
 }
 
