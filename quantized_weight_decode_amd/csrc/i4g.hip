@@ -50,8 +50,11 @@ namespace qg {
 #endif
 // Waves per workgroup for several vectors: the staged activations take S
 // times the LDS, so fewer workgroups fit a CU and each must hold more waves.
+// With at most 32 lanes per row (as for one vector), measured on 12288 x
+// 6144 with two vectors: 12 waves 11.1 us, 14 waves 12.6 us, 10 waves 18.6
+// us, 16 lanes per row 16.5 us; the former 64 lanes x 16 waves 14.6 us.
 #ifndef QG_I4G_WPB_MULTI
-#define QG_I4G_WPB_MULTI 16
+#define QG_I4G_WPB_MULTI 12
 #endif
 
 // activation items (8 columns each) each thread loads up front
@@ -591,6 +594,13 @@ __global__ __launch_bounds__(256) void i4g_dequant(
 // ---------------------------------------------------------------------------
 namespace {
 
+// lanes per row: the fullest sweep, at most QG_I4G_LPR
+inline int i4g_lanes_per_row(int I)
+{
+    const int lpr = pick_lpr(I / 32);
+    return lpr > QG_I4G_LPR ? QG_I4G_LPR : lpr;
+}
+
 template <int S, int LPR, int R, int PF>
 hipError_t launch_stream_t(const uint8_t *w, const float *s, const float *x, float *y,
                            int I, int O, int gs, hipStream_t st)
@@ -623,8 +633,7 @@ template <int S, int R>
 hipError_t launch_stream_r(const uint8_t *w, const float *s, const float *x, float *y, int I,
                            int O, int gs, hipStream_t st)
 {
-    int lpr = pick_lpr(I / 32);
-    if (S == 1 && lpr > QG_I4G_LPR) lpr = QG_I4G_LPR;
+    const int lpr = i4g_lanes_per_row(I);
     switch (lpr) {
     case 64: return launch_stream_pf<S, 64, R>(w, s, x, y, I, O, gs, st);
     case 32: return launch_stream_pf<S, 32, R>(w, s, x, y, I, O, gs, st);
@@ -643,10 +652,11 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
         return launch_stream_r<S, QG_I4G_R>(w, s, x, y, I, O, gs, st);
     } else {
         // several vectors: the staged activations take S times the LDS, so
-        // few workgroups fit a CU; R keeps them all resident (12288 rows,
-        // S = 2 or 4: R = 3, 256 workgroups of 48 rows)
-        static const int cand[] = {1, 2, 3};
-        switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_I4G_WPB_MULTI,
+        // few workgroups fit a CU; R keeps them all resident, ties going to
+        // the larger R (fewer workgroups staging the vectors).  12288 rows,
+        // two to four vectors: R = 2, 256 workgroups of 48 rows
+        static const int cand[] = {3, 2, 1};
+        switch (pick_rows_per_group(O, i4g_lanes_per_row(I), QG_I4G_WPB_MULTI,
                                     i4g_stream_lds_bytes(S, I), cand, 3)) {
         case 1: return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
         case 2: return launch_stream_r<S, 2>(w, s, x, y, I, O, gs, st);
