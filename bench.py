@@ -87,6 +87,9 @@ class I4G(Case):
     def __init__(self, O, I, gs, torch, q, o, S=1):
         import workloads as W
         self.name = f"i4g_O{O}_I{I}_gs{gs}" + (f"_S{S}" if S > 1 else "")
+        # four vectors in whole 64-column blocks run on the int8 matrix cores
+        if S == 4 and I % 64 == 0 and gs % 64 == 0:
+            self.kernel = "i4g_gemv_mv"
         self.fmt_desc = "grouped int4, f32 scale per group" + (f", {S} vectors per call" if S > 1 else "")
         self.O, self.I, self.gs, self.S = O, I, gs, S
         rb, ng = (I + 1) // 2, (I + gs - 1) // gs
@@ -406,6 +409,7 @@ CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_
 
 KERNEL_SOURCES = {
     "i4g_gemv_stream": "i4g.hip",
+    "i4g_gemv_mv": "i4g.hip",
     "fp8_gemv_stream": "fp8b128.hip",
     "mq4v2_gemv_stream": "mq4v2.hip",
     "moe_i4g_stream": "moe.hip",

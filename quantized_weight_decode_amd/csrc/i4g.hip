@@ -277,7 +277,7 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
 // ---------------------------------------------------------------------------
 // Four vectors on the int8 matrix cores.  With several vectors the
 // per-vector digit products of the streaming kernel make it VALU-bound (four
-// vectors at 12288 x 6144: 2.4x the one-vector time), while the same
+// vectors at 12288 x 6144: twice the one-vector time), while the same
 // products are a skinny dense contraction: 16 rows x 64 columns of nibbles
 // (A, unsigned 0..15 as int8) times 64 columns x 16 (vector, digit) pairs of
 // activation digits (B) per v_mfma_i32_16x16x64_i8.
