@@ -90,7 +90,8 @@ class I4G(Case):
         # four vectors in whole 64-column blocks run on the int8 matrix cores
         if S == 4 and I % 64 == 0 and gs % 64 == 0:
             self.kernel = "i4g_gemv_mv"
-        self.fmt_desc = "grouped int4, f32 scale per group" + (f", {S} vectors per call" if S > 1 else "")
+        self.fmt_desc = ("grouped int4, f32 scale per group"
+                         + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.gs, self.S = O, I, gs, S
         rb, ng = (I + 1) // 2, (I + gs - 1) // gs
         self.weight_bytes = O * rb + O * ng * 4
@@ -168,7 +169,8 @@ class FP8(Case):
     def __init__(self, O, I, torch, q, o, S=1):
         import workloads as W
         self.name = f"fp8b128_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = "fp8 e4m3, f32 scale per 128x128 block" + (f", {S} vectors per call" if S > 1 else "")
+        self.fmt_desc = ("fp8 e4m3, f32 scale per 128x128 block"
+                         + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.S = O, I, S
         nbo, nbi = W.fp8_nblocks(O, I)
         self.weight_bytes = O * I + nbo * nbi * 4
@@ -211,7 +213,8 @@ class FP8E8(Case):
     def __init__(self, O, I, torch, q, o, S=1):
         import workloads as W
         self.name = f"fp8ue8m0_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = "fp8 e4m3, UE8M0 scale byte per 128x128 block" + (f", {S} vectors per call" if S > 1 else "")
+        self.fmt_desc = ("fp8 e4m3, UE8M0 scale byte per 128x128 block"
+                         + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.S = O, I, S
         nbo, nbi = W.fp8_nblocks(O, I)
         self.weight_bytes = O * I + nbo * nbi
@@ -261,7 +264,8 @@ class MQ4(Case):
         self.fmt = fmt
         tag, desc = self.FORMATS[fmt]
         self.name = f"{tag}_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = desc + ", FWHT-256 rotated activations" + (f", {S} vectors per call" if S > 1 else "")
+        self.fmt_desc = (desc + ", FWHT-256 rotated activations"
+                         + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.S = O, I, S
         self.weight_bytes = O * (I // 256) * 136
         # up to two vectors: one fused launch (weights, x, signs in; y out),

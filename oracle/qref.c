@@ -384,8 +384,14 @@ static void mq4_group_gemv(const uint8_t *w, const float *x, float *y, int S, in
     }
 }
 
-void qref_mq4v1_dequant(const uint8_t *w, int O, int I, float *W) { mq4_group_dequant(w, O, I, W, 1); }
-void qref_mq4c_dequant(const uint8_t *w, int O, int I, float *W) { mq4_group_dequant(w, O, I, W, 2); }
+void qref_mq4v1_dequant(const uint8_t *w, int O, int I, float *W)
+{
+    mq4_group_dequant(w, O, I, W, 1);
+}
+void qref_mq4c_dequant(const uint8_t *w, int O, int I, float *W)
+{
+    mq4_group_dequant(w, O, I, W, 2);
+}
 void qref_mq4v1_gemv(const uint8_t *w, const float *x, float *y, int S, int I, int O,
                      const int *rows, int nrows)
 {

@@ -34,7 +34,8 @@ int cu_count()
     auto it = cus.find(dev);
     if (it != cus.end()) return it->second;
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
         n = 256;
     cus[dev] = n;
     return n;

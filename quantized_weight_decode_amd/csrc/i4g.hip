@@ -331,7 +331,7 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NKB = I / 64;
     u32x4 *bl = reinterpret_cast<u32x4 *>(lds_raw);                      // [NKB][64] B operands
-    int2 *ml = reinterpret_cast<int2 *>(bl + (size_t)NKB * 64);          // [NKB][16] (8 sum d, scale)
+    int2 *ml = reinterpret_cast<int2 *>(bl + (size_t)NKB * 64);          // [NKB][16] (8 sum d, c)
     float *red = reinterpret_cast<float *>(ml + (size_t)NKB * 16);       // [MV_WPB][4][16]
     int *wflag = reinterpret_cast<int *>(red + MV_WPB * 64);             // [16]
     unsigned char *wls = reinterpret_cast<unsigned char *>(wflag + 16);  // [MV_WPB][MV_WL]
@@ -449,7 +449,8 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
             sum = quad_sum_i32(sum);
             sum += __builtin_amdgcn_update_dpp(0, sum, 0x141, 0xF, 0xF, false);
             if (m == 0)
-                mm[d] = int2{8 * sum, (int)((e - 21u + 8u * (uint32_t)d) << 23)};   // 2^(E-22) 256^d
+                // scale 2^(E - 22) 256^d as f32 bits
+                mm[d] = int2{8 * sum, (int)((e - 21u + 8u * (uint32_t)d) << 23)};
         }
         *dst(3) = uint2{0u, 0u};   // column 4t + 3
         if (m == 0) mm[3] = int2{0, 0x3F800000};
@@ -487,8 +488,10 @@ __global__ __launch_bounds__(64 * MV_WPB) void i4g_gemv_mv(
                         const int kb = kb0 + i;
                         const u32x2 wv = *reinterpret_cast<const u32x2 *>(wl + j * MV_RS + p * 32 +
                                                                           8 * g);
-                        const i32x4 a = {(int)(wv.x & 0x0F0F0F0Fu), (int)((wv.x >> 4) & 0x0F0F0F0Fu),
-                                         (int)(wv.y & 0x0F0F0F0Fu), (int)((wv.y >> 4) & 0x0F0F0F0Fu)};
+                        const i32x4 a = {(int)(wv.x & 0x0F0F0F0Fu),
+                                         (int)((wv.x >> 4) & 0x0F0F0F0Fu),
+                                         (int)(wv.y & 0x0F0F0F0Fu),
+                                         (int)((wv.y >> 4) & 0x0F0F0F0Fu)};
                         const u32x4 bu = bl[(size_t)kb * 64 + 16 * g + (j ^ ((kb * 4 + g) & 15))];
                         const i32x4 b = {(int)bu.x, (int)bu.y, (int)bu.z, (int)bu.w};
                         const int2 mm = ml[(size_t)kb * 16 + j];

@@ -457,11 +457,21 @@ hipError_t launch_moe_topk(const void *w, const float *scales, long long w_strid
                       ((uintptr_t)x & 15) == 0 && moe_lds_bytes(K, I, RT) <= LDS_BUDGET;
     if (fast) {
         switch (lpr) {
-        case 64: return launch_t<64, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
-        case 32: return launch_t<32, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
-        case 16: return launch_t<16, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
-        case 8: return launch_t<8, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
-        default: return launch_t<4, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err_flag, st);
+        case 64:
+            return launch_t<64, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
+                                          y, I, O, gs, RT, NB, err_flag, st);
+        case 32:
+            return launch_t<32, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
+                                          y, I, O, gs, RT, NB, err_flag, st);
+        case 16:
+            return launch_t<16, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
+                                          y, I, O, gs, RT, NB, err_flag, st);
+        case 8:
+            return launch_t<8, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
+                                          y, I, O, gs, RT, NB, err_flag, st);
+        default:
+            return launch_t<4, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
+                                         I, O, gs, RT, NB, err_flag, st);
         }
     }
     const int wpb = 4;

@@ -81,9 +81,10 @@ __device__ __forceinline__ float mq4_chunk_plain(const u32x4 wv, float scl, floa
         nib8(wv[d], e, o);
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            acc = __builtin_fmaf(__builtin_fmaf(e[k] * NIB_XSCALE, scl, zro), x32[8 * d + 2 * k], acc);
-            acc = __builtin_fmaf(__builtin_fmaf(o[k] * NIB_XSCALE, scl, zro), x32[8 * d + 2 * k + 1],
-                                 acc);
+            const float we = __builtin_fmaf(e[k] * NIB_XSCALE, scl, zro);
+            const float wo = __builtin_fmaf(o[k] * NIB_XSCALE, scl, zro);
+            acc = __builtin_fmaf(we, x32[8 * d + 2 * k], acc);
+            acc = __builtin_fmaf(wo, x32[8 * d + 2 * k + 1], acc);
         }
     }
     return acc;

@@ -261,7 +261,8 @@ __device__ __forceinline__ float lane_xor(float v)
     int r;
     if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);
     else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);
-    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);  // row_ror:8
+    // M == 8: row_ror:8
+    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);
     else r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (M << 10));   // xor M within 32 lanes
     return __builtin_bit_cast(float, r);
 }
@@ -374,7 +375,8 @@ struct XStageQ {
             const int g = stage_index(f, items, rot);
             u32x2 sv = {0, 0};
             if constexpr (ROT)
-                sv = *reinterpret_cast<const u32x2 *>(signs + 8u * ((uint32_t)g % (uint32_t)(NU * 4)));
+                sv = *reinterpret_cast<const u32x2 *>(signs +
+                                                      8u * ((uint32_t)g % (uint32_t)(NU * 4)));
             bad |= put(ldx4(x, 2u * (uint32_t)g), ldx4(x, 2u * (uint32_t)g + 1u), sv, g, NU, xq,
                        xc, xsum);
         }
@@ -383,8 +385,8 @@ struct XStageQ {
 
     // ROT only: writes the rotated vectors as f32, xf[t][I] = x_rot (the
     // stand-alone kernel's values to the bit), for the per-element fallback.
-    __device__ __forceinline__ void store_rotated_f32(const float *__restrict__ x, int items, int NU,
-                                                      const int8_t *__restrict__ signs,
+    __device__ __forceinline__ void store_rotated_f32(const float *__restrict__ x, int items,
+                                                      int NU, const int8_t *__restrict__ signs,
                                                       float *__restrict__ xf)
     {
         const int ipv = NU * 4;
