@@ -519,8 +519,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(how the path would shard across GPUs is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported (across GPUs "
+              f"the dense GEMVs would split by output rows and the routed experts by expert, "
+              f"each GPU running these kernels on its share)", file=sys.stderr)
         sys.exit(2)
 
     import torch
