@@ -1,48 +1,47 @@
 #!/usr/bin/env python3
 """Batch-1 quantized-weight GEMV benchmark on one MI355X.
 
-A step is one pass of the hot path over one batch of synthetic input:
+The default run measures every workload in one process and prints one JSON
+line.  Its headline (`value`, `ms_per_step`, `roofline`) is the largest
+batch-1 dense GEMV, fp8-e4m3 with 128x128 block scales at 7168 x 16384
+(117.6 MB per call); a step is one qgemv_fp8b128 call.  The key `configs`
+holds every workload (the headline's included), each with its time per
+launch, algorithmic bytes, roofline fraction, the plain-read ceiling of the
+same bytes, HBM traffic from the committed counter profiles and the CPU
+oracle's rate; `host` records the machine and the build.
 
-  i4g_O12288_I6144_gs64 (default), i4g_O12288_I6144_gs128:
-      one qgemv_i4g call (grouped int4, one activation vector)
-  i4g_O12288_I6144_gs64_S2, _S4, fp8b128_O7168_I16384_S2, _S4,
-  mq4v2_O8192_I8192_S2, _S4:
-      the same step on 2 or 4 activation vectors per call (multi-token decode)
-  fp8b128_O7168_I16384:
-      one qgemv_fp8b128 call
-  mq4v1_O8192_I8192, mq4c_O8192_I8192:
-      qgemv_fwht256 then qgemv_mq4v1 / qgemv_mq4c (MQ4 v1 and the MQ4C pad
-      form on the same shape)
-  fp8ue8m0_O7168_I16384:
-      one qgemv_fp8b128_ue8m0 call (the same weights with power-of-two
-      UE8M0 block scale bytes)
-  mq4v2_O8192_I8192:
-      one qgemv_mq4v2_rot call (the FWHT-256 rotation of x fused into the
-      GEMV; the same result as qgemv_fwht256 followed by qgemv_mq4v2), also
-      for _S2; the _S4 step calls qgemv_fwht256 then qgemv_mq4v2
-  moe_E256_O2048_I7168_gs64_T4_K8:
-      one qgemv_moe_topk call (4 tokens, top-8 of 256 experts)
-  i4g_prefill_O12288_I6144_gs64_S256, _S2048:
-      one qgemv_i4g_prefill call (256 or 2048 prompt tokens through the
-      grouped-int4 matrix on f32 MFMA; its roofline is the matrix cores')
+Workloads (one launch per step each):
+  i4g_O256_I512_gs64           grouped int4, the small parity shape
+  i4g_O12288_I6144_gs64        grouped int4 at the resident-projection shape
+  i4g_O12288_I6144_gs128       the same with groups of 128
+  fp8b128_O7168_I16384         fp8-e4m3, f32 scale per 128x128 block (headline)
+  mq4v2_O8192_I8192            MQ4-v2 GEMV on activations already rotated
+  mq4v2rot_O8192_I8192         MQ4-v2 with the FWHT-256 rotation fused in
+  moe_E256_O2048_I7168_gs64_T4_K8  routed experts: 4 tokens, top-8 of 256
+`--case NAME` runs one of these (or a multi-vector / other-format variant)
+alone.
 
 Dense steps rotate through distinct weight copies totalling over 1 GiB, and
-the routed-expert step cycles through 16 seeded routings over one resident
-2.1 GB expert stack, so calls stream their weights from HBM rather than the
-256 MB last-level cache.  All inputs are resident in HBM before timing.
+the routed-expert step cycles through 16 routings in which each call's
+experts are disjoint from the previous call's, so calls stream their weights
+from HBM rather than the 256 MB last-level cache.  All inputs are resident in
+HBM before timing.  Each workload is warmed up for a fixed time (the GPU
+reaches steady clocks only after some milliseconds of load) on top of
+--warmup steps; then the headline times exactly --steps steps between two HIP
+events on the launch stream, and every workload is timed in three
+interleaved runs of max(--steps, 100) launches (median reported).
 
-Prints one JSON line.  `value` is the algorithmic bytes of K steps divided by
-the time between two HIP events bracketing them on the launch stream;
-`roofline.achieved` is the same for the step's kernel launches (one launch
-per vector group, except the rotation launch of the multi-vector MQ4 steps).
-`--copy-calibrate` instead runs a plain device-to-device copy of known size
-(used to scale the HBM traffic counters).
+`--copy-calibrate BYTES` instead times a plain device-to-device copy of known
+size (used to scale the HBM traffic counters).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -55,21 +54,19 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F32_PEAK_TFS = 157.3   # dense f32 matrix-core peak
 DENSE_27B = 27e9   # weights of the dense decode fixture the tok/s figure is scaled to
 ROTATE_BYTES = 1 << 30
+WARM_SECONDS = 0.25   # per workload, before its --warmup steps
+RUNS = 3
 METRIC = "achieved HBM GB/s (% of MI355X peak) + equiv decode tok/s, batch-1 qGEMV"
+HEADLINE = "fp8b128_O7168_I16384"
+SUITE = ["i4g_O256_I512_gs64", "i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128",
+         "fp8b128_O7168_I16384", "mq4v2_O8192_I8192", "mq4v2rot_O8192_I8192",
+         "moe_E256_O2048_I7168_gs64_T4_K8"]
+DTYPE_4BIT = ("f32 accumulate; x as a 22-bit shared-exponent fixed point per 32 columns, "
+              "exact integer nibble x digit products")
 
 
 def n_copies(bytes_per_copy):
     return max(2, int(np.ceil(ROTATE_BYTES / bytes_per_copy)))
-
-
-class Case:
-    """A workload: builds device inputs, runs one step, checks parity."""
-    name = ""
-    kernel = ""            # name fragment of the dominant kernel
-    fmt_desc = ""
-
-    def step(self, i):
-        raise NotImplementedError
 
 
 def _check(rel, what):
@@ -81,15 +78,37 @@ def _rel(got, ref):
     return float(np.linalg.norm(got.astype(np.float64) - ref) / np.linalg.norm(ref))
 
 
+class Case:
+    """A workload: device inputs, one step (one launch), parity, CPU sample."""
+    name = ""
+    kernel = ""            # name fragment of the step's kernel
+    fmt_desc = ""
+    dtype = "f32"
+    bound = "hbm"
+    S = 1
+    ceiling_pattern = 0    # plain-read pattern of the same bytes (1: MQ4 groups)
+
+    def step(self, i):
+        raise NotImplementedError
+
+    def bytes_for(self, first, k):
+        return self.alg_bytes * k
+
+    def ceiling_bytes(self):
+        return int(self.alg_bytes) // 16 * 16
+
+    def cpu_call(self, rows):
+        """The oracle on output rows `rows` (None: all); returns its bytes of work."""
+        raise NotImplementedError
+
+
 class I4G(Case):
     kernel = "i4g_gemv_stream"
+    dtype = DTYPE_4BIT
 
     def __init__(self, O, I, gs, torch, q, o, S=1):
         import workloads as W
         self.name = f"i4g_O{O}_I{I}_gs{gs}" + (f"_S{S}" if S > 1 else "")
-        # four vectors in whole 64-column blocks run on the int8 matrix cores
-        if S == 4 and I % 64 == 0 and gs % 64 == 0:
-            self.kernel = "i4g_gemv_mv"
         self.fmt_desc = ("grouped int4, f32 scale per group"
                          + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.gs, self.S = O, I, gs, S
@@ -102,20 +121,22 @@ class I4G(Case):
         self.n = n_copies(self.weight_bytes)
         g = torch.Generator(device=dev)
         g.manual_seed(1)
-        self.ws = [torch.from_numpy(d["w"]).to(dev)]
-        self.ss = [torch.from_numpy(d["scales"]).to(dev)]
-        for _ in range(1, self.n):
-            self.ws.append(torch.randint(0, 256, d["w"].shape, dtype=torch.uint8, device=dev,
-                                         generator=g))
-            self.ss.append(0.002 + 0.018 * torch.rand(d["scales"].shape, device=dev, generator=g))
+        # copy 0 is the seeded workload; the others are drawn with the same laws
+        # (one batched tensor each, so the copies cost a few launches)
+        wall = torch.randint(0, 256, (self.n - 1, *d["w"].shape), dtype=torch.uint8, device=dev,
+                             generator=g)
+        sall = 0.002 + 0.018 * torch.rand((self.n - 1, *d["scales"].shape), device=dev,
+                                          generator=g)
+        self.ws = [torch.from_numpy(d["w"]).to(dev)] + list(wall.unbind(0))
+        self.ss = [torch.from_numpy(d["scales"]).to(dev)] + list(sall.unbind(0))
         self.x = torch.from_numpy(d["x"]).to(dev)
         self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
+        self.d, self.o = d, o
         self.step(0)
         self.rel = _rel(self.y.cpu().numpy(), o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
         _check(self.rel, self.name)
-        self.cpu = lambda: o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs)
 
     def step(self, i):
         wp, spp = self.ptrs[i % self.n]
@@ -123,6 +144,11 @@ class I4G(Case):
                               self.O, self.gs, self.sp)
         if st:
             raise SystemExit(f"qgemv_i4g: {self.q.strerror(st)}")
+
+    def cpu_call(self, rows):
+        d = self.d
+        self.o.i4g_gemv(d["w"], d["scales"], d["x"], self.O, self.I, self.gs, rows=rows)
+        return self.alg_bytes * (1.0 if rows is None else len(rows) / self.O)
 
 
 class Prefill(Case):
@@ -148,13 +174,12 @@ class Prefill(Case):
         self.x = torch.from_numpy(d["x"]).to(dev)
         self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.d, self.o = d, o
         self.step(0)
         rows = np.arange(0, O, 97)
         self.rel = _rel(self.y.cpu().numpy()[:, rows],
                         o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs, rows=rows))
         _check(self.rel, self.name)
-        self.cpu_frac = len(rows) / O
-        self.cpu = lambda: o.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs, rows=rows)
 
     def step(self, i):
         st = self.q.qgemv_i4g_prefill(self.w.data_ptr(), self.s.data_ptr(), self.x.data_ptr(),
@@ -162,96 +187,77 @@ class Prefill(Case):
         if st:
             raise SystemExit(f"qgemv_i4g_prefill: {self.q.strerror(st)}")
 
+    def cpu_call(self, rows):
+        d = self.d
+        self.o.i4g_gemv(d["w"], d["scales"], d["x"], self.O, self.I, self.gs, rows=rows)
+        return self.alg_bytes * (1.0 if rows is None else len(rows) / self.O)
+
 
 class FP8(Case):
     kernel = "fp8_gemv_stream"
 
-    def __init__(self, O, I, torch, q, o, S=1):
+    def __init__(self, O, I, torch, q, o, S=1, ue8m0=False):
         import workloads as W
-        self.name = f"fp8b128_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = ("fp8 e4m3, f32 scale per 128x128 block"
-                         + (f", {S} vectors per call" if S > 1 else ""))
+        self.ue8m0 = ue8m0
+        self.name = (f"fp8ue8m0_O{O}_I{I}" if ue8m0 else f"fp8b128_O{O}_I{I}") + \
+            (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = ("fp8 e4m3, " + ("UE8M0 scale byte" if ue8m0 else "f32 scale")
+                         + " per 128x128 block" + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.S = O, I, S
         nbo, nbi = W.fp8_nblocks(O, I)
-        self.weight_bytes = O * I + nbo * nbi * 4
+        self.weight_bytes = O * I + nbo * nbi * (1 if ue8m0 else 4)
         self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4)
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
-        d = W.gen_fp8b128(O, I, S=S, seed=0)
+        d = (W.gen_fp8ue8m0 if ue8m0 else W.gen_fp8b128)(O, I, S=S, seed=0)
+        skey = "scale_e8m0" if ue8m0 else "scale_inv"
         self.n = n_copies(self.weight_bytes)
         g = torch.Generator(device=dev)
         g.manual_seed(1)
-        self.ws = [torch.from_numpy(d["w"]).to(dev)]
-        self.ss = [torch.from_numpy(d["scale_inv"]).to(dev)]
-        for _ in range(1, self.n):
-            # uniform over the 254 non-NaN codes: v in 0..253 -> v + (v >= 0x7F)
-            v = torch.randint(0, 254, (O, I), dtype=torch.uint8, device=dev, generator=g)
-            self.ws.append(v + (v >= 0x7F).to(torch.uint8))
-            self.ss.append(torch.exp(np.log(1e-4) + (np.log(1e-2) - np.log(1e-4)) *
-                                     torch.rand((nbo, nbi), device=dev, generator=g)))
+        # uniform over the 254 non-NaN codes: v in 0..253 -> v + (v >= 0x7F)
+        v = torch.randint(0, 254, (self.n - 1, O, I), dtype=torch.uint8, device=dev, generator=g)
+        v += (v >= 0x7F).to(torch.uint8)
+        if ue8m0:
+            sall = torch.randint(114, 121, (self.n - 1, nbo, nbi), dtype=torch.uint8, device=dev,
+                                 generator=g)
+        else:
+            sall = torch.exp(np.log(1e-4) + (np.log(1e-2) - np.log(1e-4)) *
+                             torch.rand((self.n - 1, nbo, nbi), device=dev, generator=g))
+        self.ws = [torch.from_numpy(d["w"]).to(dev)] + list(v.unbind(0))
+        self.ss = [torch.from_numpy(d[skey]).to(dev)] + list(sall.unbind(0))
         self.x = torch.from_numpy(d["x"]).to(dev)
         self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
+        self.d, self.o, self.skey = d, o, skey
         self.step(0)
-        self.rel = _rel(self.y.cpu().numpy(), o.fp8b128_gemv(d["w"], d["scale_inv"], d["x"], O, I))
+        self.rel = _rel(self.y.cpu().numpy(), self._ref(None))
         _check(self.rel, self.name)
-        self.cpu = lambda: o.fp8b128_gemv(d["w"], d["scale_inv"], d["x"], O, I)
+
+    def _ref(self, rows):
+        d = self.d
+        fn = self.o.fp8ue8m0_gemv if self.ue8m0 else self.o.fp8b128_gemv
+        return fn(d["w"], d[self.skey], d["x"], self.O, self.I, rows=rows)
 
     def step(self, i):
         wp, spp = self.ptrs[i % self.n]
-        st = self.q.qgemv_fp8b128(wp, spp, self.x.data_ptr(), self.y.data_ptr(), self.S, self.I,
-                                  self.O, self.sp)
+        fn = self.q.qgemv_fp8b128_ue8m0 if self.ue8m0 else self.q.qgemv_fp8b128
+        st = fn(wp, spp, self.x.data_ptr(), self.y.data_ptr(), self.S, self.I, self.O, self.sp)
         if st:
-            raise SystemExit(f"qgemv_fp8b128: {self.q.strerror(st)}")
+            raise SystemExit(f"fp8 GEMV: {self.q.strerror(st)}")
 
-
-class FP8E8(Case):
-    """fp8-e4m3 with UE8M0 (one power-of-two byte per 128x128 block) scales."""
-    kernel = "fp8_gemv_stream"
-
-    def __init__(self, O, I, torch, q, o, S=1):
-        import workloads as W
-        self.name = f"fp8ue8m0_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = ("fp8 e4m3, UE8M0 scale byte per 128x128 block"
-                         + (f", {S} vectors per call" if S > 1 else ""))
-        self.O, self.I, self.S = O, I, S
-        nbo, nbi = W.fp8_nblocks(O, I)
-        self.weight_bytes = O * I + nbo * nbi
-        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4)
-        self.bytes_per_weight = self.weight_bytes / (O * I)
-        dev = torch.device("cuda:0")
-        d = W.gen_fp8ue8m0(O, I, S=S, seed=0)
-        self.n = n_copies(self.weight_bytes)
-        g = torch.Generator(device=dev)
-        g.manual_seed(1)
-        self.ws = [torch.from_numpy(d["w"]).to(dev)]
-        self.ss = [torch.from_numpy(d["scale_e8m0"]).to(dev)]
-        for _ in range(1, self.n):
-            v = torch.randint(0, 254, (O, I), dtype=torch.uint8, device=dev, generator=g)
-            self.ws.append(v + (v >= 0x7F).to(torch.uint8))
-            self.ss.append(torch.randint(114, 121, (nbo, nbi), dtype=torch.uint8, device=dev,
-                                         generator=g))
-        self.x = torch.from_numpy(d["x"]).to(dev)
-        self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
-        self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
-        self.ptrs = [(w.data_ptr(), s.data_ptr()) for w, s in zip(self.ws, self.ss)]
-        self.step(0)
-        ref = o.fp8ue8m0_gemv(d["w"], d["scale_e8m0"], d["x"], O, I)
-        self.rel = _rel(self.y.cpu().numpy(), ref)
-        _check(self.rel, self.name)
-        self.cpu = lambda: o.fp8ue8m0_gemv(d["w"], d["scale_e8m0"], d["x"], O, I)
-
-    def step(self, i):
-        wp, spp = self.ptrs[i % self.n]
-        st = self.q.qgemv_fp8b128_ue8m0(wp, spp, self.x.data_ptr(), self.y.data_ptr(), self.S,
-                                        self.I, self.O, self.sp)
-        if st:
-            raise SystemExit(f"qgemv_fp8b128_ue8m0: {self.q.strerror(st)}")
+    def cpu_call(self, rows):
+        self._ref(rows)
+        return self.alg_bytes * (1.0 if rows is None else len(rows) / self.O)
 
 
 class MQ4(Case):
+    """MQ4 GEMV.  rot=False: qgemv_mq4v2 (or v1 / MQ4C) on activations rotated
+    beforehand (outside the timed region), the GEMV alone; rot=True:
+    qgemv_mq4v2_rot, the rotation fused into the GEMV's staging."""
     kernel = "mq4v2_gemv_stream"
+    dtype = DTYPE_4BIT
+    ceiling_pattern = 1
 
     FORMATS = {
         "v2": ("mq4v2", "MQ4-v2 136 B / 256 weights (fp16 scale+zero per 128)"),
@@ -259,23 +265,18 @@ class MQ4(Case):
         "c": ("mq4c", "MQ4C pad 136 B / 256 weights (fp16 scale+zero per 256)"),
     }
 
-    def __init__(self, O, I, torch, q, o, S=1, fmt="v2"):
+    def __init__(self, O, I, torch, q, o, S=1, fmt="v2", rot=False):
         import workloads as W
-        self.fmt = fmt
+        self.fmt, self.rot = fmt, rot
         tag, desc = self.FORMATS[fmt]
-        self.name = f"{tag}_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
-        self.fmt_desc = (desc + ", FWHT-256 rotated activations"
+        self.name = f"{tag}{'rot' if rot else ''}_O{O}_I{I}" + (f"_S{S}" if S > 1 else "")
+        self.fmt_desc = (desc + (", FWHT-256 rotation of x fused in" if rot else
+                                 ", activations FWHT-256 rotated beforehand")
                          + (f", {S} vectors per call" if S > 1 else ""))
         self.O, self.I, self.S = O, I, S
         self.weight_bytes = O * (I // 256) * 136
-        # up to two vectors: one fused launch (weights, x, signs in; y out),
-        # the rotated activations never leave the chip.  Four: the rotation
-        # kernel (x, signs in; x_rot out) then the GEMV (weights, x_rot in;
-        # y out) -- every workgroup of the fused kernel rotates all S
-        # vectors, which at S = 4 costs more than the extra launch
-        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4) + I
-        if S > 2 or fmt != "v2":
-            self.alg_bytes += S * I * 8
+        # GEMV alone: weights, x_rot in, y out; fused: weights, x, signs in, y out
+        self.alg_bytes = self.weight_bytes + S * (I * 4 + O * 4) + (I if rot else 0)
         self.bytes_per_weight = self.weight_bytes / (O * I)
         dev = torch.device("cuda:0")
         d = {"v2": W.gen_mq4v2, "v1": W.gen_mq4v1, "c": W.gen_mq4c}[fmt](O, I, S=S, seed=0)
@@ -283,48 +284,58 @@ class MQ4(Case):
         g = torch.Generator(device=dev)
         g.manual_seed(1)
         w0 = torch.from_numpy(d["w"].reshape(O, -1)).to(dev)
-        self.ws = [w0]
-        for _ in range(1, self.n):
-            # another draw: fresh payload, headers from copy 0 with their
-            # scale/zero halves re-paired at random (same value ranges)
-            w = w0.clone()
-            pay = torch.randint(0, 256, (O, I // 256, 128), dtype=torch.uint8, device=dev,
-                                generator=g)
-            w.view(O, I // 256, 136)[:, :, 8:] = pay
-            perm = torch.randperm(O, device=dev, generator=g)
-            w.view(O, I // 256, 136)[:, :, :8] = w0.view(O, I // 256, 136)[perm, :, :8]
-            self.ws.append(w)
+        # the other copies: fresh payload, headers from copy 0 with their rows
+        # re-paired at random (same value ranges)
+        G = I // 256
+        wall = torch.empty((self.n - 1, O, G, 136), dtype=torch.uint8, device=dev)
+        wall[..., 8:] = torch.randint(0, 256, (self.n - 1, O, G, 128), dtype=torch.uint8,
+                                      device=dev, generator=g)
+        perm = torch.randint(0, O, (self.n - 1, O), device=dev, generator=g)
+        wall[..., :8] = w0.view(O, G, 136)[perm, :, :8]
+        self.ws = [w0] + [c.view(O, G * 136) for c in wall.unbind(0)]
         self.x = torch.from_numpy(d["x"]).to(dev)
         self.signs = torch.from_numpy(d["signs"]).to(dev)
         self.xr = torch.empty_like(self.x)
+        st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(), S, I,
+                             torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise SystemExit(f"qgemv_fwht256: {q.strerror(st)}")
         self.y = torch.empty((S, O), dtype=torch.float32, device=dev)
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
         self.ptrs = [w.data_ptr() for w in self.ws]
+        self.d, self.o = d, o
+        self.ref_fn = {"v2": o.mq4v2_gemv, "v1": o.mq4v1_gemv, "c": o.mq4c_gemv}[fmt]
+        self.xrot_ref = o.fwht256(d["x"], d["signs"], I)
         self.step(0)
-        ref_fn = {"v2": o.mq4v2_gemv, "v1": o.mq4v1_gemv, "c": o.mq4c_gemv}[fmt]
-        ref = ref_fn(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
-        self.rel = _rel(self.y.cpu().numpy(), ref)
+        self.rel = _rel(self.y.cpu().numpy(), self.ref_fn(d["w"], self.xrot_ref, O, I))
         _check(self.rel, self.name)
-        self.cpu = lambda: ref_fn(d["w"], o.fwht256(d["x"], d["signs"], I), O, I)
 
     def step(self, i):
         q = self.q
-        if self.S <= 2 and self.fmt == "v2":
+        if self.rot:
             st = q.qgemv_mq4v2_rot(self.ptrs[i % self.n], self.x.data_ptr(),
                                    self.signs.data_ptr(), self.y.data_ptr(), self.S, self.I,
                                    self.O, self.sp)
         else:
-            st = q.qgemv_fwht256(self.x.data_ptr(), self.signs.data_ptr(), self.xr.data_ptr(),
-                                 self.S, self.I, self.sp)
             gemv = {"v2": q.qgemv_mq4v2, "v1": q.qgemv_mq4v1, "c": q.qgemv_mq4c}[self.fmt]
-            st = st or gemv(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), self.S,
-                            self.I, self.O, self.sp)
+            st = gemv(self.ptrs[i % self.n], self.xr.data_ptr(), self.y.data_ptr(), self.S,
+                      self.I, self.O, self.sp)
         if st:
-            raise SystemExit(f"mq4v2 step: {q.strerror(st)}")
+            raise SystemExit(f"mq4 step: {q.strerror(st)}")
+
+    def ceiling_bytes(self):
+        return self.weight_bytes
+
+    def cpu_call(self, rows):
+        d = self.d
+        xr = self.o.fwht256(d["x"], d["signs"], self.I) if self.rot else self.xrot_ref
+        self.ref_fn(d["w"], xr, self.O, self.I, rows=rows)
+        return self.alg_bytes * (1.0 if rows is None else len(rows) / self.O)
 
 
 class MoE(Case):
     kernel = "moe_i4g_stream"
+    dtype = DTYPE_4BIT
     N_ROUTINGS = 16
 
     def __init__(self, E, O, I, gs, T, K, torch, q, o):
@@ -332,6 +343,7 @@ class MoE(Case):
         self.name = f"moe_E{E}_O{O}_I{I}_gs{gs}_T{T}_K{K}"
         self.fmt_desc = "routed grouped-int4 experts, gate-weighted top-k sum"
         self.E, self.O, self.I, self.gs, self.T, self.K = E, O, I, gs, T, K
+        self.S = T
         rb, ng = (I + 1) // 2, (I + gs - 1) // gs
         self.expert_bytes = O * rb + O * ng * 4
         self.bytes_per_weight = self.expert_bytes / (O * I)
@@ -342,26 +354,20 @@ class MoE(Case):
         self.x = torch.from_numpy(d["x"]).to(dev)
         self.y = torch.empty((T, O), dtype=torch.float32, device=dev)
         self.ws_buf = q.moe_topk_workspace(T, K, O, dev)
-        self.routings = []
-        uniq = []
-        for r in range(self.N_ROUTINGS):
-            ids, gates = (d["ids"], d["gates"]) if r == 0 else W.gen_moe_routing(E, T, K, 1000 + r)
-            self.routings.append((torch.from_numpy(ids).to(dev), torch.from_numpy(gates).to(dev)))
-            uniq.append(len(np.unique(ids)))
-        self.uniq = uniq
+        routings = W.gen_moe_routings_disjoint(E, T, K, self.N_ROUTINGS, (d["ids"], d["gates"]))
+        self.routings = [(torch.from_numpy(i).to(dev), torch.from_numpy(g).to(dev))
+                         for i, g in routings]
+        self.uniq = [len(np.unique(i)) for i, _ in routings]
         small = T * I * 4 + T * O * 4 + T * K * 8
-        self.alg_bytes_per_routing = [u * self.expert_bytes + small for u in uniq]
+        self.alg_bytes_per_routing = [u * self.expert_bytes + small for u in self.uniq]
         self.alg_bytes = float(np.mean(self.alg_bytes_per_routing))
-        self.weight_bytes = float(np.mean(uniq)) * self.expert_bytes
+        self.weight_bytes = float(np.mean(self.uniq)) * self.expert_bytes
         self.q, self.sp = q, torch.cuda.current_stream().cuda_stream
+        self.d, self.o = d, o
         self.step(0)
-        rows = np.random.default_rng(0).choice(O, 64, replace=False)
-        ref = o.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], E, O, I, gs, rows=rows)
-        self.rel = _rel(self.y.cpu().numpy()[:, rows], ref)
+        ref = o.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], E, O, I, gs)
+        self.rel = _rel(self.y.cpu().numpy(), ref)
         _check(self.rel, self.name)
-        self.cpu_rows = rows
-        self.cpu = lambda: o.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], E, O, I,
-                                     gs, rows=rows)
 
     def step(self, i):
         ids, gates = self.routings[i % self.N_ROUTINGS]
@@ -377,80 +383,130 @@ class MoE(Case):
         n = self.N_ROUTINGS
         return sum(self.alg_bytes_per_routing[(first + i) % n] for i in range(k))
 
+    def cpu_call(self, rows):
+        d = self.d
+        self.o.moe_i4g(d["w"], d["scales"], d["ids"], d["gates"], d["x"], self.E, self.O,
+                       self.I, self.gs, rows=rows)
+        return self.alg_bytes_per_routing[0] * (1.0 if rows is None else len(rows) / self.O)
+
+
+class ReadCeiling(Case):
+    """The plain-read reference of a byte count (libqgemv_ceiling.so) as a case
+    of its own, for profiling: `read_<bytes>` contiguous, `read_<bytes>_mq4` in
+    the MQ4 group pattern; the tile is the fastest of the swept shapes."""
+    kernel = "read_stream"
+    dtype = "u8 (no arithmetic)"
+
+    def __init__(self, name, torch):
+        parts = name.split("_")
+        nbytes, pattern = int(parts[1]), 1 if name.endswith("_mq4") else 0
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        self.cl = Ceiling(torch, load_ceiling_lib(), nbytes, pattern, cus)
+        self.cl.pick(torch)
+        self.name = name
+        self.fmt_desc = f"plain streaming read, tile {self.cl.v}"
+        self.O = 1
+        self.alg_bytes = self.weight_bytes = self.cl.nbytes
+        self.bytes_per_weight = 1.0
+        self.ceiling_pattern = pattern
+        self.rel = 0.0
+
+    def step(self, i):
+        self.cl.step(i)
+
 
 def build_case(name, torch, q, o):
+    if name.startswith("read_"):
+        return ReadCeiling(name, torch)
     table = {
+        "i4g_O256_I512_gs64": lambda: I4G(256, 512, 64, torch, q, o),
         "i4g_O12288_I6144_gs64": lambda: I4G(12288, 6144, 64, torch, q, o),
         "i4g_O12288_I6144_gs128": lambda: I4G(12288, 6144, 128, torch, q, o),
         "fp8b128_O7168_I16384": lambda: FP8(7168, 16384, torch, q, o),
         "mq4v2_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o),
+        "mq4v2rot_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o, rot=True),
         "moe_E256_O2048_I7168_gs64_T4_K8": lambda: MoE(256, 2048, 7168, 64, 4, 8, torch, q, o),
-        "i4g_O256_I512_gs64": lambda: I4G(256, 512, 64, torch, q, o),
         "i4g_O12288_I6144_gs64_S2": lambda: I4G(12288, 6144, 64, torch, q, o, S=2),
-        "i4g_prefill_O12288_I6144_gs64_S256": lambda: Prefill(12288, 6144, 64, 256, torch, q, o),
-        "i4g_prefill_O12288_I6144_gs64_S2048": lambda: Prefill(12288, 6144, 64, 2048, torch, q,
-                                                               o),
         "i4g_O12288_I6144_gs64_S4": lambda: I4G(12288, 6144, 64, torch, q, o, S=4),
         "fp8b128_O7168_I16384_S2": lambda: FP8(7168, 16384, torch, q, o, S=2),
         "fp8b128_O7168_I16384_S4": lambda: FP8(7168, 16384, torch, q, o, S=4),
-        "mq4v2_O8192_I8192_S2": lambda: MQ4(8192, 8192, torch, q, o, S=2),
+        "mq4v2rot_O8192_I8192_S2": lambda: MQ4(8192, 8192, torch, q, o, S=2, rot=True),
         "mq4v2_O8192_I8192_S4": lambda: MQ4(8192, 8192, torch, q, o, S=4),
-        "fp8ue8m0_O7168_I16384": lambda: FP8E8(7168, 16384, torch, q, o),
+        "fp8ue8m0_O7168_I16384": lambda: FP8(7168, 16384, torch, q, o, ue8m0=True),
         "mq4v1_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o, fmt="v1"),
         "mq4c_O8192_I8192": lambda: MQ4(8192, 8192, torch, q, o, fmt="c"),
+        "i4g_prefill_O12288_I6144_gs64_S256": lambda: Prefill(12288, 6144, 64, 256, torch, q, o),
+        "i4g_prefill_O12288_I6144_gs64_S2048": lambda: Prefill(12288, 6144, 64, 2048, torch, q,
+                                                               o),
     }
     return table[name]()
 
 
-CASE_NAMES = ["i4g_O12288_I6144_gs64", "i4g_O12288_I6144_gs128", "fp8b128_O7168_I16384",
-              "mq4v2_O8192_I8192", "moe_E256_O2048_I7168_gs64_T4_K8", "i4g_O256_I512_gs64",
-              "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4",
-              "fp8b128_O7168_I16384_S2", "fp8b128_O7168_I16384_S4",
-              "mq4v2_O8192_I8192_S2", "mq4v2_O8192_I8192_S4", "fp8ue8m0_O7168_I16384",
-              "mq4v1_O8192_I8192", "mq4c_O8192_I8192", "i4g_prefill_O12288_I6144_gs64_S256",
-              "i4g_prefill_O12288_I6144_gs64_S2048"]
+CASE_NAMES = SUITE + [n for n in [
+    "i4g_O12288_I6144_gs64_S2", "i4g_O12288_I6144_gs64_S4", "fp8b128_O7168_I16384_S2",
+    "fp8b128_O7168_I16384_S4", "mq4v2rot_O8192_I8192_S2", "mq4v2_O8192_I8192_S4",
+    "fp8ue8m0_O7168_I16384", "mq4v1_O8192_I8192", "mq4c_O8192_I8192",
+    "i4g_prefill_O12288_I6144_gs64_S256", "i4g_prefill_O12288_I6144_gs64_S2048"]] + [
+    # plain-read references of the suite's byte counts (profiling)
+    "read_42541056", "read_40181760", "read_117563392", "read_35651584_mq4",
+    "read_250681344"]
 
 
 KERNEL_SOURCES = {
-    "i4g_gemv_stream": "i4g.hip",
-    "i4g_gemv_mv": "i4g.hip",
-    "fp8_gemv_stream": "fp8b128.hip",
-    "mq4v2_gemv_stream": "mq4v2.hip",
-    "moe_i4g_stream": "moe.hip",
-    "i4g_gemm_mfma": "prefill.hip",
+    "i4g_gemv_stream": "csrc/i4g.hip",
+    "fp8_gemv_stream": "csrc/fp8b128.hip",
+    "mq4v2_gemv_stream": "csrc/mq4v2.hip",
+    "moe_i4g_stream": "csrc/moe.hip",
+    "i4g_gemm_mfma": "csrc/prefill.hip",
+    "read_stream": "bench_csrc/ceiling.hip",
 }
 
 
 def kernel_digest(kernel):
-    """sha256 over the sources that define `kernel` (its file and the shared headers)."""
-    import hashlib
-    csrc = os.path.join(ROOT, "quantized_weight_decode_amd", "csrc")
+    """sha256 over the sources that define `kernel` (its file and, for the
+    library's kernels, the shared device and launch headers)."""
+    pkg = os.path.join(ROOT, "quantized_weight_decode_amd")
+    files = [KERNEL_SOURCES[kernel]]
+    if files[0].startswith("csrc/"):
+        files += ["csrc/qg_device.h", "csrc/qg_launch.h"]
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "qg_device.h", "qg_launch.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+    for f in files:
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
-def profiled_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary of this kernel on this
-    workload, or None when there is none or the kernel's sources changed since."""
+def profile_record(kernel, workload):
+    """From the committed profile summary of this kernel on this workload: the traced
+    average duration (us) and the calibrated HBM bytes per launch.  Each is None when
+    the summary is absent or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
     if not os.path.exists(path):
-        return None
-    digest = traffic = None
+        return None, None
+    digest = traffic = avg = None
+    import re
     with open(path) as fh:
         for line in fh:
             if line.startswith("source digest: sha256:"):
                 digest = line.split(":", 2)[2].strip()
             elif line.startswith("traffic per dispatch"):
                 traffic = int(line.rsplit(":", 1)[1].split()[0])
+            m = re.match(r"^\| `[^`]+` \| (\d+) \| ([0-9.]+) \|", line)
+            if m and avg is None:
+                avg = float(m.group(2))
     if digest != kernel_digest(kernel):
-        return None
-    return traffic
+        return None, None
+    return avg, traffic
+
+
+def profiled_traffic(kernel, workload):
+    return profile_record(kernel, workload)[1]
 
 
 def timed(torch, fn, first, k):
+    """ms for k steps fn(first), ..., fn(first + k - 1) between two HIP events
+    recorded on the launch stream (torch's current stream, which every step
+    passes to the library)."""
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -460,60 +516,207 @@ def timed(torch, fn, first, k):
         fn(first + i)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1)  # ms
+    return e0.elapsed_time(e1)
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The oracle as it stands, on the host's cores (OpenMP over rows)."""
-    import oracle
-    o = oracle.load()
-    cores = min(os.cpu_count() or 1, 16)
-    o.set_threads(cores)
-    case.cpu()  # warm-up
-    n = 0
+def warm(torch, fn, seconds, start=0):
+    """Runs steps for at least `seconds` of wall time; returns the next step index."""
+    i = start
     t0 = time.perf_counter()
     while True:
-        case.cpu()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        for _ in range(32):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+
+
+# ---------------------------------------------------------------------------
+# Plain-read ceiling (libqgemv_ceiling.so, benchmark only)
+# ---------------------------------------------------------------------------
+class Ceiling:
+    """Best plain streaming read of `nbytes` (pattern 0: contiguous 16-byte
+    chunks; 1: the MQ4 136-byte group pattern) over a sweep of tile shapes,
+    rotating through copies totalling over 1 GiB."""
+    # (waves per workgroup, loads in flight per lane, workgroups per CU; 0: one-shot)
+    VARIANTS = [(wpb, u, wpc) for wpb in (4, 8, 16) for u in (2, 4, 8) for wpc in (1, 2)
+                if wpb * wpc <= 16] + [(wpb, u, 0) for wpb in (4, 8, 16) for u in (1, 2, 4)]
+    OUT_LEN = 1 << 20
+
+    def __init__(self, torch, lib, nbytes, pattern, cus):
+        self.lib, self.pattern = lib, pattern
+        unit = 136 if pattern else 16
+        self.nbytes = nbytes // unit * unit
+        stride = (self.nbytes + 4095) // 4096 * 4096
+        self.n = n_copies(stride)
+        dev = torch.device("cuda:0")
+        self.buf = torch.randint(0, 256, (self.n * stride,), dtype=torch.uint8, device=dev)
+        self.ptrs = [self.buf.data_ptr() + i * stride for i in range(self.n)]
+        self.out = torch.empty(self.OUT_LEN, dtype=torch.int32, device=dev)
+        self.sp = torch.cuda.current_stream().cuda_stream
+        self.cus = cus
+        self.v = self.VARIANTS[0]
+        self.name = f"read_{self.nbytes}" + ("_mq4" if pattern else "")
+
+    def step(self, i):
+        wpb, u, wpc = self.v
+        st = self.lib.qgemv_ceiling_read(self.ptrs[i % self.n], self.nbytes, self.pattern, wpb,
+                                         u, self.cus * wpc, self.out.data_ptr(), self.OUT_LEN,
+                                         self.sp)
+        if st:
+            raise SystemExit(f"qgemv_ceiling_read: status {st}")
+
+    def pick(self, torch):
+        best = None
+        for v in self.VARIANTS:
+            self.v = v
+            warm(torch, self.step, 0.02)
+            ms = min(timed(torch, self.step, 0, 40) for _ in range(2))
+            if best is None or ms < best[0]:
+                best = (ms, v)
+        self.v = best[1]
+        return self.v
+
+
+def load_ceiling_lib():
+    import ctypes as C
+    path = os.path.join(ROOT, "quantized_weight_decode_amd", "libqgemv_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built: run quantized_weight_decode_amd.build")
+    L = C.CDLL(path)
+    L.qgemv_ceiling_read.restype = C.c_int
+    L.qgemv_ceiling_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_int, C.c_int,
+                                     C.c_void_p, C.c_size_t, C.c_void_p]
+    return L
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle as it stands)
+# ---------------------------------------------------------------------------
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_rate(case, threads, budget_s):
+    """Oracle throughput (algorithmic GB/s) on `threads` host threads over about
+    budget_s seconds; a row subset of the workload when a whole call would not
+    fit the budget several times."""
+    import oracle
+    o = oracle.load()
+    o.set_threads(threads)
+    try:
+        rows = None
+        O = case.O
+        t0 = time.perf_counter()
+        probe = np.arange(0, O, max(1, O // 64))
+        case.cpu_call(probe)
+        per_row = (time.perf_counter() - t0) / len(probe)
+        if per_row * O > budget_s / 4:
+            nr = max(1, min(O, int(budget_s / 8 / max(per_row, 1e-9))))
+            rows = np.linspace(0, O - 1, nr).astype(np.int64)
+        case.cpu_call(rows)  # warm-up
+        n, done = 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            done += case.cpu_call(rows)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    finally:
+        o.set_threads(1)
+    part = "whole calls" if rows is None else f"calls on {len(rows)} of {O} output rows"
+    return {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} {part} of {case.name} in {el:.2f} s ({el / n * 1e3:.2f} ms each), "
+                      f"f64 accumulate"}
+
+
+# ---------------------------------------------------------------------------
+# Host record
+# ---------------------------------------------------------------------------
+def host_record(torch):
+    def read(path):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            return None
+    cpu = None
+    txt = read("/proc/cpuinfo") or ""
+    for line in txt.splitlines():
+        if line.startswith("model name"):
+            cpu = line.split(":", 1)[1].strip()
             break
-    o.set_threads(1)
-    if isinstance(case, MoE):
-        frac = len(case.cpu_rows) / case.O
-        per_call = case.alg_bytes_per_routing[0] * frac
-        sample = (f"{n} routed-expert calls restricted to {len(case.cpu_rows)} of {case.O} output "
-                  f"rows (routing seed 0) in {el:.1f} s")
-    else:
-        frac = getattr(case, "cpu_frac", 1.0)
-        per_call = case.alg_bytes * frac
-        part = "full GEMVs" if frac == 1.0 else f"calls on {frac:.2%} of the output rows"
-        sample = f"{n} {part} of {case.name} in {el:.1f} s ({el / n * 1e3:.1f} ms each)"
-    return {"value": round(per_call * n / el / 1e9, 3), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "sample": sample + ", f64 accumulate"}
+    sha = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        if r.returncode == 0:
+            sha = r.stdout.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+
+    def digest(path):
+        try:
+            with open(path, "rb") as f:
+                return hashlib.sha256(f.read()).hexdigest()
+        except OSError:
+            return None
+    lib = os.path.join(ROOT, "quantized_weight_decode_amd", "libqgemv.so")
+    props = torch.cuda.get_device_properties(0)
+    return {
+        "cmdline": " ".join([os.path.basename(sys.executable)] + sys.argv),
+        "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": cpu,
+        "gpu": props.name, "gpu_arch": getattr(props, "gcnArchName", None),
+        "cus": props.multi_processor_count,
+        "rocm": read("/opt/rocm/.info/version"), "torch": torch.__version__,
+        "python": platform.python_version(), "git_sha": sha,
+        "libqgemv_sha256": digest(lib),
+        "env": {k: os.environ[k] for k in ("HIP_VISIBLE_DEVICES", "ROCR_VISIBLE_DEVICES",
+                                           "GPU_MAX_HW_QUEUES", "HSA_XNACK")
+                if k in os.environ},
+    }
 
 
-def copy_calibrate(torch, nbytes, steps):
-    dev = torch.device("cuda:0")
-    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-    b = torch.empty_like(a)
-    for _ in range(5):
-        b.copy_(a)
-    ms = timed(torch, lambda i: b.copy_(a), 0, steps)
-    print(json.dumps({"copy_calibrate_bytes": nbytes, "steps": steps,
-                      "ms_per_copy": ms / steps,
-                      "GBs_read_plus_write": 2 * nbytes / (ms / steps * 1e-3) / 1e9}), flush=True)
+def roofline(case, us, alg_bytes):
+    gbs = alg_bytes / (us * 1e-6) / 1e9
+    r = {"bound": "hbm", "kernel": case.kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "us_per_launch": round(us, 3),
+         "alg_bytes_per_launch": round(alg_bytes)}
+    avg, traffic = profile_record(case.kernel, case.name)
+    r["traffic"] = traffic
+    if traffic and avg:
+        # counter view: calibrated HBM bytes over the traced kernel duration
+        r["counter_gbs"] = round(traffic / (avg * 1e-6) / 1e9, 1)
+        r["profile_avg_us"] = avg
+        r["traffic_over_alg"] = round(traffic / alg_bytes, 4)
+    if case.bound == "mfma":
+        tf = case.alg_flops / (us * 1e-6) / 1e12
+        r.update({"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F32_PEAK_TFS,
+                  "unit": "TFLOP/s", "frac": round(tf / MFMA_F32_PEAK_TFS, 4),
+                  "alg_flops_per_launch": case.alg_flops})
+    return r
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    # the GPU reaches its steady clocks only after some milliseconds of load:
-    # the first few hundred calls run 5-15 % slower
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--case", default="i4g_O12288_I6144_gs64", choices=CASE_NAMES)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--case", default=None, choices=CASE_NAMES,
+                    help="run one workload alone (default: the whole suite)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-read ceilings")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only time a plain device copy of BYTES bytes")
     args = ap.parse_args()
@@ -532,50 +735,126 @@ def main():
     import oracle
     import quantized_weight_decode_amd as q
 
-    case = build_case(args.case, torch, q, oracle.load())
-    for i in range(args.warmup):
-        case.step(i)
-    ms = timed(torch, case.step, args.warmup, args.steps)
-    ms_step = ms / args.steps
-    if isinstance(case, MoE):
-        step_bytes = case.bytes_for(args.warmup, args.steps) / args.steps
-    else:
-        step_bytes = case.alg_bytes
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    o = oracle.load()
+    names = [args.case] if args.case else SUITE
+    headline = args.case or HEADLINE
+    cases = {}
+    for n in names:
+        cases[n] = build_case(n, torch, q, o)
+        print(f"bench: built {n} (parity rel L2 {cases[n].rel:.2e})", file=sys.stderr,
+              flush=True)
 
-    # the dominant kernel is the step's one launch
-    kms, kbytes = ms_step, step_bytes
-    kgbs = kbytes / (kms * 1e-3) / 1e9
-    wgbs = case.weight_bytes / (kms * 1e-3) / 1e9
+    # headline: time-based warm-up, --warmup steps, then exactly --steps steps
+    hc = cases[headline]
+    nxt = warm(torch, hc.step, WARM_SECONDS)
+    for i in range(args.warmup):
+        hc.step(nxt + i)
+    first = nxt + args.warmup
+    ms = timed(torch, hc.step, first, args.steps)
+    ms_step = ms / args.steps
+    step_bytes = hc.bytes_for(first, args.steps) / args.steps
+    us_head = ms_step * 1e3
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    wgbs = hc.weight_bytes / (ms_step * 1e-3) / 1e9
+    nexti = {headline: first + args.steps}
+
+    # every workload: warm-up, then RUNS interleaved runs of max(--steps, 100) launches
+    k = max(args.steps, 100)
+    runs = {n: [] for n in names}
+    for n in names:
+        nexti[n] = warm(torch, cases[n].step, WARM_SECONDS, nexti.get(n, 0))
+    for _ in range(RUNS):
+        for n in names:
+            ms_r = timed(torch, cases[n].step, nexti[n], k)
+            runs[n].append((ms_r * 1e3 / k, cases[n].bytes_for(nexti[n], k) / k))
+            nexti[n] += k
+
+    # plain-read ceilings of the same bytes
+    ceilings = {}
+    if not args.no_ceiling:
+        lib = load_ceiling_lib()
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        for n in names:
+            c = cases[n]
+            key = (c.ceiling_bytes(), c.ceiling_pattern)
+            if key not in ceilings:
+                cl = Ceiling(torch, lib, key[0], key[1], cus)
+                v = cl.pick(torch)
+                warm(torch, cl.step, WARM_SECONDS)
+                us = sorted(timed(torch, cl.step, j * k, k) * 1e3 / k for j in range(RUNS))
+                ceilings[key] = {"name": cl.name, "bytes": cl.nbytes, "us": round(us[1], 3),
+                                 "gbs": round(cl.nbytes / (us[1] * 1e-6) / 1e9, 1),
+                                 "frac": round(cl.nbytes / (us[1] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                               4),
+                                 "tile": {"waves_per_wg": v[0], "loads_in_flight": v[1],
+                                          "mapping": "slab" if v[2] else "one-shot",
+                                          "wgs_per_cu": v[2] or None}}
+                del cl
+                torch.cuda.empty_cache()
+
+    threads = host_threads()
+    configs = {}
+    for n in names:
+        c = cases[n]
+        rr = sorted(runs[n])
+        us_med, bytes_med = rr[len(rr) // 2]
+        ent = {"format": c.fmt_desc, "dtype": c.dtype, "vectors": c.S,
+               "us_per_launch": {"median": round(us_med, 3), "min": round(rr[0][0], 3),
+                                 "max": round(rr[-1][0], 3), "runs": RUNS, "launches": k},
+               "alg_bytes_per_launch": round(bytes_med),
+               "roofline": roofline(c, us_med, bytes_med),
+               "weights_gbs": round(c.weight_bytes / (us_med * 1e-6) / 1e9, 1),
+               "equiv_decode_tok_s": round(c.weight_bytes / (us_med * 1e-6) /
+                                           (DENSE_27B * c.bytes_per_weight), 1),
+               "parity_rel_l2": c.rel}
+        key = (c.ceiling_bytes(), c.ceiling_pattern)
+        if key in ceilings:
+            ce = ceilings[key]
+            ent["ceiling"] = dict(ce)
+            # the workload's time against a plain read of its bytes
+            ent["frac_of_ceiling"] = round(ce["us"] / us_med, 4)
+        if isinstance(c, MoE):
+            ent["distinct_experts_per_routing"] = c.uniq
+            ent["tokens_per_s"] = round(c.T / (us_med * 1e-6), 1)
+        if not args.no_cpu and not isinstance(c, ReadCeiling):
+            budget = 2.5
+            ent["cpu_baseline"] = {"all_threads": cpu_rate(c, threads, budget),
+                                   "one_thread": cpu_rate(c, 1, budget)}
+        configs[n] = ent
+        print(f"bench: {n}: {us_med:.3f} us/launch, "
+              f"{ent['roofline']['frac']:.3f} of peak", file=sys.stderr, flush=True)
 
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": case.name, "batch": getattr(case, "S", 1), "format": case.fmt_desc,
+        "dtype": hc.dtype, "data": "synthetic",
+        "config": {"workload": hc.name, "batch": hc.S, "format": hc.fmt_desc,
                    "alg_bytes_per_step": round(step_bytes)},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "weights_gbs": round(wgbs, 1),
-        "equiv_decode_tok_s": round(wgbs * 1e9 / (DENSE_27B * case.bytes_per_weight), 1),
-        "roofline": {"bound": "hbm", "kernel": case.kernel, "achieved": round(kgbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
-                     "us_per_launch": round(kms * 1e3, 3), "alg_bytes_per_launch": round(kbytes),
-                     "traffic": profiled_traffic(case.kernel, case.name)},
-        "parity_rel_l2": case.rel,
+        "equiv_decode_tok_s": round(wgbs * 1e9 / (DENSE_27B * hc.bytes_per_weight), 1),
+        "roofline": roofline(hc, us_head, step_bytes),
+        "parity_rel_l2": hc.rel,
     }
-    if getattr(case, "bound", "hbm") == "mfma":
-        tf = case.alg_flops / (kms * 1e-3) / 1e12
-        out["roofline"].update({"bound": "mfma", "achieved": round(tf, 2),
-                                "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
-                                "frac": round(tf / MFMA_F32_PEAK_TFS, 4),
-                                "alg_flops_per_launch": case.alg_flops})
-    if isinstance(case, MoE):
-        out["config"]["distinct_experts_per_routing"] = case.uniq
-        out["tokens_per_s"] = round(case.T / (ms_step * 1e-3), 1)
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(case)
+    if not args.no_cpu and not isinstance(hc, ReadCeiling):
+        # the headline workload's oracle on all host threads over a longer sample
+        out["cpu_baseline"] = cpu_rate(hc, threads, 10.0)
+    out["configs"] = configs
+    out["host"] = host_record(torch)
     print(json.dumps(out), flush=True)
+
+
+def copy_calibrate(torch, nbytes, steps):
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    ms = timed(torch, lambda i: b.copy_(a), 0, steps)
+    print(json.dumps({"copy_calibrate_bytes": nbytes, "steps": steps,
+                      "ms_per_copy": ms / steps,
+                      "GBs_read_plus_write": 2 * nbytes / (ms / steps * 1e-3) / 1e9}), flush=True)
 
 
 if __name__ == "__main__":

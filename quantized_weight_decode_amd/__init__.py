@@ -215,6 +215,37 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _shape(t, name, shape):
+    """t must have exactly this shape (a tuple of ints)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _one_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
+def _out(out, S, O, like):
+    """The caller's y (checked: f32 [S][O] on like's device) or a new one."""
+    torch = _torch()
+    if out is None:
+        return torch.empty((S, O), dtype=torch.float32, device=like.device)
+    if out.numel() != S * O or out.dim() not in (1, 2) or \
+            (out.dim() == 2 and tuple(out.shape) != (S, O)) or (out.dim() == 1 and S != 1):
+        raise ValueError(f"out must have shape ({S}, {O})" + (f" or ({O},)" if S == 1 else ""))
+    return out
+
+
+def _gs(gs):
+    import operator
+    gs = operator.index(gs)
+    if gs < 2 or gs % 2:
+        raise QgemvError("argument check", 3, "group size must be an even number >= 2")
+    return gs
+
+
 def _vecs(x, I, name="x"):
     if x.dim() == 1:
         return 1
@@ -223,13 +254,23 @@ def _vecs(x, I, name="x"):
     raise ValueError(f"{name} must be [I] or [S, I]")
 
 
+def _i4g_check(w, scales, x, gs, S, I):
+    O = w.shape[0]
+    _gs(gs)
+    _shape(w, "w", (O, (I + 1) // 2))
+    if scales.numel() != O * ((I + gs - 1) // gs):
+        raise ValueError(f"scales must hold {O} x {(I + gs - 1) // gs} floats")
+    return O
+
+
 def i4g(w, scales, x, gs, out=None):
     """y[S][O] = grouped-int4 W[O][I] . x[S][I]; w u8 [O][(I+1)//2], scales f32 [O][ng]."""
     torch = _torch()
-    O = w.shape[0]
     I = x.shape[-1]
     S = _vecs(x, I)
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    O = _i4g_check(w, scales, x, gs, S, I)
+    _one_device(w, scales, x, out)
+    y = _out(out, S, O, x)
     _call("qgemv_i4g", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
           _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, gs, _stream())
     return y
@@ -238,19 +279,31 @@ def i4g(w, scales, x, gs, out=None):
 def i4g_prefill(w, scales, x, gs, out=None):
     """Grouped-int4 product for many tokens (MFMA): x f32 [S][I] -> y f32 [S][O]."""
     torch = _torch()
-    O, I = w.shape[0], x.shape[-1]
+    I = x.shape[-1]
     S = x.reshape(-1, I).shape[0]
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    O = _i4g_check(w, scales, x, gs, S, I)
+    _one_device(w, scales, x, out)
+    y = _out(out, S, O, x)
     _call("qgemv_i4g_prefill", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
           _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, gs, _stream())
     return y
 
 
+def _fp8_check(w, sc, I, name):
+    O = w.shape[0]
+    _shape(w, "w", (O, I))
+    if sc.numel() != ((O + 127) // 128) * ((I + 127) // 128):
+        raise ValueError(f"{name} must hold {(O + 127) // 128} x {(I + 127) // 128} block scales")
+    return O
+
+
 def fp8b128(w, scale_inv, x, out=None):
     torch = _torch()
-    O, I = w.shape[0], x.shape[-1]
+    I = x.shape[-1]
     S = _vecs(x, I)
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    O = _fp8_check(w, scale_inv, I, "scale_inv")
+    _one_device(w, scale_inv, x, out)
+    y = _out(out, S, O, x)
     _call("qgemv_fp8b128", _dev(w, "w", torch.uint8), _dev(scale_inv, "scale_inv", torch.float32),
           _dev(x, "x", torch.float32), _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
@@ -259,20 +312,32 @@ def fp8b128(w, scale_inv, x, out=None):
 def fp8b128_ue8m0(w, scale_e8m0, x, out=None):
     """fp8-e4m3 GEMV with UE8M0 (power-of-two byte) block scales."""
     torch = _torch()
-    O, I = w.shape[0], x.shape[-1]
+    I = x.shape[-1]
     S = _vecs(x, I)
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    O = _fp8_check(w, scale_e8m0, I, "scale_e8m0")
+    _one_device(w, scale_e8m0, x, out)
+    y = _out(out, S, O, x)
     _call("qgemv_fp8b128_ue8m0", _dev(w, "w", torch.uint8),
           _dev(scale_e8m0, "scale_e8m0", torch.uint8), _dev(x, "x", torch.float32),
           _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
 
 
+def _mq4_check(w, I):
+    O = w.shape[0]
+    if I % 256 == 0:  # otherwise the library refuses the call by name
+        if w.numel() != O * (I // 256) * 136:
+            raise ValueError(f"w must hold {O} rows of {I // 256} 136-byte groups")
+    return O
+
+
 def mq4v2(w, x_rot, out=None):
     torch = _torch()
-    O, I = w.shape[0], x_rot.shape[-1]
+    I = x_rot.shape[-1]
     S = _vecs(x_rot, I, "x_rot")
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x_rot.device)
+    O = _mq4_check(w, I)
+    _one_device(w, x_rot, out)
+    y = _out(out, S, O, x_rot)
     _call("qgemv_mq4v2", _dev(w, "w", torch.uint8), _dev(x_rot, "x_rot", torch.float32),
           _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
@@ -280,9 +345,11 @@ def mq4v2(w, x_rot, out=None):
 
 def _mq4_any(fn, w, x_rot, out):
     torch = _torch()
-    O, I = w.shape[0], x_rot.shape[-1]
+    I = x_rot.shape[-1]
     S = _vecs(x_rot, I, "x_rot")
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x_rot.device)
+    O = _mq4_check(w, I)
+    _one_device(w, x_rot, out)
+    y = _out(out, S, O, x_rot)
     _call(fn, _dev(w, "w", torch.uint8), _dev(x_rot, "x_rot", torch.float32),
           _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
@@ -302,6 +369,9 @@ def mq4v2_encode(W, out=None):
     """MQ4-v2 groups [O][I/256*136] u8 from rotated-space weights W f32 [O][I]."""
     torch = _torch()
     O, I = W.shape
+    _one_device(W, out)
+    if out is not None and out.numel() != O * (I // 256) * 136:
+        raise ValueError(f"out must hold {O} rows of {I // 256} 136-byte groups")
     w = out if out is not None else torch.empty((O, (I // 256) * 136), dtype=torch.uint8,
                                                  device=W.device)
     _call("qgemv_mq4v2_encode", _dev(W, "W", torch.float32), _dev(w, "w_out", torch.uint8),
@@ -312,9 +382,13 @@ def mq4v2_encode(W, out=None):
 def mq4v2_rot(w, x, signs, out=None):
     """MQ4-v2 GEMV on unrotated x: the FWHT-256 pre-rotation fused in."""
     torch = _torch()
-    O, I = w.shape[0], x.shape[-1]
+    I = x.shape[-1]
     S = _vecs(x, I)
-    y = out if out is not None else torch.empty((S, O), dtype=torch.float32, device=x.device)
+    O = _mq4_check(w, I)
+    if signs.numel() != I:
+        raise ValueError(f"signs must hold {I} values")
+    _one_device(w, x, signs, out)
+    y = _out(out, S, O, x)
     _call("qgemv_mq4v2_rot", _dev(w, "w", torch.uint8), _dev(x, "x", torch.float32),
           _dev(signs, "signs", torch.int8), _dev(y, "y", torch.float32), S, I, O, _stream())
     return y
@@ -324,6 +398,11 @@ def fwht256(x, signs, out=None):
     torch = _torch()
     I = x.shape[-1]
     S = _vecs(x, I)
+    if signs.numel() != I:
+        raise ValueError(f"signs must hold {I} values")
+    _one_device(x, signs, out)
+    if out is not None and out.numel() != x.numel():
+        raise ValueError(f"out must hold {x.numel()} floats")
     y = out if out is not None else torch.empty_like(x)
     _call("qgemv_fwht256", _dev(x, "x", torch.float32), _dev(signs, "signs", torch.int8),
           _dev(y, "x_rot", torch.float32), S, I, _stream())
@@ -334,6 +413,8 @@ def router_topk(logits, E, K):
     """logits f32 [T][ld] (experts 0..E-1 valid) -> (ids int32 [T][K], gates f32 [T][K])."""
     torch = _torch()
     T, ld = logits.shape
+    if not (1 <= E <= ld):
+        raise ValueError(f"E must be in 1..{ld} (the row stride of logits)")
     ids = torch.empty((T, K), dtype=torch.int32, device=logits.device)
     gates = torch.empty((T, K), dtype=torch.float32, device=logits.device)
     _call("qgemv_router_topk", _dev(logits, "logits", torch.float32), T, E, ld, K,
@@ -353,8 +434,16 @@ def moe_topk(w, scales, ids, gates, x, gs, workspace=None, out=None):
     E, O = w.shape[0], w.shape[1]
     T, K = ids.shape
     I = x.shape[-1]
+    _gs(gs)
+    _shape(w, "w", (E, O, (I + 1) // 2))
+    _shape(scales, "scales", (E, O, (I + gs - 1) // gs))
+    _shape(gates, "gates", (T, K))
+    _shape(x, "x", (T, I))
+    _one_device(w, scales, ids, gates, x, workspace, out)
     ws = workspace if workspace is not None else moe_topk_workspace(T, K, O, x.device)
-    y = out if out is not None else torch.empty((T, O), dtype=torch.float32, device=x.device)
+    if ws.numel() < qgemv_moe_topk_workspace(T, K, O):
+        raise ValueError(f"workspace must hold {qgemv_moe_topk_workspace(T, K, O)} bytes")
+    y = _out(out, T, O, x)
     _call("qgemv_moe_topk", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
           w[0].numel(), scales[0].numel(), E, _dev(ids, "ids", torch.int32),
           _dev(gates, "gates", torch.float32), T, K, _dev(x, "x", torch.float32),
@@ -371,7 +460,8 @@ def moe_topk_error(workspace):
 
 def dequant_i4g(w, scales, I, gs):
     torch = _torch()
-    O = w.shape[0]
+    O = _i4g_check(w, scales, None, gs, 1, I)
+    _one_device(w, scales)
     W = torch.empty((O, I), dtype=torch.float32, device=w.device)
     _call("qgemv_dequant_i4g", _dev(w, "w", torch.uint8), _dev(scales, "scales", torch.float32),
           _dev(W, "W"), I, O, gs, _stream())
@@ -381,6 +471,8 @@ def dequant_i4g(w, scales, I, gs):
 def dequant_fp8b128(w, scale_inv):
     torch = _torch()
     O, I = w.shape
+    _fp8_check(w, scale_inv, I, "scale_inv")
+    _one_device(w, scale_inv)
     W = torch.empty((O, I), dtype=torch.float32, device=w.device)
     _call("qgemv_dequant_fp8b128", _dev(w, "w", torch.uint8),
           _dev(scale_inv, "scale_inv", torch.float32), _dev(W, "W"), I, O, _stream())
@@ -390,6 +482,8 @@ def dequant_fp8b128(w, scale_inv):
 def dequant_fp8b128_ue8m0(w, scale_e8m0):
     torch = _torch()
     O, I = w.shape
+    _fp8_check(w, scale_e8m0, I, "scale_e8m0")
+    _one_device(w, scale_e8m0)
     W = torch.empty((O, I), dtype=torch.float32, device=w.device)
     _call("qgemv_dequant_fp8b128_ue8m0", _dev(w, "w", torch.uint8),
           _dev(scale_e8m0, "scale_e8m0", torch.uint8), _dev(W, "W"), I, O, _stream())
@@ -398,7 +492,7 @@ def dequant_fp8b128_ue8m0(w, scale_e8m0):
 
 def _dequant_mq4_any(fn, w, I):
     torch = _torch()
-    O = w.shape[0]
+    O = _mq4_check(w, I)
     W = torch.empty((O, I), dtype=torch.float32, device=w.device)
     _call(fn, _dev(w, "w", torch.uint8), _dev(W, "W"), I, O, _stream())
     return W
@@ -414,7 +508,7 @@ def dequant_mq4c(w, I):
 
 def dequant_mq4v2(w, I):
     torch = _torch()
-    O = w.shape[0]
+    O = _mq4_check(w, I)
     W = torch.empty((O, I), dtype=torch.float32, device=w.device)
     _call("qgemv_dequant_mq4v2", _dev(w, "w", torch.uint8), _dev(W, "W"), I, O, _stream())
     return W

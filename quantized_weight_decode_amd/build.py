@@ -1,4 +1,5 @@
-"""Builds libqgemv.so (all HIP kernels + the C ABI) for gfx950 with hipcc."""
+"""Builds libqgemv.so (all HIP kernels + the C ABI) for gfx950 with hipcc, and
+the benchmark's plain-read reference kernel into its own libqgemv_ceiling.so."""
 from __future__ import annotations
 
 import glob
@@ -11,6 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqgemv.so")
+CEILING_SRC = os.path.join(HERE, "bench_csrc", "ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libqgemv_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 instructions
@@ -54,5 +57,17 @@ def build(out: str = LIB, extra=()) -> str:
     return out
 
 
+def build_ceiling(out: str = CEILING_LIB) -> str:
+    """The plain-read reference kernel (benchmark only; not part of the C ABI)."""
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, *HIPFLAGS, CEILING_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed compiling " + CEILING_SRC)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_ceiling())

@@ -72,6 +72,8 @@ constexpr int MAX_DIM = 1 << 24;
 
 bool mis4(const void *p) { return ((uintptr_t)p & 3) != 0; }
 
+bool bad_gs(int gs) { return gs < 2 || (gs & 1) || gs > MAX_DIM; }
+
 int launched(hipError_t e) { return e == hipSuccess ? QGEMV_OK : QGEMV_E_HIP; }
 
 int check_gemv_dims(int S, int I, int O)
@@ -91,7 +93,7 @@ const char *qgemv_strerror(int status)
     case QGEMV_OK: return "ok";
     case QGEMV_E_NULL: return "a required pointer is NULL";
     case QGEMV_E_DIMS: return "a dimension is out of range";
-    case QGEMV_E_GS: return "group size must be an even number >= 2";
+    case QGEMV_E_GS: return "group size must be an even number in 2 .. 2^24";
     case QGEMV_E_ALIGN: return "an f32/int32 pointer is not 4-byte aligned";
     case QGEMV_E_K256: return "I must be a multiple of 256 for this format";
     case QGEMV_E_IDS: return "expert strides are smaller than one expert";
@@ -108,7 +110,7 @@ int qgemv_i4g(const void *w, const float *scales, const float *x, float *y, int 
 {
     if (!w || !scales || !x || !y) return QGEMV_E_NULL;
     if (int e = check_gemv_dims(S, I, O)) return e;
-    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (bad_gs(gs)) return QGEMV_E_GS;
     if (mis4(scales) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
     return launched(qg::launch_i4g_gemv(w, scales, x, y, S, I, O, gs, (hipStream_t)stream));
 }
@@ -119,7 +121,7 @@ int qgemv_i4g_prefill(const void *w, const float *scales, const float *x, float 
     if (!w || !scales || !x || !y) return QGEMV_E_NULL;
     if (S < 1 || S > MAX_DIM || I < 1 || O < 1 || I > MAX_DIM || O > MAX_DIM) return QGEMV_E_DIMS;
     if ((long long)((S + 63) / 64) * ((O + 63) / 64) > 0x7FFFFFFFLL) return QGEMV_E_DIMS;
-    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (bad_gs(gs)) return QGEMV_E_GS;
     if (mis4(scales) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
     return launched(qg::launch_i4g_prefill(w, scales, x, y, S, I, O, gs, (hipStream_t)stream));
 }
@@ -129,7 +131,7 @@ int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I, int O
 {
     if (!w || !scales || !W) return QGEMV_E_NULL;
     if (int e = check_gemv_dims(1, I, O)) return e;
-    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (bad_gs(gs)) return QGEMV_E_GS;
     if (mis4(scales) || mis4(W)) return QGEMV_E_ALIGN;
     return launched(qg::launch_i4g_dequant(w, scales, W, I, O, gs, (hipStream_t)stream));
 }
@@ -279,9 +281,9 @@ int qgemv_moe_topk(const void *w, const float *scales, long long w_stride, long 
     if (T < 1 || T > QGEMV_MAX_S || K < 1 || K > 64 || E < 1 || I < 1 || O < 1 ||
         I > MAX_DIM || O > MAX_DIM)
         return QGEMV_E_DIMS;
-    if (gs < 2 || (gs & 1)) return QGEMV_E_GS;
+    if (bad_gs(gs)) return QGEMV_E_GS;
     if (mis4(scales) || mis4(ids) || mis4(gates) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
-    const long long rb = (I + 1) / 2, ng = (I + gs - 1) / gs;
+    const long long rb = ((long long)I + 1) / 2, ng = ((long long)I + gs - 1) / gs;
     if (w_stride < (long long)O * rb || s_stride < (long long)O * ng) return QGEMV_E_IDS;
     if (!workspace || ws_bytes < qgemv_moe_topk_workspace(T, K, O) || mis4(workspace))
         return QGEMV_E_WORKSPACE;

@@ -6,30 +6,33 @@
 // gates are the selection probabilities renormalised over the selected
 // experts; colibri PR #457, section 4: routed experts are grouped-int4.)
 //
-// One launch, no host round trip, no atomics:
-//   * workgroup (t, b) owns token t and RT consecutive output rows; the
-//     T * NB workgroups (NB row blocks per token) cover about one CU each;
-//   * it stages x[t] in LDS as the dense grouped-int4 GEMV does (per-chunk
-//     fixed-point digits for the 4-bit integer dot product; one vector:
-//     staging every token in every workgroup makes thousands of workgroups
-//     fetch the same lines at once, which costs more than it saves); a token
-//     whose activations hold an infinity or NaN is multiplied per element in
-//     f32 instead, so they propagate as in the plain definition;
-//   * one wave reads the token's K ids and hands them over in LDS; every wave
-//     derives with ballots the distinct valid experts (first-occurrence
-//     order) -- the routing never leaves the device;
-//   * work units are (distinct expert, sub-tile of rows); each wave starts
-//     on one and takes the next free one from an LDS counter when it is
-//     done; a unit streams its rows of that expert (dwordx4, scale gather);
-//     a wave's (unit, sweep) steps form one stream with PF sweeps of loads in
-//     flight, crossing unit boundaries;
-//   * a unit's row sums go to an LDS partial array [K][RT] for every slot k
+// One launch, no host round trip, no global atomics, and every distinct
+// expert of the call streamed exactly once:
+//   * workgroup b owns RT consecutive output rows for every token; the NB
+//     workgroups cover about one CU each;
+//   * it stages the activations of all tokens in LDS as the dense
+//     grouped-int4 GEMV does (per-chunk fixed-point digits for the 4-bit
+//     integer dot product); a token whose activations hold an infinity or
+//     NaN, or a dynamic range the fixed point cannot carry precisely enough,
+//     is multiplied per element in f32 after the stream instead;
+//   * one wave reads the T*K ids and hands them over in LDS (lane l holds
+//     slot l = t*K + k); every wave derives with ballots the distinct valid
+//     experts in first-occurrence order -- the routing never leaves the
+//     device;
+//   * work units are (distinct expert, sub-tile of rows); a unit streams its
+//     rows of that expert once (dwordx4, scale gather) and multiplies every
+//     token that selected the expert with the same weight registers; each
+//     wave starts on one unit and takes the next free one from an LDS counter
+//     when it is done, and a wave's (unit, sweep) steps form one stream with
+//     PF sweeps of loads in flight, crossing unit boundaries;
+//   * a unit's row sums go to an LDS partial array [T*K][RT] for every slot
 //     that selected the expert (a duplicated id is streamed once and counted
 //     per slot); after a barrier the workgroup forms y[t] = sum_k gates *
 //     partial in ascending k (deterministic).
-// An expert selected by several tokens is streamed once per selecting token.
 // An id outside [0, E) is never dereferenced: its token's row of y is NaN and
-// the token's error flag in the workspace is set.
+// the token's error flag in the workspace is set.  Tokens beyond what the LDS
+// stages at once run in groups of launches (an expert shared across groups is
+// then read once per group).
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -39,22 +42,14 @@
 #ifndef QG_MOE_WPB
 #define QG_MOE_WPB 8
 #endif
-// workgroups per launch the row blocking aims at (over all tokens)
+// workgroups per launch the row blocking aims at
 #ifndef QG_MOE_WGS
 #define QG_MOE_WGS 256
 #endif
 #ifndef QG_MOE_PF
 #define QG_MOE_PF 3
 #endif
-// activation items (8 columns each) each thread loads up front: two cover a
-// 7168-column token with 8 waves, so no second round trip follows the
-// conversion (46.4 -> 46.0 us at 256 experts of 2048 x 7168, 4 tokens, top-8)
-#ifndef QG_MOE_NPRE
-#define QG_MOE_NPRE 2
-#endif
-// ring slots filled before the activations are converted.  Measured at 256
-// experts of 2048 x 7168, 4 tokens, top-8 (mean of five interleaved runs of
-// 300 calls): none 45.9 us, one 45.7, two 45.6, three 45.8.
+// ring slots filled before the activations are converted
 #ifndef QG_MOE_EARLY
 #define QG_MOE_EARLY 2
 #endif
@@ -62,7 +57,7 @@
 namespace qg {
 
 constexpr int MOE_MAX_T = 8;
-constexpr int MOE_FAST_MAX_K = 64;
+constexpr int MOE_FAST_MAX_TK = 64;   // slots t*K + k held by one wave's lanes
 
 // Lane holding the ui-th set bit of a wave-uniform lane mask (-1 if none).
 __device__ __forceinline__ int nth_lane(uint64_t m, int ui)
@@ -73,26 +68,88 @@ __device__ __forceinline__ int nth_lane(uint64_t m, int ui)
     return __ffsll((long long)sel) - 1;
 }
 
-template <int LPR, int R, int PF>
+// The workgroup's rows for every (distinct expert, selecting slot) pair of the
+// tokens in tokm with per-element f32 products, ((q - 8) * s) * x: the path of
+// tokens whose activations hold an infinity or NaN, or too wide a dynamic
+// range for the staged fixed point.  Wave w takes units w, w + WPB, ... of
+// the (distinct expert ui, lane-group row) units; each writes the partials of
+// the slots that chose the expert, as the streaming path does.
+template <int LPR, int R>
+__device__ __noinline__ void moe_rows_plain(const uint8_t *__restrict__ w,
+                                            const float *__restrict__ scales, long long w_stride,
+                                            long long s_stride, const float *__restrict__ x,
+                                            int I, int O, int ng, Div20 div_cpg, int RT, int o0,
+                                            int K, int TK, uint64_t firstm, int e, float *part,
+                                            uint32_t tokm)
+{
+    constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane / LPR, sl = lane % LPR;
+    const int NU = I / 32;
+    const size_t rb = (size_t)I / 2;
+    const int nsub = RT / ROWS_PER_WAVE;
+    const int nunits = __popcll(firstm) * nsub;
+#pragma unroll 1
+    for (int i = wave; i < nunits; i += QG_MOE_WPB) {
+        const int ui = i / nsub, st = i - ui * nsub;
+        const int ql = nth_lane(firstm, ui);
+        const int ue = __builtin_amdgcn_readlane(e, ql);
+        const uint64_t slots = __ballot(lane < TK && e == ue);
+        const uint8_t *we = w + (size_t)ue * (size_t)w_stride;
+        const float *se = scales + (size_t)ue * (size_t)s_stride;
+        const int row0 = o0 + st * ROWS_PER_WAVE + sub * R;
+#pragma unroll 1
+        for (int q = 0; q < TK; q++) {
+            if (!((slots >> q) & 1ull)) continue;   // wave-uniform
+            const int t = q / K;
+            if (!((tokm >> t) & 1u)) continue;
+            // the first slot of token t that chose the expert computes; the
+            // token's other such slots copy it
+            if (q % K > 0 && ((slots >> (t * K)) & ((1ull << (q % K)) - 1))) continue;
+#pragma unroll 1
+            for (int r = 0; r < R; r++) {
+                const int row = min(row0 + r, O - 1);
+                float acc = 0.0f;
+                for (int u = sl; u < NU; u += LPR)
+                    acc += nib_chunk_plain(*reinterpret_cast<const u32x4 *>(we + (size_t)row * rb +
+                                                                            (size_t)u * 16),
+                                           se[(size_t)row * ng + div_cpg((uint32_t)u)],
+                                           x + (size_t)t * I + (size_t)u * 32);
+                const float v = sub_reduce<LPR>(acc);
+                if (sl == LPR - 1 && row0 + r < O)
+                    for (int k = 0; k < K; k++)
+                        if ((slots >> (t * K + k)) & 1ull)
+                            part[(size_t)(t * K + k) * RT + row0 + r - o0] = v;
+            }
+        }
+    }
+}
+
+// TM: the most tokens one launch stages (T <= TM at run time).
+template <int TM, int LPR, int R, int PF>
 __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const uint8_t *__restrict__ w, const float *__restrict__ scales, long long w_stride,
     long long s_stride, int E, const int32_t *__restrict__ ids, const float *__restrict__ gates,
     int T, int K, const float *__restrict__ x, float *__restrict__ y, int I, int O, int ng,
-    Div20 div_cpg, int RT, int NB, int *__restrict__ err_flag)
+    Div20 div_cpg, int RT, int *__restrict__ err_flag, int nflag)
 {
     constexpr int ROWS_PER_WAVE = (WAVE / LPR) * R;
     constexpr int MOE_EARLY = QG_MOE_EARLY < PF ? QG_MOE_EARLY : PF;
+    constexpr int NT = 64 * QG_MOE_WPB;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int NU = I / 32;
-    u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                      // [6][NU]
-    float *xc = reinterpret_cast<float *>(xq + 6 * NU);                   // [NU]
-    float *part = xc + NU;                                                // [K][RT]
-    int *ids_l = reinterpret_cast<int *>(part + (size_t)K * RT);          // [64]
+    const int TK = T * K;
+    u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                      // [T][6][NU]
+    float *xc = reinterpret_cast<float *>(xq + (size_t)T * 6 * NU);       // [T][NU]
+    unsigned char *tail = lds_raw + q8_verdict_offset(T, NU, false);
+    void *vlds = tail;                                                    // stage_verdict
+    float *part = reinterpret_cast<float *>(tail + verdict_bytes(QG_MOE_WPB, TM));  // [TK][RT]
+    int *ids_l = reinterpret_cast<int *>(part + (size_t)TK * RT);         // [64]
     int *ctr = ids_l + 64;                                                // next unit
-    int *wflag = ctr + 1;                                                 // [WPB]
+    float *xacc_base = reinterpret_cast<float *>(ctr + 1);   // [WPB][TM-1][R][64], zeroed
 
-    const int t = blockIdx.x / NB;
-    const int o0 = (blockIdx.x - t * NB) * RT;
+    const int o0 = blockIdx.x * RT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     constexpr int nwaves = QG_MOE_WPB;
@@ -102,36 +159,42 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const int nit = (NU + LPR - 1) / LPR;
     const int nsub = RT / ROWS_PER_WAVE;
 
-    // the token's ids (one wave; thousands of waves reading one line would
-    // queue on one L2 channel) and its activations, before any weight load
+    // the ids (one wave; thousands of waves reading one line would queue on
+    // one L2 channel) and the activations, before any weight load
     int id = 0;
-    if (wave == 0) id = ids[t * K + min(lane, K - 1)];
-    const float *xt = x + (size_t)t * I;
-    XStageQ<1, QG_MOE_NPRE, 64 * QG_MOE_WPB> xst;
-    const int items = NU * 4;
-    xst.load(xt, items);
+    if (wave == 0) id = ids[min(lane, TK - 1)];
+    // two items per token and thread cover 7168 columns (at most eight up front)
+    constexpr int NPRE = 2 * TM < 8 ? 2 * TM : 8;
+    XStageQ<TM, NPRE, NT> xst;
+    const int items = T * NU * 4;
+    xst.load(x, items);
     __builtin_amdgcn_sched_barrier(0);
     if (wave == 0) ids_l[lane] = id;
     if (threadIdx.x == 0) *ctr = nwaves;
+#pragma unroll
+    for (int m = 0; m < (TM - 1) * R; m++)
+        xacc_base[((size_t)wave * (TM - 1) * R + m) * 64 + lane] = 0.0f;
     // raw barrier (the activation loads stay in flight); the LDS write must
     // have landed before it
     __builtin_amdgcn_s_waitcnt(QG_WAIT_LGKM0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // distinct valid experts of the token, first-occurrence order
-    const int e = lane < K ? ids_l[lane] : -1;
-    const bool valid = lane < K && e >= 0 && e < E;
+    // distinct valid experts over all slots, first-occurrence order
+    const int e = lane < TK ? ids_l[lane] : -1;
+    const bool valid = lane < TK && e >= 0 && e < E;
     bool first = valid;
-    for (int q = 0; q < K; q++)
+    for (int q = 0; q < TK; q++)
         if (q < lane && __builtin_amdgcn_readlane(e, q) == e) first = false;
     const uint64_t firstm = __ballot(first);
-    const bool bad = __ballot(lane < K && !valid) != 0;
-    if (o0 == 0 && threadIdx.x == 0) {
-        err_flag[t] = bad ? 1 : 0;
-        if (t == 0)
-            for (int u = T; u < MOE_MAX_T; u++) err_flag[u] = 0;
-    }
+    const uint64_t badm = __ballot(lane < TK && !valid);   // slots holding a bad id
+    uint32_t badtok = 0;                                   // tokens with a bad id
+    for (int t = 0; t < T; t++)
+        if ((badm >> (t * K)) & (K == 64 ? ~0ull : ((1ull << K) - 1))) badtok |= 1u << t;
+    // error flags of this launch's tokens, and zeros for the flag slots past
+    // the call's last token (nflag slots in all)
+    if (blockIdx.x == 0 && (int)threadIdx.x < nflag)
+        err_flag[threadIdx.x] = (int)threadIdx.x < T ? (int)((badtok >> threadIdx.x) & 1u) : 0;
 
     // Work units are (distinct expert ui, row sub-tile st), numbered
     // i = ui * nsub + st.  Wave w starts on unit w; each later unit goes to
@@ -141,14 +204,24 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 
     struct Unit {
         int e, row0;
+        uint64_t slots;   // slots (lanes) that selected the expert
+        uint32_t toks;    // tokens with such a slot
     };
     auto unit_of = [&](int i) {
         const int ui = i / nsub, st = i - ui * nsub;
         const int ql = nth_lane(firstm, ui);
         Unit u;
-        // past the last unit (or none): expert 0, so clamped loads stay valid
-        u.e = ql >= 0 && i < nunits ? __builtin_amdgcn_readlane(e, ql) : 0;
+        // past the last unit (or none): expert 0 and no tokens, so the clamped
+        // loads stay valid and nothing is multiplied
+        const bool any = ql >= 0 && i < nunits;
+        u.e = any ? __builtin_amdgcn_readlane(e, ql) : 0;
         u.row0 = o0 + st * ROWS_PER_WAVE + sub * R;
+        u.slots = any ? __ballot(lane < TK && e == u.e) : 0ull;
+        u.toks = 0;
+#pragma unroll
+        for (int t = 0; t < TM; t++)
+            if (t < T && ((u.slots >> (t * K)) & (K == 64 ? ~0ull : ((1ull << K) - 1))))
+                u.toks |= 1u << t;
         return u;
     };
     auto grab = [&]() {
@@ -162,12 +235,14 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     // each ring slot records the unit and sweep its loads belong to
     // (unit >= nunits: nothing, the loads re-read the previous step)
     int slot_u[PF], slot_c[PF];
+    uint32_t slot_t[PF];
     // fetch cursor: unit fi, sweep fc
     int fi = wave, fc = 0;
     Unit fu = unit_of(min(fi, nunits > 0 ? nunits - 1 : 0));
     auto fetch = [&](int j) {
         slot_u[j] = fi;
         slot_c[j] = fc;
+        slot_t[j] = fi < nunits ? fu.toks : 0u;
         const uint8_t *we = w + (size_t)fu.e * (size_t)w_stride;
         const float *se = scales + (size_t)fu.e * (size_t)s_stride;
         const int u = min(fc * LPR + sl, NU - 1);
@@ -200,20 +275,21 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
     for (int j = 0; j < MOE_EARLY; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t xbad = xst.store(xt, items, NU, reinterpret_cast<uint32_t *>(xq), xc, nullptr);
-    const bool wbad = __ballot(xbad != 0) != 0;
-    if (lane == 0) wflag[wave] = wbad;
-    __syncthreads();
-    int xnan = 0;
-#pragma unroll
-    for (int k = 0; k < QG_MOE_WPB; k++) xnan |= wflag[k];
-    xnan = __builtin_amdgcn_readfirstlane(xnan);
+    const uint32_t xbad = xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, nullptr);
+    // tokens whose activations hold an infinity or NaN, or too wide a dynamic
+    // range for the fixed point: their products are formed per element after
+    // the stream (kept out of the streaming loop)
+    const uint32_t plainm = (uint32_t)stage_verdict<QG_MOE_WPB, TM>(xbad, xst.dsum, vlds);
+
 #pragma unroll
     for (int j = MOE_EARLY; j < PF; j++) fetch(j);
     __builtin_amdgcn_sched_barrier(0);
 
+    // The unit's first token accumulates in registers, with running digit
+    // sums (q8_dot_run); any further token (an expert several tokens chose)
+    // accumulates in this lane's slots of xacc, [wave][extra token][row][lane]
     float acc[R];
-    uint32_t P[R][6], V[R];   // running digit sums per row (see q8_dot_run)
+    uint32_t P[R][6], V[R];
 #pragma unroll
     for (int r = 0; r < R; r++) {
         acc[r] = 0.0f;
@@ -221,30 +297,64 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 #pragma unroll
         for (int k = 0; k < 6; k++) P[r][k] = 0;
     }
+    float *xacc = xacc_base + (size_t)wave * (TM - 1) * R * 64 + lane;
+
+    // the row sums of token t (slots km of it chose the expert) -> partials
+    auto emit = [&](const Unit &cu, int t, float v, int r) {
+        uint64_t km = cu.slots >> (t * K);
+        if (K < 64) km &= (1ull << K) - 1;
+        const int lr = cu.row0 + r - o0;
+        const bool st = sl == LPR - 1 && cu.row0 + r < O;
+        for (uint64_t m = km; m; m &= m - 1) {
+            const int k = __builtin_ctzll(m);
+            if (st) part[(size_t)(t * K + k) * RT + lr] = v;
+        }
+    };
 
     auto consume = [&](int j) {
         const int ci = slot_u[j];
         if (ci >= nunits) return;                      // nothing (wave-uniform)
+        // tokens on the per-element path are formed after the stream
+        const uint32_t toks = slot_t[j] & ~plainm;
+        if (!toks) return;
         const int u = slot_c[j] * LPR + sl;
         const bool in_row = u < NU;
         const int uu = in_row ? u : 0;
-        if (xnan) {
-            if (in_row)
+        const int t0 = __builtin_ctz(toks);
+        uint32_t wx[R][4];
 #pragma unroll
-                for (int r = 0; r < R; r++)
-                    acc[r] += nib_chunk_plain(wb[j][r], sb[j][r], xt + (size_t)uu * 32);
-        } else {
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) wx[r][d] = wb[j][r][d] ^ Q8_NIB_FLIP;
+        {
+            const u32x4 *xt = xq + (size_t)t0 * 6 * NU;
             u32x4 L[6];
 #pragma unroll
-            for (int k = 0; k < 6; k++) L[k] = xq[k * NU + uu];
-            const float cs = in_row ? xc[uu] : 0.0f;
+            for (int k = 0; k < 6; k++) L[k] = xt[k * NU + uu];
+            const float cs = in_row ? xc[(size_t)t0 * NU + uu] : 0.0f;
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                uint32_t wx[4];
-#pragma unroll
-                for (int d = 0; d < 4; d++) wx[d] = wb[j][r][d] ^ Q8_NIB_FLIP;
-                const int dv = q8_dot_run(wx, L, P[r], V[r]);
+                const int dv = q8_dot_run(wx[r], L, P[r], V[r]);
                 acc[r] = __builtin_fmaf(sb[j][r] * cs, (float)dv, acc[r]);
+            }
+        }
+        // wave-uniform, usually 0 (never with one token)
+        const uint32_t more = TM > 1 ? toks & (toks - 1) : 0u;
+        if (more) {
+            int m = 0;
+#pragma unroll 1
+            for (uint32_t b = more; b; b &= b - 1, m++) {
+                const int t = __builtin_ctz(b);
+                const u32x4 *xt = xq + (size_t)t * 6 * NU;
+                u32x4 L[6];
+#pragma unroll
+                for (int k = 0; k < 6; k++) L[k] = xt[k * NU + uu];
+                const float cs = in_row ? xc[(size_t)t * NU + uu] : 0.0f;
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    float *a = xacc + (size_t)(m * R + r) * 64;
+                    *a = __builtin_fmaf(sb[j][r] * cs, (float)q8_dot(wx[r], L), *a);
+                }
             }
         }
         if (slot_c[j] + 1 < nit) return;
@@ -252,15 +362,26 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         const Unit cu = unit_of(ci);
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const float v = sub_reduce<LPR>(acc[r]);
-            const int lr = cu.row0 + r - o0;
-            for (int kk = 0; kk < K; kk++)
-                if (__builtin_amdgcn_readlane(e, kk) == cu.e && sl == LPR - 1 && cu.row0 + r < O)
-                    part[(size_t)kk * RT + lr] = v;
+            emit(cu, t0, sub_reduce<LPR>(acc[r]), r);
             acc[r] = 0.0f;
+        }
+        if (more) {
+            int m = 0;
+#pragma unroll 1
+            for (uint32_t b = more; b; b &= b - 1, m++) {
+                const int t = __builtin_ctz(b);
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    float *a = xacc + (size_t)(m * R + r) * 64;
+                    emit(cu, t, sub_reduce<LPR>(*a), r);
+                    *a = 0.0f;
+                }
+            }
         }
     };
 
+    // rounds of PF slots: consume a slot, then refill it; stop once the
+    // oldest slot of a round holds nothing (slots are filled in order)
     // rounds of PF slots: consume a slot, then refill it; stop once the
     // oldest slot of a round holds nothing (slots are filled in order)
     while (slot_u[0] < nunits) {
@@ -273,18 +394,25 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         }
     }
     __syncthreads();
+    if (plainm) {
+        // tokens whose activations the fixed point cannot carry: per element
+        moe_rows_plain<LPR, R>(w, scales, w_stride, s_stride, x, I, O, ng, div_cpg, RT, o0, K, TK,
+                               firstm, e, part, plainm);
+        __syncthreads();
+    }
 
     // y[t] = sum_k gates * partial, ascending k
-    for (int i = threadIdx.x; i < RT; i += 64 * QG_MOE_WPB) {
-        const int row = o0 + i;
+    for (int i = threadIdx.x; i < T * RT; i += NT) {
+        const int t = i / RT, r = i - t * RT;
+        const int row = o0 + r;
         if (row >= O) continue;
         float v;
-        if (bad) {
+        if ((badtok >> t) & 1u) {
             v = __builtin_nanf("");
         } else {
             v = 0.0f;
             for (int kk = 0; kk < K; kk++)
-                v = __builtin_fmaf(gates[t * K + kk], part[(size_t)kk * RT + i], v);
+                v = __builtin_fmaf(gates[t * K + kk], part[(size_t)(t * K + kk) * RT + r], v);
         }
         y[(size_t)t * O + row] = v;
     }
@@ -409,36 +537,55 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 
 namespace {
 
-size_t moe_lds_bytes(int K, int I, int RT)
+// LDS of one launch staging T tokens (kernel instance TM >= T)
+size_t moe_lds_bytes(int TM, int T, int K, int I, int RT)
 {
-    return q8_stage_bytes(1, I / 32, false) + (size_t)K * RT * sizeof(float) +
-           (65 + QG_MOE_WPB) * sizeof(int);
+    return q8_verdict_offset(T, I / 32, false) + verdict_bytes(QG_MOE_WPB, TM) +
+           (size_t)T * K * RT * sizeof(float) + 65 * sizeof(int) +
+           (size_t)QG_MOE_WPB * (TM - 1) * QG_MOE_R * 64 * sizeof(float);
 }
 
-// Row blocks: about one workgroup per CU over all T tokens, RT rows each (a
-// multiple of the wave tile rpw).
-void moe_blocks(int T, int O, int rpw, int &RT, int &NB)
+// Row blocks: about QG_MOE_WGS workgroups, RT rows each (a multiple of the
+// wave tile rpw).
+void moe_blocks(int O, int rpw, int &RT, int &NB)
 {
-    const int want = (QG_MOE_WGS + T - 1) / T;
-    const int per = (O + want - 1) / want;
+    const int per = (O + QG_MOE_WGS - 1) / QG_MOE_WGS;
     RT = (per + rpw - 1) / rpw * rpw;
     NB = (O + RT - 1) / RT;
 }
 
-template <int LPR, int R>
+template <int TM, int LPR>
 hipError_t launch_t(const uint8_t *w, const float *s, long long ws, long long ss, int E,
                     const int32_t *ids, const float *gates, int T, int K, const float *x,
-                    float *y, int I, int O, int gs, int RT, int NB, int *err, hipStream_t st)
+                    float *y, int I, int O, int gs, int RT, int NB, int *err, int nflag,
+                    hipStream_t st)
 {
-    const size_t lds = moe_lds_bytes(K, I, RT);
-    auto kern = moe_i4g_stream<LPR, R, QG_MOE_PF>;
+    const size_t lds = moe_lds_bytes(TM, T, K, I, RT);
+    auto kern = moe_i4g_stream<TM, LPR, QG_MOE_R, QG_MOE_PF>;
     hipError_t e = set_max_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(T * NB), dim3(64 * QG_MOE_WPB), lds, st, w, s, ws, ss, E, ids,
-                       gates, T, K, x, y, I, O, (I + gs - 1) / gs,
-                       Div20::make((uint32_t)(gs / 32)), RT, NB, err);
+    hipLaunchKernelGGL(kern, dim3(NB), dim3(64 * QG_MOE_WPB), lds, st, w, s, ws, ss, E, ids, gates,
+                       T, K, x, y, I, O, (I + gs - 1) / gs, Div20::make((uint32_t)(gs / 32)), RT,
+                       err, nflag);
     return hipGetLastError();
 }
+
+template <int TM>
+hipError_t launch_tm(int lpr, const uint8_t *w, const float *s, long long ws, long long ss, int E,
+                     const int32_t *ids, const float *gates, int T, int K, const float *x,
+                     float *y, int I, int O, int gs, int RT, int NB, int *err, int nflag,
+                     hipStream_t st)
+{
+    switch (lpr) {
+    case 64: return launch_t<TM, 64>(w, s, ws, ss, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err, nflag, st);
+    case 32: return launch_t<TM, 32>(w, s, ws, ss, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err, nflag, st);
+    case 16: return launch_t<TM, 16>(w, s, ws, ss, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err, nflag, st);
+    case 8: return launch_t<TM, 8>(w, s, ws, ss, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err, nflag, st);
+    default: return launch_t<TM, 4>(w, s, ws, ss, E, ids, gates, T, K, x, y, I, O, gs, RT, NB, err, nflag, st);
+    }
+}
+
+inline int tm_of(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
 
 }  // namespace
 
@@ -451,28 +598,34 @@ hipError_t launch_moe_topk(const void *w, const float *scales, long long w_strid
     const int lpr = pick_lpr(I / 32 > 0 ? I / 32 : 1);
     const int rpw = (WAVE / lpr) * QG_MOE_R;
     int RT, NB;
-    moe_blocks(T, O, rpw, RT, NB);
-    const bool fast = K <= MOE_FAST_MAX_K && I % 32 == 0 && gs % 32 == 0 &&
+    moe_blocks(O, rpw, RT, NB);
+    // tokens per launch: all of them if the LDS stages them together
+    int tg = T;
+    while (tg > 1 && moe_lds_bytes(tm_of(tg), tg, K, I, RT) > LDS_BUDGET) --tg;
+    const bool fast = tg * K <= MOE_FAST_MAX_TK && I % 32 == 0 && gs % 32 == 0 &&
                       ((uintptr_t)w & 15) == 0 && (w_stride & 15) == 0 &&
-                      ((uintptr_t)x & 15) == 0 && moe_lds_bytes(K, I, RT) <= LDS_BUDGET;
+                      ((uintptr_t)x & 15) == 0 && moe_lds_bytes(tm_of(tg), tg, K, I, RT) <= LDS_BUDGET;
     if (fast) {
-        switch (lpr) {
-        case 64:
-            return launch_t<64, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
-                                          y, I, O, gs, RT, NB, err_flag, st);
-        case 32:
-            return launch_t<32, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
-                                          y, I, O, gs, RT, NB, err_flag, st);
-        case 16:
-            return launch_t<16, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
-                                          y, I, O, gs, RT, NB, err_flag, st);
-        case 8:
-            return launch_t<8, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x,
-                                          y, I, O, gs, RT, NB, err_flag, st);
-        default:
-            return launch_t<4, QG_MOE_R>(wb, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
-                                         I, O, gs, RT, NB, err_flag, st);
+        for (int t0 = 0; t0 < T; t0 += tg) {
+            const int n = T - t0 < tg ? T - t0 : tg;
+            const int32_t *ids_g = ids + (size_t)t0 * K;
+            const float *gates_g = gates + (size_t)t0 * K;
+            const float *x_g = x + (size_t)t0 * I;
+            float *y_g = y + (size_t)t0 * O;
+            int *err_g = err_flag + t0;
+            // flag slots this launch writes: its tokens, and for the last one
+            // every slot up to MOE_MAX_T
+            const int nflag = t0 + n >= T ? MOE_MAX_T - t0 : n;
+            hipError_t e;
+            switch (tm_of(n)) {
+            case 1: e = launch_tm<1>(lpr, wb, scales, w_stride, s_stride, E, ids_g, gates_g, n, K, x_g, y_g, I, O, gs, RT, NB, err_g, nflag, st); break;
+            case 2: e = launch_tm<2>(lpr, wb, scales, w_stride, s_stride, E, ids_g, gates_g, n, K, x_g, y_g, I, O, gs, RT, NB, err_g, nflag, st); break;
+            case 4: e = launch_tm<4>(lpr, wb, scales, w_stride, s_stride, E, ids_g, gates_g, n, K, x_g, y_g, I, O, gs, RT, NB, err_g, nflag, st); break;
+            default: e = launch_tm<8>(lpr, wb, scales, w_stride, s_stride, E, ids_g, gates_g, n, K, x_g, y_g, I, O, gs, RT, NB, err_g, nflag, st); break;
+            }
+            if (e != hipSuccess) return e;
         }
+        return hipSuccess;
     }
     const int wpb = 4;
     hipLaunchKernelGGL(moe_i4g_general, dim3((O + wpb - 1) / wpb), dim3(64 * wpb), 0, st, wb,

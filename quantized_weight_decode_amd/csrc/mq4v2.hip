@@ -17,7 +17,8 @@
 // P = sum (q - 8) v and
 //     sum w x~ = scale * c * P + (8 * scale + zero) * xsum,
 // weight = q * scale + zero reassociated.  Activations holding an infinity or
-// NaN are multiplied per element in f32 instead (fma(q, scale, zero) * x).
+// NaN, or too wide a dynamic range for the fixed point (stage_verdict), are
+// multiplied per element in f32 instead (fma(q, scale, zero) * x).
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     u32x4 *xq = reinterpret_cast<u32x4 *>(lds_raw);                        // [S][6][NU]
     float *xc = reinterpret_cast<float *>(xq + (size_t)S * 6 * NU);        // [S][NU]
     float *xsm = xc + (size_t)S * NU;                                      // [S][NU]
-    int *wflag = reinterpret_cast<int *>(xsm + (size_t)S * NU);            // [16]
+    void *vlds = lds_raw + q8_verdict_offset(S, NU, true);                 // stage_verdict
     // ROT fallback: x_rot as f32 [S][I], over the staging area once it is unused
     float *xf = reinterpret_cast<float *>(lds_raw);
 
@@ -249,14 +250,9 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t bad =
         xst.store(x, items, NU, reinterpret_cast<uint32_t *>(xq), xc, xsm, signs);
-    const bool wbad = __ballot(bad != 0) != 0;
-    if (lane == 0) wflag[wave] = wbad;
-    __syncthreads();
-    int xnan = 0;
-#pragma unroll
-    for (int k = 0; k < WPB; k++) xnan |= wflag[k];
-    xnan = __builtin_amdgcn_readfirstlane(xnan);
-    if (xnan) {
+    // non-finite activations or a dynamic range too wide for the fixed point
+    const int plain = stage_verdict<WPB, S>(bad, xst.dsum, vlds);
+    if (plain) {
         // the whole workgroup takes this branch; with ROT it first rebuilds
         // x_rot as f32 over the staging area (every wave has read the flags)
         if constexpr (ROT) {
@@ -512,7 +508,7 @@ namespace {
 
 size_t mq4_lds_bytes(int S, int I, bool rot)
 {
-    const size_t stage = q8_stage_bytes(S, I / 32, true) + 16 * sizeof(int);
+    const size_t stage = q8_verdict_offset(S, I / 32, true) + verdict_bytes(16, S);
     const size_t fallback = rot ? (size_t)S * I * sizeof(float) : 0;
     return stage > fallback ? stage : fallback;
 }

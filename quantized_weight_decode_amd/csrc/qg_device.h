@@ -165,6 +165,9 @@ __device__ __forceinline__ void pin_values(const float (&v)[N])
 }
 
 constexpr float Q8_MAGIC = 12582912.0f;        // 1.5 * 2^23
+// Precision test of the staged fixed point (see q8_put): the squared bound
+// on its estimated relative error on y, (3e-6)^2.
+constexpr float Q8_TAU2 = 9.0e-12f;
 constexpr uint32_t Q8_UNBIAS = 0x4AB77778u;    // 0x4B400000 - 0x888888
 constexpr uint32_t Q8_DIGIT_BIAS = 0x888888u;  // 8 * (16^0 + ... + 16^5)
 constexpr uint32_t Q8_NIB_FLIP = 0x88888888u;
@@ -190,24 +193,51 @@ __device__ __forceinline__ int quad_sum_i32(int v)
 // chunk exponent is a max over them).  Lanes with ok == false store nothing.
 // Returns nonzero if the chunk holds an infinity or NaN (its staged values
 // are then meaningless).
+//
+// Precision test.  The fixed point represents every element of a chunk to
+// within half its quantum 2^(E-21), whatever the element's own size, so
+// elements much smaller than the chunk's largest lose relative precision.
+// With weights of no particular sign or size, the relative L2 error this
+// puts on y is about sqrt(A / B), A the sum of the squared representation
+// errors and B the sum of the squared values.  An outlier of the chunk may
+// meet a zero weight, so both sums leave out each lane's largest element
+// (whose own relative error is at most 2^-21).  dl returns this lane's
+// A - TAU^2 B (exact power-of-two rescaling into f64); a vector is staged
+// precisely enough when its sum over all lanes is not positive.
 template <bool SUM>
 __device__ __forceinline__ uint32_t q8_put(const float xv[8], bool ok, uint32_t t, uint32_t u,
                                            uint32_t d, uint32_t NU, uint32_t *__restrict__ xq,
                                            float *__restrict__ xc, float *__restrict__ xsum,
-                                           float post = 1.0f)
+                                           double &dl, float post = 1.0f)
 {
     // |x| as ordered integers: every NaN sorts above infinity, above every finite
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < 8; k++) m = max(m, __builtin_bit_cast(uint32_t, xv[k]) & 0x7FFFFFFFu);
+    const uint32_t ml = m;                       // this lane's largest |x|
     m = quad_max_u32(m);
     const uint32_t eb = m >> 23;                 // biased exponent of max|x|: E = eb - 126
     const uint32_t e = max(eb, 26u);             // E >= -100
     const float sin = __builtin_bit_cast(float, (274u - e) << 23);   // 2^(21 - E)
     uint32_t n[8];                                // v + 0x888888, in [0x688888, 0xA88888]
+    float pa = 0.0f, pb = 0.0f;                   // A and B of the lane, in units of 2^(2E-42)
 #pragma unroll
-    for (int k = 0; k < 8; k++)
-        n[k] = __builtin_bit_cast(uint32_t, __builtin_fmaf(xv[k], sin, Q8_MAGIC)) - Q8_UNBIAS;
+    for (int k = 0; k < 8; k++) {
+        const float r = __builtin_fmaf(xv[k], sin, Q8_MAGIC);
+        n[k] = __builtin_bit_cast(uint32_t, r) - Q8_UNBIAS;
+        const float vf = r - Q8_MAGIC;                            // v, exactly
+        const float dv = __builtin_fmaf(xv[k], sin, -vf);         // x 2^(21-E) - v, exactly
+        pa = __builtin_fmaf(dv, dv, pa);
+        pb = __builtin_fmaf(vf, vf, pb);
+    }
+    {   // leave out the lane's largest element
+        const float xm = __builtin_bit_cast(float, ml);
+        const float vm = __builtin_fmaf(xm, sin, Q8_MAGIC) - Q8_MAGIC;
+        const float dm = __builtin_fmaf(xm, sin, -vm);
+        pa = __builtin_fmaf(-dm, dm, pa);
+        pb = __builtin_fmaf(-vm, vm, pb);
+    }
+    dl = ok ? __builtin_ldexp((double)__builtin_fmaf(-Q8_TAU2, pb, pa), 2 * (int)e - 294) : 0.0;
     // byte b of the even columns (0, 2, 4, 6) and of the odd columns (1, 3, 5, 7)
     const uint32_t te = __builtin_amdgcn_perm(n[2], n[0], 0x05010400u);
     const uint32_t ue = __builtin_amdgcn_perm(n[6], n[4], 0x05010400u);
@@ -301,8 +331,8 @@ __device__ __forceinline__ void fwht256_item(float v[8], int lane)
 // and store() converts them, then any further items one at a time.  Items
 // past the end belong to whole lane groups (items is a multiple of 32 with
 // ROT, of 4 otherwise; NT a multiple of 64), which skip both.  NT is the
-// workgroup size.  store() returns nonzero in a lane that met an infinity or
-// NaN.
+// workgroup size; items may cover fewer than S vectors.  store() returns the
+// mask of vectors (bit t) in which this thread met an infinity or NaN.
 //
 // With ROT the vectors are first rotated as the FWHT-256 pre-rotation
 // defines it: x_rot = H256 (signs . x) / 16 per 256-column block (I % 256 ==
@@ -316,6 +346,7 @@ struct XStageQ {
     f32x4 a[NPRE], b[NPRE];
     u32x2 sg[ROT ? NPRE : 1];
     int rot;
+    double dsum[S];   // per vector: this thread's share of A - TAU^2 B (q8_put)
 
     __device__ __forceinline__ void load(const float *__restrict__ x, int items,
                                          const int8_t *__restrict__ signs = nullptr, int ipv = 0)
@@ -354,8 +385,12 @@ struct XStageQ {
             fwht256_item(v, (int)threadIdx.x & 63);
             post = 0.0625f;
         }
-        return q8_put<SUM>(v, true, (uint32_t)t, (uint32_t)rem >> 2, (uint32_t)rem & 3u,
-                           (uint32_t)NU, xq, xc, xsum, post);
+        double dl;
+        const uint32_t bad = q8_put<SUM>(v, true, (uint32_t)t, (uint32_t)rem >> 2,
+                                         (uint32_t)rem & 3u, (uint32_t)NU, xq, xc, xsum, dl, post);
+#pragma unroll
+        for (int k = 0; k < S; k++) dsum[k] += t == k ? dl : 0.0;
+        return bad << t;
     }
 
     __device__ __forceinline__ uint32_t store(const float *__restrict__ x, int items, int NU,
@@ -364,6 +399,8 @@ struct XStageQ {
                                               const int8_t *__restrict__ signs = nullptr)
     {
         uint32_t bad = 0;
+#pragma unroll
+        for (int k = 0; k < S; k++) dsum[k] = 0.0;
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
             const int f = (int)threadIdx.x + j * NT;
@@ -434,6 +471,11 @@ __host__ __device__ constexpr size_t q8_stage_bytes(int S, int NU, bool sum)
 {
     return (size_t)S * NU * (6 * 16 + 4 + (sum ? 4 : 0));
 }
+// 8-byte aligned offset just past the fixed-point staging (the verdict area)
+__host__ __device__ constexpr size_t q8_verdict_offset(int S, int NU, bool sum)
+{
+    return (q8_stage_bytes(S, NU, sum) + 7) / 8 * 8;
+}
 
 // sum (q - 8) v over one lane chunk of packed weights wx (already XOR-ed with
 // 0x88888888) against the chunk's digit dwords L.  P and V carry running
@@ -495,6 +537,74 @@ __device__ __forceinline__ float sub_reduce(float v)
     if (LPR >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
     if (LPR >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
     return v;
+}
+
+// Sum of a double over the 64 lanes of a wave (DPP on both halves, the
+// order of sub_reduce); the full sum lands in lane 63.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK,
+                                                             0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL,
+                                                             ROW_MASK, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    v += dpp64<0xB1>(v);
+    v += dpp64<0x4E>(v);
+    v += dpp64<0x141>(v);
+    v += dpp64<0x140>(v);
+    v += dpp64<0x142, 0xA>(v);
+    v += dpp64<0x143, 0xC>(v);
+    return v;
+}
+
+// LDS bytes stage_verdict needs (8-byte aligned start).
+__host__ __device__ constexpr size_t verdict_bytes(int WPB, int S)
+{
+    return (size_t)WPB * (8 * S + 8);
+}
+
+// Workgroup verdict on the staged activations, the same in every wave: the
+// mask of vectors t (bit t) that must take the per-element path, because a
+// thread met an infinity or NaN in it (bit t of bad) or because its summed
+// A - TAU^2 B of q8_put is positive (the fixed point is not precise enough
+// for it).  The sums run in a fixed order.  Contains the workgroup barrier
+// that publishes the staged activations.  lds: an 8-byte aligned area of
+// verdict_bytes(WPB, S) bytes.
+template <int WPB, int S>
+__device__ __forceinline__ int stage_verdict(uint32_t bad, const double (&dsum)[S], void *lds)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    double *dw = reinterpret_cast<double *>(lds);            // [WPB][S]
+    int *fw = reinterpret_cast<int *>(dw + WPB * S);           // [WPB]
+    uint32_t wbad = 0;
+#pragma unroll
+    for (int t = 0; t < S; t++) wbad |= (__ballot((bad >> t) & 1u) != 0) ? 1u << t : 0u;
+    double r[S];
+#pragma unroll
+    for (int t = 0; t < S; t++) r[t] = wave_sum_f64(dsum[t]);
+    if (lane == 63) {
+#pragma unroll
+        for (int t = 0; t < S; t++) dw[wave * S + t] = r[t];
+        fw[wave] = (int)wbad;
+    }
+    __syncthreads();
+    int v = 0;
+#pragma unroll
+    for (int t = 0; t < S; t++) {
+        double sum = 0.0;
+#pragma unroll
+        for (int k = 0; k < WPB; k++) sum += dw[k * S + t];
+        v |= sum > 0.0 ? 1 << t : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < WPB; k++) v |= fw[k];
+    return __builtin_amdgcn_readfirstlane(v);
 }
 
 // ---------------------------------------------------------------------------

@@ -26,16 +26,22 @@ def test_more_than_one_gpu_exits_with_a_message(n):
     assert "one GPU" in r.stderr
 
 
-def test_default_case_is_the_resident_projection():
-    # the headline workload: 12288 x 6144 grouped int4, groups of 64
-    assert bench.CASE_NAMES[0] == "i4g_O12288_I6144_gs64"
+def test_headline_is_the_largest_batch1_dense_gemv():
+    # the headline workload: fp8 7168 x 16384 (117.6 MB per call), the largest
+    # batch-1 dense GEMV; the default suite covers every workload shape
+    assert bench.HEADLINE == "fp8b128_O7168_I16384"
+    assert bench.HEADLINE in bench.SUITE
+    import workloads as W
+    for name in W.WORKLOADS:
+        assert name in bench.SUITE, name
+    assert "mq4v2rot_O8192_I8192" in bench.SUITE
     assert len(set(bench.CASE_NAMES)) == len(bench.CASE_NAMES)
 
 
 def test_kernel_sources_exist_and_digest_is_stable():
-    csrc = os.path.join(ROOT, "quantized_weight_decode_amd", "csrc")
+    pkg = os.path.join(ROOT, "quantized_weight_decode_amd")
     for kernel, src in bench.KERNEL_SOURCES.items():
-        assert os.path.exists(os.path.join(csrc, src)), src
+        assert os.path.exists(os.path.join(pkg, src)), src
         d = bench.kernel_digest(kernel)
         assert re.fullmatch(r"[0-9a-f]{64}", d) and d == bench.kernel_digest(kernel)
 

@@ -3,17 +3,20 @@
 Shapes follow colibri PR #457, section 5 (I a multiple of gs, I = 200 / 201,
 I <= gs, S = 1..4, an activation forced to 50.0 in group 0) plus the
 workload shapes O=256 x I=512 and O=12288 x I=6144 at gs = 64 and 128.
-Decoded weights must match bit for bit; y to relative L2 <= 1e-5.  Four
-vectors of rows in whole 64-column blocks run on the int8 matrix cores
-(activations in a 22-bit fixed point per 64 columns): their cases include
-scale groups of one, two and three blocks, infinities and a twelve-decade
-dynamic range.
+Decoded weights must match bit for bit (the decode-only export, and one-hot
+activations through the streaming GEMV itself); y to relative L2 <= 1e-5 and
+every element to |dy| / sum_i |w_i x_i| <= 1e-4.  The cases include several
+vectors per call, infinities, a twelve-decade dynamic range, and outliers on
+a column whose weights are all zero (the staged fixed point is then not
+precise enough and the kernel multiplies per element in f32).  Canary zones
+around y catch stray writes.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from gpu_util import assert_bits_equal, assert_y_close, dev, host, torch_cuda
+from gpu_util import (assert_bits_equal, assert_guard_intact, assert_y_close, dev, guarded, host,
+                      magnitude, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,14 +46,53 @@ def test_dequant_bit_exact(q, qref, O, I, gs):
     (1, 32, 32, 1), (1, 1, 2, 1),
     # several vectors: 16-wave workgroups; S > 4 runs as groups of streaming launches
     (12288, 6144, 64, 2), (4000, 6144, 64, 4), (300, 1024, 64, 6), (65, 6144, 64, 7),
-    # four vectors on the int8 matrix cores: scale groups of one, two and three
-    # 64-column blocks, ragged row blocks
+    # four vectors, scale groups of one, two and three 64-column blocks, ragged
+    # row blocks
     (1000, 6144, 128, 4), (96, 4096, 192, 4), (17, 64, 64, 4), (12288, 6144, 64, 4),
 ])
 def test_gemv_matches_oracle(q, qref, O, I, gs, S):
     d = W.gen_i4g(O, I, gs, S=S, seed=7 * O + I)
     y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), gs))
-    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
+    mag = magnitude(qref.i4g_dequant(d["w"], d["scales"], O, I, gs), d["x"])
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs), mag=mag)
+
+
+@pytest.mark.parametrize("S,big", [(1, 1e3), (1, 1e4), (4, 1e4), (2, 3e5)])
+def test_outlier_on_zero_weight_column(q, qref, S, big):
+    # an activation 1e3..3e5 times its chunk neighbours on a column whose
+    # weights are all zero (nibble 8): the outlier contributes nothing, so y
+    # rests on the neighbours, which a fixed point sharing the outlier's
+    # exponent would carry to about 2^-21 * big only
+    O, I, gs = 512, 6144, 64
+    d = W.gen_i4g(O, I, gs, S=S, seed=int(big) + S)
+    col = 130
+    b = d["w"][:, col // 2]
+    d["w"][:, col // 2] = (b & 0xF0) | 0x08 if col % 2 == 0 else (b & 0x0F) | 0x80
+    d["x"][:, col] = big
+    Wd = qref.i4g_dequant(d["w"], d["scales"], O, I, gs)
+    assert np.all(Wd[:, col] == 0.0)
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), gs))
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs),
+                   mag=magnitude(Wd, d["x"]))
+
+
+@pytest.mark.parametrize("O,I,gs,S", [(256, 2048, 64, 1), (300, 6144, 128, 1), (96, 4096, 64, 4)])
+def test_one_hot_columns_bit_exact(q, qref, O, I, gs, S):
+    # x = e_j (1.0) through the streaming GEMV: the fixed point of 1.0 is
+    # exact, so y is the decoded column j, (q - 8) * s with one rounding
+    import torch
+    d = W.gen_i4g(O, I, gs, seed=O + 3)
+    Wd = qref.i4g_dequant(d["w"], d["scales"], O, I, gs)
+    wt, st = dev(d["w"]), dev(d["scales"])
+    cols = [0, 1, 7, 8, 31, 32, 33, 63, 64, gs - 1, gs, I // 2 + 5, I - 2, I - 1]
+    for c0 in range(0, len(cols), S):
+        cs = cols[c0:c0 + S]
+        x = torch.zeros((len(cs), I), device="cuda")
+        for t, j in enumerate(cs):
+            x[t, j] = 1.0
+        y = host(q.i4g(wt, st, x, gs))
+        for t, j in enumerate(cs):
+            assert_bits_equal(y[t], Wd[:, j])
 
 
 @pytest.mark.parametrize("I", [512, 201])
@@ -58,7 +100,8 @@ def test_outlier_activation(q, qref, I):
     d = W.gen_i4g(64, I, 64, seed=3)
     d["x"][0, 5] = 50.0
     y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
-    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], 64, I, 64))
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], 64, I, 64),
+                   mag=magnitude(qref.i4g_dequant(d["w"], d["scales"], 64, I, 64), d["x"]))
 
 
 def test_magnitude_relative_error(q, qref):
@@ -105,7 +148,8 @@ def test_wide_dynamic_range_activations(q, qref, O, I, S):
     x[:, 130] = 1e4 * np.abs(x[:, 131]).max() + 1.0
     d["x"] = x.astype(np.float32)
     y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
-    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, 64))
+    assert_y_close(y, qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, 64),
+                   mag=magnitude(qref.i4g_dequant(d["w"], d["scales"], O, I, 64), d["x"]))
 
 
 def test_zero_activations_give_zero(q):
@@ -131,14 +175,28 @@ def test_misaligned_weights_take_general_path(q, qref):
     assert_y_close(host(y), qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
 
 
+@pytest.mark.parametrize("O,I,gs,S", [(37, 512, 64, 1), (300, 6144, 64, 4), (20, 201, 64, 2)])
+def test_canaries_around_y(q, qref, O, I, gs, S):
+    import torch
+    d = W.gen_i4g(O, I, gs, S=S, seed=O + S)
+    yv, buf, fill = guarded(torch, S * O, torch.float32)
+    # inputs held in locals: a temporary's memory could be reused before the launch
+    wt, sc, xt = dev(d["w"]), dev(d["scales"]), dev(d["x"])
+    st = q.qgemv_i4g(wt.data_ptr(), sc.data_ptr(), xt.data_ptr(), yv.data_ptr(), S, I, O, gs,
+                     torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert_guard_intact(buf, S * O, fill)
+    assert_y_close(host(yv).reshape(S, O), qref.i4g_gemv(d["w"], d["scales"], d["x"], O, I, gs))
+
+
 def test_output_rows_outside_o_untouched(q):
     import torch
     d = W.gen_i4g(37, 512, 64, S=2, seed=6)
     y = torch.full((2, 37 + 64), 7.0, device="cuda")
-    yv = y[:, :37]
     # write through the raw ABI into a wider buffer: rows >= O must stay 7.0
-    st = q.qgemv_i4g(dev(d["w"]).data_ptr(), dev(d["scales"]).data_ptr(), dev(d["x"]).data_ptr(),
-                     y.data_ptr(), 2, 512, 37, 64, torch.cuda.current_stream().cuda_stream)
+    wt, sc, xt = dev(d["w"]), dev(d["scales"]), dev(d["x"])
+    st = q.qgemv_i4g(wt.data_ptr(), sc.data_ptr(), xt.data_ptr(), y.data_ptr(), 2, 512, 37, 64,
+                     torch.cuda.current_stream().cuda_stream)
     assert st == 0
     flat = host(y).reshape(-1)
     assert np.all(flat[2 * 37:] == 7.0)

@@ -5,13 +5,18 @@ chosen by weight index) and section 1e (a discriminating fixture).  The
 rotation is the orthonormal Sylvester FWHT-256 with signs applied first
 (the reading stated in the oracle); the GPU does radix-2 butterflies in f32,
 so x_rot is compared with a tolerance: relative L2 <= 1e-6 per call (eight
-rounding stages of 2^-24).
+rounding stages of 2^-24).  y: relative L2 <= 1e-5 and every element within
+1e-4 of sum_i |w_i x_i|.  The streaming kernel forms sum_i w_i x_i as
+scale * sum (q - 8) x + (8 scale + zero) * sum x, which rounds 8 scale + zero
+once more than the definition's q * scale + zero; one-hot activations show
+each recovered weight within that bound.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from gpu_util import assert_bits_equal, assert_y_close, dev, host, rel_l2, torch_cuda
+from gpu_util import (assert_bits_equal, assert_guard_intact, assert_y_close, dev, guarded, host,
+                      magnitude, rel_l2, torch_cuda)
 from test_oracle_mq4v2 import handbuilt_fixture
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +52,108 @@ def test_dequant_bit_exact(q, qref, O, I):
 def test_gemv_matches_oracle(q, qref, O, I, S):
     d = W.gen_mq4v2(O, I, S=S, seed=O + 7)
     y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), dev(d["x"])))
-    assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I))
+    mag = magnitude(qref.mq4v2_dequant(d["w"], O, I), d["x"])
+    assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I), mag=mag)
+
+
+def _zero_half(d, g, h):
+    """Sets every row's header of group g, half h to scale 0, zero 0 (all its
+    128 weights decode to 0)."""
+    d["w"][:, g, 4 * h:4 * h + 4] = 0
+
+
+def _unrotate(x_rot, signs, I):
+    """x whose FWHT-256 pre-rotation is x_rot (the transform is its own
+    inverse up to the signs): x = signs * (H256 x_rot) / 16, in f64."""
+    from scipy.linalg import hadamard
+    H = hadamard(256).astype(np.float64)
+    xr = np.asarray(x_rot, np.float64).reshape(-1, I // 256, 256)
+    return (np.einsum("ij,sbj->sbi", H, xr).reshape(-1, I) / 16.0) * signs.astype(np.float64)
+
+
+@pytest.mark.parametrize("S,big,rot", [(1, 1e3, False), (1, 1e4, False), (2, 1e4, False),
+                                       (1, 1e4, True), (2, 3e4, True)])
+def test_outlier_on_zero_weight_column(q, qref, S, big, rot):
+    # an activation big times its neighbours where every row's weights are
+    # zero: y rests on the neighbours, which a fixed point sharing the
+    # outlier's exponent would carry to about 2^-21 * big only
+    O, I = 512, 4096
+    d = W.gen_mq4v2(O, I, S=S, seed=int(big) + S)
+    _zero_half(d, 3, 0)
+    col = 3 * 256 + 40
+    w = dev(d["w"].reshape(O, -1))
+    Wd = qref.mq4v2_dequant(d["w"], O, I)
+    assert np.all(Wd[:, col] == 0.0)
+    if rot:
+        xr = qref.fwht256(d["x"], d["signs"], I)
+        xr[:, col] = big
+        x = _unrotate(xr, d["signs"], I).astype(np.float32)
+        xd, sg = dev(x), dev(d["signs"])
+        y = host(q.mq4v2_rot(w, xd, sg))
+        # the reference GEMV takes the rotation the GPU computed (qgemv_fwht256,
+        # bit-identical to the fused one): an f32 rotation of a block this
+        # large carries its own rounding, which the FWHT tests bound
+        xr = host(q.fwht256(xd, sg))
+    else:
+        xr = d["x"].copy()
+        xr[:, col] = big
+        y = host(q.mq4v2(w, dev(xr)))
+    assert np.abs(xr[:, col]).min() > 0.5 * big
+    assert_y_close(y, qref.mq4v2_gemv(d["w"], xr, O, I), mag=magnitude(Wd, xr))
+
+
+def test_one_hot_columns_within_two_roundings(q, qref):
+    # x = e_j: y[o] = scale * (q - 8) + (8 scale + zero), rounded twice; the
+    # definition rounds q * scale + zero once
+    import torch
+    O, I = 256, 2048
+    d = W.gen_mq4v2(O, I, seed=17)
+    Wd = qref.mq4v2_dequant(d["w"], O, I).astype(np.float64)
+    w = dev(d["w"].reshape(O, -1))
+    G = I // 256
+    sc = d["sc16"].astype(np.float64)   # [O][G][2]
+    zp = d["zp16"].astype(np.float64)
+    for j in [0, 1, 31, 32, 127, 128, 129, 255, 256, 1000, I - 1]:
+        x = torch.zeros((1, I), device="cuda")
+        x[0, j] = 1.0
+        got = host(q.mq4v2(w, x))[0].astype(np.float64)
+        g, h = j // 256, (j % 256) // 128
+        off = 8.0 * sc[:, g, h] + zp[:, g, h]
+        bound = 2.0 ** -24 * (np.abs(off) + np.abs(Wd[:, j])) * 1.0000001
+        assert np.all(np.abs(got - Wd[:, j]) <= bound), f"column {j}"
+
+
+@pytest.mark.parametrize("rot", [False, True])
+def test_canaries_around_y(q, qref, rot):
+    import torch
+    O, I, S = 300, 2048, 2
+    d = W.gen_mq4v2(O, I, S=S, seed=31)
+    yv, buf, fill = guarded(torch, S * O, torch.float32)
+    w, x, sg = dev(d["w"].reshape(O, -1)), dev(d["x"]), dev(d["signs"])
+    sp = torch.cuda.current_stream().cuda_stream
+    if rot:
+        st = q.qgemv_mq4v2_rot(w.data_ptr(), x.data_ptr(), sg.data_ptr(), yv.data_ptr(), S, I, O,
+                               sp)
+        xr = qref.fwht256(d["x"], d["signs"], I)
+    else:
+        st = q.qgemv_mq4v2(w.data_ptr(), x.data_ptr(), yv.data_ptr(), S, I, O, sp)
+        xr = d["x"]
+    assert st == 0
+    assert_guard_intact(buf, S * O, fill)
+    assert_y_close(host(yv).reshape(S, O), qref.mq4v2_gemv(d["w"], xr, O, I))
+
+
+def test_fwht_canaries(q):
+    import torch
+    S, I = 3, 512
+    x = dev(np.random.default_rng(5).standard_normal((S, I)).astype(np.float32))
+    sg = dev(W.gen_fwht_signs(I))
+    pad = 256
+    yv, buf, fill = guarded(torch, S * I, torch.float32, pad=pad)
+    st = q.qgemv_fwht256(x.data_ptr(), sg.data_ptr(), yv.data_ptr(), S, I,
+                         torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert_guard_intact(buf, S * I, fill, pad=pad)
 
 
 @pytest.mark.parametrize("O,I,S", [(256, 512, 1), (8192, 8192, 1), (300, 2048, 2)])
@@ -82,7 +188,8 @@ def test_wide_dynamic_range_activations(q, qref, O, I, S):
     x[:, 130] = 1e4 * np.abs(x[:, 131]).max() + 1.0
     d["x"] = x.astype(np.float32)
     y = host(q.mq4v2(dev(d["w"].reshape(O, -1)), dev(d["x"])))
-    assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I))
+    assert_y_close(y, qref.mq4v2_gemv(d["w"], d["x"], O, I),
+                   mag=magnitude(qref.mq4v2_dequant(d["w"], O, I), d["x"]))
 
 
 def test_unaligned_rows_take_general_path(q, qref):

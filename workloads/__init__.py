@@ -237,6 +237,30 @@ def gen_moe_routing(E: int, T: int, K: int, seed: int) -> tuple[np.ndarray, np.n
     return ids, gates
 
 
+def gen_moe_routings_disjoint(E: int, T: int, K: int, n: int, first: tuple,
+                              seed: int = 1000) -> list:
+    """n routings for timing: routing 0 is ``first`` (ids, gates); routing r
+    draws each token's K experts uniformly without replacement from the
+    experts routing r - 1 did not select (and, for the last one, not routing 0
+    either, so a cycle through them never repeats an expert between calls).
+    Gates as in gen_moe_routing.  Returns a list of (ids, gates)."""
+    out = [first]
+    used0 = set(np.unique(first[0]).tolist())
+    for r in range(1, n):
+        rng = np.random.default_rng(seed + r)
+        banned = set(np.unique(out[-1][0]).tolist())
+        if r == n - 1:
+            banned |= used0
+        allowed = np.array([e for e in range(E) if e not in banned], dtype=np.int64)
+        if allowed.size < K:
+            raise ValueError("too few experts left to draw a disjoint routing")
+        ids = np.stack([rng.choice(allowed, K, replace=False) for _ in range(T)]).astype(np.int32)
+        logits = rng.standard_normal((T, K))
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        out.append((ids, (e / e.sum(axis=1, keepdims=True)).astype(np.float32)))
+    return out
+
+
 def gen_moe(E: int, O: int, I: int, gs: int, T: int, K: int, seed: int = 0,
             routing_seed: int | None = None) -> dict:
     """Routed-expert inputs: E grouped-int4 experts of shape [O x I].
