@@ -55,13 +55,15 @@ const char *qgemv_version(void);
  *                             for odd I the last high nibble is ignored
  *   scales  f32 [O][ceil(I/gs)]  weight (o,i) = (nibble - 8) * scales[o][i/gs]
  *   x       f32 [S][I],  y f32 [S][O]
- *   gs      even, >= 2; any I >= 1 (a last partial group is allowed)
+ *   gs      even, 2 .. 2^24; any I >= 1 (a last partial group is allowed)
  * Rows whose bytes are 16-byte aligned (I % 32 == 0, w and x 16-byte
  * aligned) with gs % 32 == 0 take the streaming kernel (S > 4 runs in groups
- * of up to 4 vectors, each group streaming the weights once); a group of
- * exactly four vectors with I % 64 == 0, gs % 64 == 0 and I up to 8896 runs
- * on the int8 matrix cores instead (activations in a 22-bit fixed point per
- * 64 columns, integer block sums exact).  Every other valid shape takes a
+ * of up to 4 vectors, each group streaming the weights once).  It stages x
+ * per 32 columns as a 22-bit shared-exponent fixed point and forms exact
+ * integer nibble x digit sums, accumulated in f32; activations holding an
+ * infinity or NaN, or whose estimated error in that form would exceed
+ * 3e-6 relative on y (a large value next to much smaller ones), are
+ * multiplied per element in f32 instead.  Every other valid shape takes a
  * slower general kernel with the same result definition.
  */
 int qgemv_i4g(const void *w, const float *scales, const float *x, float *y,
@@ -211,13 +213,16 @@ int qgemv_router_topk(const float *logits, int T, int E, int ld, int K, int32_t 
  *            y NaN (it is never dereferenced) and sets a flag in the
  *            workspace (qgemv_moe_topk_error)
  *   gates    f32 [T][K],  x f32 [T][I],  y f32 [T][O] (overwritten)
- *   T in 1..8, K in 1..64, gs even >= 2
+ *   T in 1..8, K in 1..64, gs even 2 .. 2^24
  *   workspace  device scratch of at least qgemv_moe_topk_workspace(T, K, O)
- *              bytes, 4-byte aligned; its contents are overwritten.
- * Each token streams each distinct expert it selected once (an id repeated
- * within a token is read once and counted per slot; an expert selected by
- * several tokens is read once per selecting token).  The routing never
- * leaves the device.
+ *              bytes, 4-byte aligned: the per-token error flags; its
+ *              contents are overwritten.
+ * Each distinct expert of the call is streamed once: every token that
+ * selected it is multiplied from the same weight registers (an id repeated
+ * within a token is counted per slot).  When T * K > 64, or the tokens'
+ * staged activations exceed the LDS (about seven of 7168 columns), the
+ * tokens run in groups and an expert shared across groups is read once per
+ * group.  The routing never leaves the device.
  */
 size_t qgemv_moe_topk_workspace(int T, int K, int O);
 int qgemv_moe_topk(const void *w, const float *scales, long long w_stride,
@@ -230,9 +235,15 @@ int qgemv_moe_topk(const void *w, const float *scales, long long w_stride,
 int qgemv_moe_topk_error(const void *workspace, int *flag, void *stream);
 
 /*
- * Decode-only entry points: write the decoded f32 weights W[O][I] using the
- * same device decode code as the GEMVs (the decoded values must match the
- * format definitions bit for bit).  Arguments as the GEMV of the same format.
+ * Decode-only entry points: write the decoded f32 weights W[O][I], each the
+ * format's definition rounded once to f32 -- grouped int4 (q - 8) * s
+ * (colibri PR #457, section 3), fp8 e4m3 * block scale (colibri PR #528,
+ * section "Design"), MQ4 q * scale + zero (hipfire "MQ4 V2", sections 1b,
+ * 1e and 4) -- with the device's nibble / fp8 / fp16 converters.  They are
+ * the bit-exact decode check of those converters and layouts.  The 4-bit
+ * GEMVs do not form these values: they multiply q - 8 (packed nibbles XOR 8)
+ * with fixed-point activation digits; their decode is checked through
+ * one-hot activations instead.  Arguments as the GEMV of the same format.
  */
 int qgemv_dequant_i4g(const void *w, const float *scales, float *W, int I,
                       int O, int gs, void *stream);

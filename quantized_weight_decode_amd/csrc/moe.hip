@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     u32x4 wb[PF][R];
     float sb[PF][R];
     // each ring slot records the unit and sweep its loads belong to
-    // (unit >= nunits: nothing, the loads re-read the previous step)
+    // (unit >= nunits: nothing; the loads read the activations)
     int slot_u[PF], slot_c[PF];
     uint32_t slot_t[PF];
     // fetch cursor: unit fi, sweep fc
@@ -243,13 +243,18 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
         slot_u[j] = fi;
         slot_c[j] = fc;
         slot_t[j] = fi < nunits ? fu.toks : 0u;
-        const uint8_t *we = w + (size_t)fu.e * (size_t)w_stride;
-        const float *se = scales + (size_t)fu.e * (size_t)s_stride;
+        // past the wave's last unit the refills (unconditional, so that the
+        // waits count exactly) read the activations, which the caches hold,
+        // instead of streaming weights from memory again
+        const bool live = fi < nunits;
+        const uint8_t *we = live ? w + (size_t)fu.e * (size_t)w_stride
+                                 : reinterpret_cast<const uint8_t *>(x);
+        const float *se = live ? scales + (size_t)fu.e * (size_t)s_stride : x;
         const int u = min(fc * LPR + sl, NU - 1);
         const uint32_t g = div_cpg((uint32_t)u);
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const int row = min(fu.row0 + r, O - 1);
+            const int row = live ? min(fu.row0 + r, O - 1) : 0;
             wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(we + (size_t)row * rb +
                                                                  (uint32_t)u * 16u));
             sb[j][r] = ld_stream(se + (size_t)row * ng + g);
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
                     fc = 0;
                     fu = unit_of(fi);
                 } else {
-                    fi = nunits;   // done; keep re-reading the last step
+                    fi = nunits;   // done
                 }
             }
         }
