@@ -235,6 +235,23 @@ int qgemv_moe_topk(const void *w, const float *scales, long long w_stride,
 int qgemv_moe_topk_error(const void *workspace, int *flag, void *stream);
 
 /*
+ * qgemv_moe_topk for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid it): the same
+ * arguments without the workspace, the same kernels and the same y.  The
+ * per-token error flags go to a fixed 256-byte device array of the library
+ * (one per GPU, held until the process ends) and are not readable through
+ * the ABI; an out-of-range id still makes its token's row of y NaN.  No
+ * host or device memory is allocated.  Calls that overlap on one GPU share
+ * that array and race on the flags (y is unaffected).  Refusals as
+ * qgemv_moe_topk; QGEMV_E_WORKSPACE if the flags would not fit the array
+ * (never for T <= 8).
+ */
+int qgemv_moe_topk_noalloc(const void *w, const float *scales, long long w_stride,
+                           long long s_stride, int E, const int32_t *ids, const float *gates,
+                           int T, int K, const float *x, float *y, int I, int O, int gs,
+                           void *stream);
+
+/*
  * Decode-only entry points: write the decoded f32 weights W[O][I], each the
  * format's definition rounded once to f32 -- grouped int4 (q - 8) * s
  * (colibri PR #457, section 3), fp8 e4m3 * block scale (colibri PR #528,

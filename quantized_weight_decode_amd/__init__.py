@@ -53,6 +53,10 @@ _SIGS = {
                                  C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                  C.c_void_p, C.c_size_t, C.c_void_p]),
     "qgemv_moe_topk_error": (C.c_int, [C.c_void_p, C.POINTER(C.c_int), C.c_void_p]),
+    "qgemv_moe_topk_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_longlong, C.c_longlong,
+                                         C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                         C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                         C.c_void_p]),
     "qgemv_dequant_i4g": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "qgemv_dequant_fp8b128": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p,
@@ -168,6 +172,12 @@ def qgemv_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, 
                    workspace, ws_bytes, stream):
     return lib().qgemv_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
                                 I, O, gs, workspace, ws_bytes, stream)
+
+
+def qgemv_moe_topk_noalloc(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y, I, O, gs,
+                           stream):
+    return lib().qgemv_moe_topk_noalloc(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
+                                        I, O, gs, stream)
 
 
 def qgemv_dequant_i4g(w, scales, W, I, O, gs, stream):

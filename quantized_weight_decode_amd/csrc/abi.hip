@@ -70,6 +70,42 @@ namespace {
 
 constexpr int MAX_DIM = 1 << 24;
 
+// The calling thread's current device's address of `scratch` (below),
+// looked up once per device (with that device current) and kept; no host or
+// device memory is allocated.
+constexpr int MAX_DEVICES = 64;
+hipError_t scratch_address(void **out);
+
+}  // namespace
+
+// Device memory of the allocation-free routed-expert call: its per-token
+// error flags (what the workspace of qgemv_moe_topk holds).  Each GPU has its
+// own copy at its own address; host code uses that address (scratch_address),
+// never this name, which on the host is only a stand-in.
+static __device__ __align__(256) int scratch[qg::MOE_WORKSPACE_BYTES / sizeof(int)];
+
+namespace {
+
+hipError_t scratch_address(void **out)
+{
+    static std::mutex mu;
+    static void *addr[MAX_DEVICES];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
 bool mis4(const void *p) { return ((uintptr_t)p & 3) != 0; }
 
 bool bad_gs(int gs) { return gs < 2 || (gs & 1) || gs > MAX_DIM; }
@@ -290,6 +326,28 @@ int qgemv_moe_topk(const void *w, const float *scales, long long w_stride, long 
     return launched(qg::launch_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
                                         I, O, gs, static_cast<int *>(workspace),
                                         (hipStream_t)stream));
+}
+
+int qgemv_moe_topk_noalloc(const void *w, const float *scales, long long w_stride,
+                           long long s_stride, int E, const int32_t *ids, const float *gates,
+                           int T, int K, const float *x, float *y, int I, int O, int gs,
+                           void *stream)
+{
+    if (!w || !scales || !ids || !gates || !x || !y) return QGEMV_E_NULL;
+    if (T < 1 || T > QGEMV_MAX_S || K < 1 || K > 64 || E < 1 || I < 1 || O < 1 ||
+        I > MAX_DIM || O > MAX_DIM)
+        return QGEMV_E_DIMS;
+    if (bad_gs(gs)) return QGEMV_E_GS;
+    if (mis4(scales) || mis4(ids) || mis4(gates) || mis4(x) || mis4(y)) return QGEMV_E_ALIGN;
+    const long long rb = ((long long)I + 1) / 2, ng = ((long long)I + gs - 1) / gs;
+    if (w_stride < (long long)O * rb || s_stride < (long long)O * ng) return QGEMV_E_IDS;
+    // the flags' room in the device array (the same size as the workspace
+    // qgemv_moe_topk asks for)
+    if (qgemv_moe_topk_workspace(T, K, O) > sizeof(scratch)) return QGEMV_E_WORKSPACE;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess || !ws) return QGEMV_E_HIP;
+    return launched(qg::launch_moe_topk(w, scales, w_stride, s_stride, E, ids, gates, T, K, x, y,
+                                        I, O, gs, static_cast<int *>(ws), (hipStream_t)stream));
 }
 
 int qgemv_moe_topk_error(const void *workspace, int *flag, void *stream)
