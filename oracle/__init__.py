@@ -24,9 +24,17 @@ CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
           "-Wall", "-Wextra", "-Werror", "-shared", "-fPIC"]
 
 
-def build(out: str = LIB, mutate: int = 0) -> str:
-    """Compile qref.c (optionally with planted mistake ``mutate``) to ``out``."""
-    cmd = ["gcc", *CFLAGS, f"-DQREF_MUTATE={int(mutate)}", SRC, "-o", out, "-lm"]
+# AddressSanitizer and UndefinedBehaviorSanitizer build (host code only); any
+# report aborts the process
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-g",
+            "-fno-omit-frame-pointer"]
+
+
+def build(out: str = LIB, mutate: int = 0, sanitize: bool = False) -> str:
+    """Compile qref.c (optionally with planted mistake ``mutate``, or with the
+    address and undefined-behaviour sanitizers) to ``out``."""
+    cmd = ["gcc", *CFLAGS, *(SANITIZE if sanitize else []), f"-DQREF_MUTATE={int(mutate)}", SRC,
+           "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -245,10 +253,12 @@ _default = None
 
 
 def load() -> Oracle:
-    """The oracle built next to this file (built on first use if missing)."""
+    """The oracle built next to this file (built on first use if missing), or
+    the library the environment variable QREF_LIB names (a sanitizer build)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("QREF_LIB", LIB)
+        if path == LIB and not os.path.exists(LIB):
             build()
-        _default = Oracle(LIB)
+        _default = Oracle(path)
     return _default

@@ -40,6 +40,13 @@
 #define QG_FP8_PF0 4
 #endif
 
+// activation float4s each thread loads up front (the rest follow one round
+// trip later); ten, covering a 16384-column vector with 7 waves in one round
+// trip, measured no faster than eight (21.2 against 21.1 us)
+#ifndef QG_FP8_NPRE
+#define QG_FP8_NPRE 8
+#endif
+
 namespace qg {
 
 constexpr int FP8_FAST_MAX_S = 4;
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(64 * WPB) void fp8_gemv_stream(
         if (PH && c0 > 0) __syncthreads();   // every wave is done with the previous phase
 
         // activations first; every load unconditional
-        XStageF8<8, 64 * WPB> xst;
+        XStageF8<QG_FP8_NPRE, 64 * WPB> xst;
         const int total4 = S * NU * 4;
         xst.template load<PH>(x, total4, NU, I / 4, c0 * 4);
         // every wave of the workgroup has issued its activation loads before
