@@ -15,10 +15,9 @@
 //     integer dot product); a token whose activations hold an infinity or
 //     NaN, or a dynamic range the fixed point cannot carry precisely enough,
 //     is multiplied per element in f32 after the stream instead;
-//   * one wave reads the T*K ids and hands them over in LDS (lane l holds
-//     slot l = t*K + k); every wave derives with ballots the distinct valid
-//     experts in first-occurrence order -- the routing never leaves the
-//     device;
+//   * one wave reads the T*K ids (lane l holds slot l = t*K + k), finds with
+//     ballots the distinct valid experts in first-occurrence order, and hands
+//     both over in LDS -- the routing never leaves the device;
 //   * work units are (distinct expert, sub-tile of rows); a unit streams its
 //     rows of that expert once (dwordx4, scale gather) and multiplies every
 //     token that selected the expert with the same weight registers; each
@@ -146,7 +145,8 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     void *vlds = tail;                                                    // stage_verdict
     float *part = reinterpret_cast<float *>(tail + verdict_bytes(QG_MOE_WPB, TM));  // [TK][RT]
     int *ids_l = reinterpret_cast<int *>(part + (size_t)TK * RT);         // [64]
-    int *ctr = ids_l + 64;                                                // next unit
+    uint32_t *meta = reinterpret_cast<uint32_t *>(ids_l + 64);            // slot masks [4]
+    int *ctr = reinterpret_cast<int *>(meta + 4);                         // next unit
     float *xacc_base = reinterpret_cast<float *>(ctr + 1);   // [WPB][TM-1][R][64], zeroed
 
     const int o0 = blockIdx.x * RT;
@@ -159,17 +159,37 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const int nit = (NU + LPR - 1) / LPR;
     const int nsub = RT / ROWS_PER_WAVE;
 
-    // the ids (one wave; thousands of waves reading one line would queue on
-    // one L2 channel) and the activations, before any weight load
-    int id = 0;
-    if (wave == 0) id = ids[min(lane, TK - 1)];
+    // the activations, then the ids, before any weight load
     // two items per token and thread cover 7168 columns (at most eight up front)
     constexpr int NPRE = 2 * TM < 8 ? 2 * TM : 8;
     XStageQ<TM, NPRE, NT> xst;
     const int items = T * NU * 4;
     xst.load(x, items);
     __builtin_amdgcn_sched_barrier(0);
-    if (wave == 0) ids_l[lane] = id;
+    if (wave == 0) {
+        // One wave reads the ids (thousands of waves reading one line would
+        // queue on one L2 channel); lane l holds slot l = t*K + k.  It finds
+        // the distinct valid experts in first-occurrence order, one pass per
+        // distinct expert, and hands ids and slot masks over in LDS.  (Its
+        // wait for the ids also covers its activation loads, issued first.)
+        const int ev = lane < TK ? ids[min(lane, TK - 1)] : -1;
+        const bool ok = lane < TK && ev >= 0 && ev < E;
+        uint64_t rem = __ballot(ok), fm = 0;
+        while (rem) {
+            const int q = __builtin_ctzll(rem);
+            const int v = __builtin_amdgcn_readlane(ev, q);
+            fm |= 1ull << q;
+            rem &= ~__ballot(ev == v);
+        }
+        const uint64_t bm = __ballot(lane < TK && !ok);
+        ids_l[lane] = ev;
+        if (lane == 0) {
+            meta[0] = (uint32_t)fm;
+            meta[1] = (uint32_t)(fm >> 32);
+            meta[2] = (uint32_t)bm;
+            meta[3] = (uint32_t)(bm >> 32);
+        }
+    }
     if (threadIdx.x == 0) *ctr = nwaves;
 #pragma unroll
     for (int m = 0; m < (TM - 1) * R; m++)
@@ -180,14 +200,18 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // distinct valid experts over all slots, first-occurrence order
+    // the slots' ids, the first slot of each distinct valid expert, and the
+    // slots holding an id outside [0, E)
+    // (each half zero-extended; only the TK slot lanes can be set)
     const int e = lane < TK ? ids_l[lane] : -1;
-    const bool valid = lane < TK && e >= 0 && e < E;
-    bool first = valid;
-    for (int q = 0; q < TK; q++)
-        if (q < lane && __builtin_amdgcn_readlane(e, q) == e) first = false;
-    const uint64_t firstm = __ballot(first);
-    const uint64_t badm = __ballot(lane < TK && !valid);   // slots holding a bad id
+    const uint64_t slotm = TK >= 64 ? ~0ull : (1ull << TK) - 1;
+    auto mask64 = [&](int i) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)meta[i]);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)meta[i + 1]);
+        return ((uint64_t)hi << 32 | (uint64_t)lo) & slotm;
+    };
+    const uint64_t firstm = mask64(0);
+    const uint64_t badm = mask64(2);
     uint32_t badtok = 0;                                   // tokens with a bad id
     for (int t = 0; t < T; t++)
         if ((badm >> (t * K)) & (K == 64 ? ~0ull : ((1ull << K) - 1))) badtok |= 1u << t;
@@ -546,7 +570,7 @@ namespace {
 size_t moe_lds_bytes(int TM, int T, int K, int I, int RT)
 {
     return q8_verdict_offset(T, I / 32, false) + verdict_bytes(QG_MOE_WPB, TM) +
-           (size_t)T * K * RT * sizeof(float) + 65 * sizeof(int) +
+           (size_t)T * K * RT * sizeof(float) + 69 * sizeof(int) +
            (size_t)QG_MOE_WPB * (TM - 1) * QG_MOE_R * 64 * sizeof(float);
 }
 
