@@ -58,6 +58,13 @@ namespace qg {
 #ifndef QG_I4G_WPB_MULTI
 #define QG_I4G_WPB_MULTI 12
 #endif
+// Lanes per row for several vectors (at most).  Measured at 12288 x 6144:
+// 64 lanes x 4 rows x 12 waves 14.1 / 24.0 us at two / four vectors against
+// 11.3 / 19.6 us for 32 x 2 x 12; refilling a ring slot before its products
+// instead of after them gained nothing (the products are VALU-bound).
+#ifndef QG_I4G_LPR_MULTI
+#define QG_I4G_LPR_MULTI 32
+#endif
 
 // activation items (8 columns each) each thread loads up front
 #ifndef QG_I4G_NPRE
@@ -197,14 +204,20 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
     for (int t = 0; t < S; t++)
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
-    // one vector: running digit sums per row (see q8_dot_run)
-    uint32_t P[R][6], V[R];
+    // running digit sums per vector and row (see q8_dot_run), so no
+    // accumulator is cleared per chunk, where the registers allow; otherwise
+    // fresh sums per chunk
+    constexpr bool RUN = S * R <= 8;
+    constexpr int SR = RUN ? S : 1;
+    uint32_t P[SR][R][6], V[SR][R];
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-        V[r] = 0;
+    for (int t = 0; t < SR; t++)
 #pragma unroll
-        for (int k = 0; k < 6; k++) P[r][k] = 0;
-    }
+        for (int r = 0; r < R; r++) {
+            V[t][r] = 0;
+#pragma unroll
+            for (int k = 0; k < 6; k++) P[t][r][k] = 0;
+        }
 
     // 4. sweep in rounds of PF chunk-sweeps: consume ring slot j, then refill
     //    it with the sweep one round ahead.  All refills are unconditional
@@ -229,7 +242,9 @@ __global__ __launch_bounds__(64 * WPB) void i4g_gemv_stream(
             const float cs = valid ? xc[(size_t)t * NU + uu] : 0.0f;
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const int dv = S == 1 ? q8_dot_run(wx[r], L, P[r], V[r]) : q8_dot(wx[r], L);
+                int dv;
+                if constexpr (RUN) dv = q8_dot_run(wx[r], L, P[t][r], V[t][r]);
+                else dv = q8_dot(wx[r], L);
                 acc[t][r] = __builtin_fmaf(sb[j][r] * cs, (float)dv, acc[t][r]);
             }
             if constexpr (S > 1) pin_values(acc[t]);   // one vector's digits live at a time
@@ -330,11 +345,13 @@ __global__ __launch_bounds__(256) void i4g_dequant(
 // ---------------------------------------------------------------------------
 namespace {
 
-// lanes per row: the fullest sweep, at most QG_I4G_LPR
-inline int i4g_lanes_per_row(int I)
+// lanes per row: the fullest sweep, at most QG_I4G_LPR (one vector) or
+// QG_I4G_LPR_MULTI (several)
+inline int i4g_lanes_per_row(int I, int S = 1)
 {
     const int lpr = pick_lpr(I / 32);
-    return lpr > QG_I4G_LPR ? QG_I4G_LPR : lpr;
+    const int cap = S == 1 ? QG_I4G_LPR : QG_I4G_LPR_MULTI;
+    return lpr > cap ? cap : lpr;
 }
 
 template <int S, int LPR, int R, int PF>
@@ -369,7 +386,7 @@ template <int S, int R>
 hipError_t launch_stream_r(const uint8_t *w, const float *s, const float *x, float *y, int I,
                            int O, int gs, hipStream_t st)
 {
-    const int lpr = i4g_lanes_per_row(I);
+    const int lpr = i4g_lanes_per_row(I, S);
     switch (lpr) {
     case 64: return launch_stream_pf<S, 64, R>(w, s, x, y, I, O, gs, st);
     case 32: return launch_stream_pf<S, 32, R>(w, s, x, y, I, O, gs, st);
@@ -392,7 +409,7 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
         // the larger R (fewer workgroups staging the vectors).  12288 rows,
         // two to four vectors: R = 2, 256 workgroups of 48 rows
         static const int cand[] = {3, 2, 1};
-        switch (pick_rows_per_group(O, i4g_lanes_per_row(I), QG_I4G_WPB_MULTI,
+        switch (pick_rows_per_group(O, i4g_lanes_per_row(I, S), QG_I4G_WPB_MULTI,
                                     i4g_stream_lds_bytes(S, I), cand, 3)) {
         case 1: return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
         case 2: return launch_stream_r<S, 2>(w, s, x, y, I, O, gs, st);

@@ -273,13 +273,20 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
     for (int t = 0; t < S; t++)
 #pragma unroll
         for (int r = 0; r < R; r++) acc[t][r] = 0.0f;
-    uint32_t P[R][6], V[R];   // one vector: running digit sums per row (see q8_dot_run)
+    // running digit sums per vector and row (see q8_dot_run) where the
+    // registers allow (16-wave workgroups have 128); otherwise fresh sums
+    // per chunk
+    constexpr bool RUN = S == 1 || (S == 2 && R <= 2);
+    constexpr int SR = RUN ? S : 1;
+    uint32_t P[SR][R][6], V[SR][R];
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-        V[r] = 0;
+    for (int t = 0; t < SR; t++)
 #pragma unroll
-        for (int k = 0; k < 6; k++) P[r][k] = 0;
-    }
+        for (int r = 0; r < R; r++) {
+            V[t][r] = 0;
+#pragma unroll
+            for (int k = 0; k < 6; k++) P[t][r][k] = 0;
+        }
 
     auto consume = [&](int c, int j) {
         const int u = c * LPR + sl;
@@ -303,7 +310,9 @@ __global__ __launch_bounds__(64 * WPB) void mq4v2_gemv_stream(
             const float xsum = valid ? xsm[(size_t)t * NU + uu] : 0.0f;
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const int dv = S == 1 ? q8_dot_run(wx[r], L, P[r], V[r]) : q8_dot(wx[r], L);
+                int dv;
+                if constexpr (RUN) dv = q8_dot_run(wx[r], L, P[t][r], V[t][r]);
+                else dv = q8_dot(wx[r], L);
                 const float off = __builtin_fmaf(8.0f, scl[r], zro[r]) * xsum;
                 acc[t][r] = __builtin_fmaf(scl[r] * cs, (float)dv, acc[t][r] + off);
             }
