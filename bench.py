@@ -643,6 +643,27 @@ def cpu_rate(case, threads, budget_s):
 # ---------------------------------------------------------------------------
 # Host record
 # ---------------------------------------------------------------------------
+SOURCE_GLOBS = ["bench.py", "include/*.h", "quantized_weight_decode_amd/*.py",
+                "quantized_weight_decode_amd/csrc/*", "quantized_weight_decode_amd/bench_csrc/*",
+                "workloads/*.py", "oracle/qref.c", "oracle/*.py"]
+
+
+def sources_digest():
+    """sha256 over the sources that decide what a run computes and times (path and
+    bytes of each, in sorted order): the record's link to a checkout where the
+    git metadata is not present (recompute with --sources-digest)."""
+    import glob
+    h = hashlib.sha256()
+    paths = sorted({p for g in SOURCE_GLOBS for p in glob.glob(os.path.join(ROOT, g))
+                    if os.path.isfile(p)})
+    for p in paths:
+        h.update(os.path.relpath(p, ROOT).encode() + b"\0")
+        with open(p, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def host_record(torch):
     def read(path):
         try:
@@ -681,6 +702,7 @@ def host_record(torch):
         "cus": props.multi_processor_count,
         "rocm": read("/opt/rocm/.info/version"), "torch": torch.__version__,
         "python": platform.python_version(), "git_sha": sha,
+        "sources_sha256": sources_digest(),
         "libqgemv_sha256": digest(lib),
         "env": {k: os.environ[k] for k in ("HIP_VISIBLE_DEVICES", "ROCR_VISIBLE_DEVICES",
                                            "GPU_MAX_HW_QUEUES", "HSA_XNACK")
@@ -719,7 +741,12 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-read ceilings")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only time a plain device copy of BYTES bytes")
+    ap.add_argument("--sources-digest", action="store_true",
+                    help="print the sources digest a record carries, and exit")
     args = ap.parse_args()
+    if args.sources_digest:
+        print(sources_digest())
+        return
 
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported (across GPUs "

@@ -61,3 +61,13 @@ def test_profile_summaries_parse():
         t = bench.profiled_traffic(kernel, workload)
         # None once the kernel's sources changed since the counters were taken
         assert t is None or t > 0
+
+
+def test_sources_digest_covers_the_kernels_and_is_stable():
+    d = bench.sources_digest()
+    assert re.fullmatch(r"[0-9a-f]{64}", d) and d == bench.sources_digest()
+    covered = {os.path.relpath(p, ROOT) for g in bench.SOURCE_GLOBS
+               for p in glob.glob(os.path.join(ROOT, g))}
+    for src in bench.KERNEL_SOURCES.values():
+        assert os.path.join("quantized_weight_decode_amd", src) in covered, src
+    assert "include/qgemv.h" in covered and "bench.py" in covered
