@@ -561,6 +561,16 @@ hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y
                     hipStream_t st)
 {
     if constexpr (S == 1) {
+        // one row per lane group where that puts fewer rows on the busiest CU
+        // (short matrices: the workgroups then spread over all CUs)
+        const long ncu = cu_count();
+        auto busiest = [&](int r) {
+            const long rows_wg = (long)QG_MQ4_WPB * (64 / pick_lpr(I / 32)) * r;
+            const long wgs = (O + rows_wg - 1) / rows_wg;
+            return (wgs + ncu - 1) / ncu * rows_wg;
+        };
+        if (QG_MQ4_R > 1 && busiest(1) < busiest(QG_MQ4_R))
+            return launch_r<HF, S, 1, ROT>(w, x, sg, y, I, O, st);
         return launch_r<HF, S, QG_MQ4_R, ROT>(w, x, sg, y, I, O, st);
     } else {
         // several vectors: R keeps every workgroup resident at once.  With the
