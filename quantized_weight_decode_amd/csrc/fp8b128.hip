@@ -378,6 +378,16 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
                     hipStream_t st)
 {
     if constexpr (S == 1) {
+        // one row per lane group where that puts fewer rows on the busiest
+        // CU (short matrices: the workgroups then spread over all CUs)
+        const long ncu = cu_count();
+        auto busiest = [&](int r) {
+            const long rows_wg = (long)QG_FP8_WPB * (64 / pick_lpr(I / 16)) * r;
+            const long wgs = (O + rows_wg - 1) / rows_wg;
+            return (wgs + ncu - 1) / ncu * rows_wg;
+        };
+        if (QG_FP8_R > 1 && busiest(1) < busiest(QG_FP8_R))
+            return launch_r<ST, S, 1>(w, sc, x, y, I, O, st);
         return launch_r<ST, S, QG_FP8_R>(w, sc, x, y, I, O, st);
     } else {
         // several vectors: R keeps every workgroup resident at once (the rows
