@@ -44,6 +44,9 @@ def test_dequant_bit_exact(q, qref, O, I, gs):
     (77, 200, 64, 2), (77, 201, 64, 1), (9, 64, 64, 1), (9, 40, 64, 4),
     (50, 512, 64, 8), (100, 1024, 96, 2), (31, 4096, 256, 1), (3, 96, 32, 1),
     (1, 32, 32, 1), (1, 1, 2, 1),
+    # tiles the launcher picks by rows on the busiest CU: two rows per lane
+    # group (16384 x 512), one row (20000 x 1024, ragged)
+    (16384, 512, 64, 1), (20000, 1024, 64, 1),
     # several vectors: 16-wave workgroups; S > 4 runs as groups of streaming launches
     (12288, 6144, 64, 2), (4000, 6144, 64, 4), (300, 1024, 64, 6), (65, 6144, 64, 7),
     # four vectors, scale groups of one, two and three 64-column blocks, ragged
