@@ -411,8 +411,6 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
 
     // rounds of PF slots: consume a slot, then refill it; stop once the
     // oldest slot of a round holds nothing (slots are filled in order)
-    // rounds of PF slots: consume a slot, then refill it; stop once the
-    // oldest slot of a round holds nothing (slots are filled in order)
     while (slot_u[0] < nunits) {
 #pragma unroll
         for (int j = 0; j < PF; j++) {
