@@ -159,20 +159,22 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
     const int nit = (NU + LPR - 1) / LPR;
     const int nsub = RT / ROWS_PER_WAVE;
 
-    // the activations, then the ids, before any weight load
+    // the ids (wave 0), then the activations, before any weight load.  One
+    // wave reads the ids (thousands of waves reading one line would queue on
+    // one L2 channel); lane l holds slot l = t*K + k.  The activation loads
+    // behind it are unconditional, so its wait for the ids counts them and
+    // lets them stay in flight.
     // two items per token and thread cover 7168 columns (at most eight up front)
     constexpr int NPRE = 2 * TM < 8 ? 2 * TM : 8;
     XStageQ<TM, NPRE, NT> xst;
     const int items = T * NU * 4;
-    xst.load(x, items);
+    const int ev = wave == 0 && lane < TK ? ids[min(lane, TK - 1)] : -1;
+    __builtin_amdgcn_sched_barrier(0);
+    xst.load_all(x, items);
     __builtin_amdgcn_sched_barrier(0);
     if (wave == 0) {
-        // One wave reads the ids (thousands of waves reading one line would
-        // queue on one L2 channel); lane l holds slot l = t*K + k.  It finds
         // the distinct valid experts in first-occurrence order, one pass per
-        // distinct expert, and hands ids and slot masks over in LDS.  (Its
-        // wait for the ids also covers its activation loads, issued first.)
-        const int ev = lane < TK ? ids[min(lane, TK - 1)] : -1;
+        // distinct expert; ids and slot masks are handed over in LDS
         const bool ok = lane < TK && ev >= 0 && ev < E;
         uint64_t rem = __ballot(ok), fm = 0;
         while (rem) {

@@ -328,7 +328,10 @@ __device__ __forceinline__ void fwht256_item(float v[8], int lane)
 // 8f .. 8f + 7 (two float4 loads), so a chunk is four consecutive lanes.
 // Each workgroup starts at its own aligned offset and wraps around, as
 // stage_rot describes.  load() issues the thread's first NPRE items (those that exist)
-// and store() converts them, then any further items one at a time.  Items
+// and store() converts them, then any further items one at a time
+// (load_all() issues all NPRE, past the end at clamped indices, so that the
+// count of loads in flight is the same in every thread and a wait for a load
+// issued before them is exact).  Items
 // past the end belong to whole lane groups (items is a multiple of 32 with
 // ROT, of 4 otherwise; NT a multiple of 64), which skip both.  NT is the
 // workgroup size; items may cover fewer than S vectors.  store() returns the
@@ -364,6 +367,19 @@ struct XStageQ {
                 if constexpr (ROT)
                     sg[j] = *reinterpret_cast<const u32x2 *>(signs + 8u * (g % (uint32_t)ipv));
             }
+        }
+    }
+
+    __device__ __forceinline__ void load_all(const float *__restrict__ x, int items)
+    {
+        static_assert(!ROT, "load_all stages unrotated vectors");
+        const unsigned groups = (unsigned)items / 4u;
+        rot = groups ? (int)(((blockIdx.x * 2654435761u) >> 7) % groups * 4u) : 0;
+#pragma unroll
+        for (int j = 0; j < NPRE; j++) {
+            const uint32_t g = (uint32_t)stage_index((int)threadIdx.x + j * NT, items, rot);
+            a[j] = ldx4(x, 2u * g);
+            b[j] = ldx4(x, 2u * g + 1u);
         }
     }
 
