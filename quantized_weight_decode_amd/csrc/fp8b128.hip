@@ -29,6 +29,14 @@
 #ifndef QG_FP8_WPB
 #define QG_FP8_WPB 7
 #endif
+// the alternative one-vector workgroup size (see launch_s), for rows of at
+// least QG_FP8_WPB2_MIN_I columns
+#ifndef QG_FP8_WPB2
+#define QG_FP8_WPB2 8
+#endif
+#ifndef QG_FP8_WPB2_MIN_I
+#define QG_FP8_WPB2_MIN_I 4096
+#endif
 // waves per workgroup for several vectors (S times the LDS per workgroup)
 #ifndef QG_FP8_WPB_MULTI
 #define QG_FP8_WPB_MULTI 16
@@ -356,11 +364,10 @@ hipError_t launch_t(const uint8_t *w, const ST *sc, const float *x, float *y, in
     return hipGetLastError();
 }
 
-template <typename ST, int S, int R>
+template <typename ST, int S, int R, int WPB = S == 1 ? QG_FP8_WPB : QG_FP8_WPB_MULTI>
 hipError_t launch_r(const uint8_t *w, const ST *sc, const float *x, float *y, int I, int O,
                     hipStream_t st)
 {
-    constexpr int WPB = S == 1 ? QG_FP8_WPB : QG_FP8_WPB_MULTI;
     // several vectors: 16-wave workgroups leave 128 registers per lane, so
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_FP8_PF : 2;
@@ -378,17 +385,40 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
                     hipStream_t st)
 {
     if constexpr (S == 1) {
-        // one row per lane group where that puts fewer rows on the busiest
-        // CU (short matrices: the workgroups then spread over all CUs)
+        // Tile: WPB waves of R rows per lane group.  The workgroups are dealt
+        // to the CUs in rounds, so the tile that fills its last round best
+        // (workgroups / (CUs x rounds)) wins, and among equals the one with
+        // the fewest workgroups.  Seven-wave two-row tiles fill two rounds
+        // exactly at 7168 rows; eight-wave tiles fill whole rounds at 2048
+        // and 4096 rows (measured at 2048 x 7168: 5.8 -> 4.9 us; 4096 x 7168:
+        // 8.5 -> 7.2 us; 2048 x 16384: 9.7 -> 8.1 us).  Short rows keep
+        // seven waves: at 2048 x 2048 eight-wave one-row tiles took 5.4 us
+        // against 4.4 us.
         const long ncu = cu_count();
-        auto busiest = [&](int r) {
-            const long rows_wg = (long)QG_FP8_WPB * (64 / pick_lpr(I / 16)) * r;
+        const long rpg = 64 / pick_lpr(I / 16);   // lane groups per wave
+        struct Tile { int wpb, r; };
+        const Tile cand[] = {{QG_FP8_WPB, QG_FP8_R}, {QG_FP8_WPB2, QG_FP8_R},
+                             {QG_FP8_WPB, 1}, {QG_FP8_WPB2, 1}};
+        int best = 0;
+        double best_fill = -1.0;
+        long best_wgs = 0;
+        for (int i = 0; i < 4; i++) {
+            if (cand[i].wpb == QG_FP8_WPB2 && I < QG_FP8_WPB2_MIN_I) continue;
+            const long rows_wg = cand[i].wpb * rpg * cand[i].r;
             const long wgs = (O + rows_wg - 1) / rows_wg;
-            return (wgs + ncu - 1) / ncu * rows_wg;
-        };
-        if (QG_FP8_R > 1 && busiest(1) < busiest(QG_FP8_R))
-            return launch_r<ST, S, 1>(w, sc, x, y, I, O, st);
-        return launch_r<ST, S, QG_FP8_R>(w, sc, x, y, I, O, st);
+            const double fill = (double)wgs / (double)(((wgs + ncu - 1) / ncu) * ncu);
+            if (fill > best_fill + 1e-9 || (fill > best_fill - 1e-9 && wgs < best_wgs)) {
+                best = i;
+                best_fill = fill;
+                best_wgs = wgs;
+            }
+        }
+        switch (best) {
+        case 0: return launch_r<ST, S, QG_FP8_R, QG_FP8_WPB>(w, sc, x, y, I, O, st);
+        case 1: return launch_r<ST, S, QG_FP8_R, QG_FP8_WPB2>(w, sc, x, y, I, O, st);
+        case 2: return launch_r<ST, S, 1, QG_FP8_WPB>(w, sc, x, y, I, O, st);
+        default: return launch_r<ST, S, 1, QG_FP8_WPB2>(w, sc, x, y, I, O, st);
+        }
     } else {
         // several vectors: R keeps every workgroup resident at once (the rows
         // of a lane group must share a 128-row band, so R divides 128)

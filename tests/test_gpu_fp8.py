@@ -42,6 +42,9 @@ def test_dequant_bit_exact(q, qref, O, I):
     (2048, 6144, 1), (2048, 6144, 4), (6144, 2048, 1), (384, 6144, 3),
     (130, 200, 2), (129, 128, 1), (128, 129, 1), (1, 1, 1), (300, 2048, 2),
     (77, 16, 1), (64, 4096, 8),
+    # one vector on eight-wave tiles: two rows per lane group (4096, ragged
+    # 4001 rows) and one (2048 x 6144 above, ragged 2047 rows)
+    (4096, 7168, 1), (4001, 4096, 1), (2047, 16384, 1),
     # several vectors whose activations do not all fit the LDS: column phases
     (300, 16384, 4), (7168, 16384, 2),
 ])
