@@ -385,33 +385,21 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
                     hipStream_t st)
 {
     if constexpr (S == 1) {
-        // Tile: WPB waves of R rows per lane group.  The workgroups are dealt
-        // to the CUs in rounds, so the tile that fills its last round best
-        // (workgroups / (CUs x rounds)) wins, and among equals the one with
-        // the fewest workgroups.  Seven-wave two-row tiles fill two rounds
-        // exactly at 7168 rows; eight-wave tiles fill whole rounds at 2048
-        // and 4096 rows (measured at 2048 x 7168: 5.8 -> 4.9 us; 4096 x 7168:
-        // 8.5 -> 7.2 us; 2048 x 16384: 9.7 -> 8.1 us).  Short rows keep
-        // seven waves: at 2048 x 2048 eight-wave one-row tiles took 5.4 us
-        // against 4.4 us.
-        const long ncu = cu_count();
+        // Tile: the one that fills whole rounds of the CUs best
+        // (pick_fill_tile).  Seven-wave two-row tiles fill two rounds exactly
+        // at 7168 rows; eight-wave tiles fill whole rounds at 2048 and 4096
+        // rows (measured at 2048 x 7168: 5.8 -> 4.9 us; 4096 x 7168: 8.5 ->
+        // 7.2 us; 2048 x 16384: 9.7 -> 8.1 us).  Short rows keep seven waves:
+        // at 2048 x 2048 eight-wave one-row tiles took 5.4 us against 4.4 us.
+        static const WaveTile cand[] = {{QG_FP8_WPB, QG_FP8_R}, {QG_FP8_WPB2, QG_FP8_R},
+                                        {QG_FP8_WPB, 1}, {QG_FP8_WPB2, 1}};
+        static const WaveTile cand7[] = {{QG_FP8_WPB, QG_FP8_R}, {QG_FP8_WPB, 1}};
         const long rpg = 64 / pick_lpr(I / 16);   // lane groups per wave
-        struct Tile { int wpb, r; };
-        const Tile cand[] = {{QG_FP8_WPB, QG_FP8_R}, {QG_FP8_WPB2, QG_FP8_R},
-                             {QG_FP8_WPB, 1}, {QG_FP8_WPB2, 1}};
-        int best = 0;
-        double best_fill = -1.0;
-        long best_wgs = 0;
-        for (int i = 0; i < 4; i++) {
-            if (cand[i].wpb == QG_FP8_WPB2 && I < QG_FP8_WPB2_MIN_I) continue;
-            const long rows_wg = cand[i].wpb * rpg * cand[i].r;
-            const long wgs = (O + rows_wg - 1) / rows_wg;
-            const double fill = (double)wgs / (double)(((wgs + ncu - 1) / ncu) * ncu);
-            if (fill > best_fill + 1e-9 || (fill > best_fill - 1e-9 && wgs < best_wgs)) {
-                best = i;
-                best_fill = fill;
-                best_wgs = wgs;
-            }
+        int best;
+        if (I >= QG_FP8_WPB2_MIN_I) {
+            best = pick_fill_tile(O, rpg, cand, 4, cu_count());
+        } else {
+            best = pick_fill_tile(O, rpg, cand7, 2, cu_count()) ? 2 : 0;
         }
         switch (best) {
         case 0: return launch_r<ST, S, QG_FP8_R, QG_FP8_WPB>(w, sc, x, y, I, O, st);

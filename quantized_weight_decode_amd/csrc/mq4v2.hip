@@ -22,22 +22,16 @@
 #include "qg_device.h"
 #include "qg_launch.h"
 
-// Tile shape for one vector: R rows per lane group, a ring of PF
-// chunk-sweeps per lane, WPB waves per workgroup, the first EARLY sweeps
-// issued before the activations are converted.  Measured on the 8192 x 8192
-// workload with the fused rotation (mean of six interleaved runs of 300
-// calls): 64 lanes x 2 rows x 16 waves with a ring of two and one early
-// sweep 9.2 us; the same with a ring of four 9.4 us, and without the early
-// sweep 10.3 us; two early sweeps 9.4 us; 32 lanes per row 10.1-10.2 us;
-// 4 rows x 8 waves 10.1 us.
-#ifndef QG_MQ4_R
-#define QG_MQ4_R 2
-#endif
+// Streaming for one vector: a ring of PF chunk-sweeps per lane, the first
+// EARLY sweeps issued before the activations are converted; the tile (waves
+// per workgroup, rows per lane group) is chosen per shape at launch.
+// Measured on the 8192 x 8192 workload with the fused rotation (mean of six
+// interleaved runs of 300 calls): 64 lanes x 2 rows x 16 waves with a ring
+// of two and one early sweep 9.2 us; the same with a ring of four 9.4 us,
+// and without the early sweep 10.3 us; two early sweeps 9.4 us; 32 lanes
+// per row 10.1-10.2 us; 4 rows x 8 waves 10.1 us.
 #ifndef QG_MQ4_PF
 #define QG_MQ4_PF 2
-#endif
-#ifndef QG_MQ4_WPB
-#define QG_MQ4_WPB 16
 #endif
 // at most this many lanes per row for one vector
 #ifndef QG_MQ4_LPR
@@ -538,11 +532,10 @@ hipError_t launch_t(const uint8_t *w, const float *x, const int8_t *sg, float *y
     return hipGetLastError();
 }
 
-template <int HF, int S, int R, bool ROT>
+template <int HF, int S, int R, bool ROT, int WPB = QG_MQ4_WPB_MULTI>
 hipError_t launch_r(const uint8_t *w, const float *x, const int8_t *sg, float *y, int I, int O,
                     hipStream_t st)
 {
-    constexpr int WPB = S == 1 ? QG_MQ4_WPB : QG_MQ4_WPB_MULTI;
     // several vectors: 16-wave workgroups leave 128 registers per lane, so
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_MQ4_PF : 2;
@@ -561,17 +554,26 @@ hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y
                     hipStream_t st)
 {
     if constexpr (S == 1) {
-        // one row per lane group where that puts fewer rows on the busiest CU
-        // (short matrices: the workgroups then spread over all CUs)
-        const long ncu = cu_count();
-        auto busiest = [&](int r) {
-            const long rows_wg = (long)QG_MQ4_WPB * (64 / pick_lpr(I / 32)) * r;
-            const long wgs = (O + rows_wg - 1) / rows_wg;
-            return (wgs + ncu - 1) / ncu * rows_wg;
-        };
-        if (QG_MQ4_R > 1 && busiest(1) < busiest(QG_MQ4_R))
-            return launch_r<HF, S, 1, ROT>(w, x, sg, y, I, O, st);
-        return launch_r<HF, S, QG_MQ4_R, ROT>(w, x, sg, y, I, O, st);
+        // Tile: 16, 14, 12 or 8 waves of two or one rows per lane group,
+        // whichever fills whole rounds of the CUs best (pick_fill_tile).  At
+        // 8192 x 8192 the 16-wave two-row tile fills one round exactly.
+        // Against 16 waves with R by the busiest CU, in us: 2048 x 7168 8.2
+        // -> 5.9 (8 waves), 5120 x 5120 7.1 -> 6.2 and 17408 x 5120 17.4 ->
+        // 13.8 (12), 7168 x 8192 8.8 -> 8.6 and 14336 x 4096 9.2 -> 8.9 (14).
+        static const WaveTile cand[] = {{16, 2}, {16, 1}, {14, 2}, {14, 1},
+                                        {12, 2}, {12, 1}, {8, 2},  {8, 1}};
+        int lpr = pick_lpr(I / 32);
+        if (lpr > QG_MQ4_LPR) lpr = QG_MQ4_LPR;
+        switch (pick_fill_tile(O, 64 / lpr, cand, 8, cu_count())) {
+        case 0: return launch_r<HF, S, 2, ROT, 16>(w, x, sg, y, I, O, st);
+        case 1: return launch_r<HF, S, 1, ROT, 16>(w, x, sg, y, I, O, st);
+        case 2: return launch_r<HF, S, 2, ROT, 14>(w, x, sg, y, I, O, st);
+        case 3: return launch_r<HF, S, 1, ROT, 14>(w, x, sg, y, I, O, st);
+        case 4: return launch_r<HF, S, 2, ROT, 12>(w, x, sg, y, I, O, st);
+        case 5: return launch_r<HF, S, 1, ROT, 12>(w, x, sg, y, I, O, st);
+        case 6: return launch_r<HF, S, 2, ROT, 8>(w, x, sg, y, I, O, st);
+        default: return launch_r<HF, S, 1, ROT, 8>(w, x, sg, y, I, O, st);
+        }
     } else {
         // several vectors: R keeps every workgroup resident at once.  With the
         // rotation every workgroup rotates all S vectors, so ties go to the

@@ -39,6 +39,37 @@ int cu_count();
 // candidate when none fits one round.
 int pick_rows_per_group(int O, int lpr, int wpb, size_t lds, const int *cand, int ncand);
 
+// One-vector tile: wpb waves per workgroup, r rows per lane group.
+struct WaveTile {
+    int wpb, r;
+};
+// Index of the tile, out of n candidates, for O rows with rpg lane groups per
+// wave on ncu CUs.  Workgroups are dealt to the CUs in rounds, so the tile
+// whose workgroup count fills its last round best (workgroups / (CUs x
+// rounds)) wins; among equals the one with the fewest workgroups, then the
+// one with more rows per lane group.
+inline int pick_fill_tile(long O, long rpg, const WaveTile *cand, int n, long ncu)
+{
+    int best = 0;
+    double best_fill = -1.0;
+    long best_wgs = 0;
+    for (int i = 0; i < n; i++) {
+        const long rows_wg = cand[i].wpb * rpg * cand[i].r;
+        const long wgs = (O + rows_wg - 1) / rows_wg;
+        const double fill = (double)wgs / (double)(((wgs + ncu - 1) / ncu) * ncu);
+        const bool better =
+            fill > best_fill + 1e-9 ||
+            (fill > best_fill - 1e-9 &&
+             (wgs < best_wgs || (wgs == best_wgs && cand[i].r > cand[best].r)));
+        if (better) {
+            best = i;
+            best_fill = fill;
+            best_wgs = wgs;
+        }
+    }
+    return best;
+}
+
 // grouped int4
 // Vectors one streaming launch takes for this shape (0: the streaming
 // kernel does not apply; larger S runs in groups of this many).
