@@ -402,20 +402,23 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
 {
     // R rows of a lane group share each activation read from LDS
     if constexpr (S == 1) {
-        // QG_I4G_R rows per lane group, or two where that puts no more rows on
-        // the busiest CU, or one where that puts fewer.  Measured at 6144
-        // columns: 12288 rows 8.97 (R = 3) against 9.76 us (R = 2); 16384
-        // rows 13.2 against 11.1 us; 32768 rows 20.6 against 19.9 us; 65536
-        // rows 39.2 against 36.3 us; 4096 rows 5.89 (R = 2) against 5.44 us
-        // (R = 1), 1024 rows 5.63 against 4.96 us
+        // QG_I4G_R rows per lane group, or two where that puts fewer rows on
+        // the busiest CU, or one where that puts fewer still and leaves at
+        // most one workgroup per CU.  Measured at 6144 columns: 12288 rows
+        // 8.97 (R = 3) against 9.76 us (R = 2); 16384 rows 13.2 against 11.1
+        // us; 32768 rows 20.6 against 19.9 us; 65536 rows 39.2 against 36.3
+        // us; 4096 rows 5.89 (R = 2) against 5.44 us (R = 1), 1024 rows 5.63
+        // against 4.96 us.  Where one-row tiles would put several workgroups
+        // on a CU, each staging x, they lose: 28672 x 8192 32.2 us (R = 1)
+        // against 25.9 us (R = 2); and on a tie R = 3 wins: 18432 x 7168
+        // 15.96 us against 17.52 us (R = 2).
         const long ncu = cu_count();
-        auto busiest = [&](int r) {
-            const long rows_wg = (long)QG_I4G_WPB * (64 / i4g_lanes_per_row(I)) * r;
-            const long wgs = (O + rows_wg - 1) / rows_wg;
-            return (wgs + ncu - 1) / ncu * rows_wg;
-        };
-        if (QG_I4G_R > 2 && busiest(2) <= busiest(QG_I4G_R)) {
-            if (busiest(1) < busiest(2)) return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
+        auto rows_wg = [&](int r) { return (long)QG_I4G_WPB * (64 / i4g_lanes_per_row(I)) * r; };
+        auto wgs = [&](int r) { return (O + rows_wg(r) - 1) / rows_wg(r); };
+        auto busiest = [&](int r) { return (wgs(r) + ncu - 1) / ncu * rows_wg(r); };
+        if (QG_I4G_R > 2 && busiest(2) < busiest(QG_I4G_R)) {
+            if (wgs(1) <= ncu && busiest(1) < busiest(2))
+                return launch_stream_r<S, 1>(w, s, x, y, I, O, gs, st);
             return launch_stream_r<S, 2>(w, s, x, y, I, O, gs, st);
         }
         return launch_stream_r<S, QG_I4G_R>(w, s, x, y, I, O, gs, st);
