@@ -391,15 +391,17 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
         // rows (measured at 2048 x 7168: 5.8 -> 4.9 us; 4096 x 7168: 8.5 ->
         // 7.2 us; 2048 x 16384: 9.7 -> 8.1 us).  Short rows keep seven waves:
         // at 2048 x 2048 eight-wave one-row tiles took 5.4 us against 4.4 us.
+        // One-row tiles only where they leave at most one workgroup per CU:
+        // 18432 x 7168 24.6 us (8 x 1, 2304 workgroups) against 23.4 us (8 x 2).
         static const WaveTile cand[] = {{QG_FP8_WPB, QG_FP8_R}, {QG_FP8_WPB2, QG_FP8_R},
                                         {QG_FP8_WPB, 1}, {QG_FP8_WPB2, 1}};
         static const WaveTile cand7[] = {{QG_FP8_WPB, QG_FP8_R}, {QG_FP8_WPB, 1}};
         const long rpg = 64 / pick_lpr(I / 16);   // lane groups per wave
         int best;
         if (I >= QG_FP8_WPB2_MIN_I) {
-            best = pick_fill_tile(O, rpg, cand, 4, cu_count());
+            best = pick_fill_tile(O, rpg, cand, 4, cu_count(), true);
         } else {
-            best = pick_fill_tile(O, rpg, cand7, 2, cu_count()) ? 2 : 0;
+            best = pick_fill_tile(O, rpg, cand7, 2, cu_count(), true) ? 2 : 0;
         }
         switch (best) {
         case 0: return launch_r<ST, S, QG_FP8_R, QG_FP8_WPB>(w, sc, x, y, I, O, st);

@@ -47,8 +47,11 @@ struct WaveTile {
 // wave on ncu CUs.  Workgroups are dealt to the CUs in rounds, so the tile
 // whose workgroup count fills its last round best (workgroups / (CUs x
 // rounds)) wins; among equals the one with the fewest workgroups, then the
-// one with more rows per lane group.
-inline int pick_fill_tile(long O, long rpg, const WaveTile *cand, int n, long ncu)
+// one with more rows per lane group.  With one_row_single, one-row tiles
+// count only where they leave at most one workgroup per CU (the first
+// candidate must have more rows).
+inline int pick_fill_tile(long O, long rpg, const WaveTile *cand, int n, long ncu,
+                          bool one_row_single = false)
 {
     int best = 0;
     double best_fill = -1.0;
@@ -56,6 +59,7 @@ inline int pick_fill_tile(long O, long rpg, const WaveTile *cand, int n, long nc
     for (int i = 0; i < n; i++) {
         const long rows_wg = cand[i].wpb * rpg * cand[i].r;
         const long wgs = (O + rows_wg - 1) / rows_wg;
+        if (one_row_single && cand[i].r == 1 && wgs > ncu) continue;
         const double fill = (double)wgs / (double)(((wgs + ncu - 1) / ncu) * ncu);
         const bool better =
             fill > best_fill + 1e-9 ||
