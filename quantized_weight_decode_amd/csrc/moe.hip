@@ -624,7 +624,23 @@ hipError_t launch_moe_topk(const void *w, const float *scales, long long w_strid
                            int *err_flag, hipStream_t st)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);
-    const int lpr = pick_lpr(I / 32 > 0 ? I / 32 : 1);
+    // Lanes per row: the widest with the fewest idle lanes, narrowed (not
+    // below 8) until a unit -- one expert's rows of a wave -- spans at least
+    // two sweeps, and from two to four where the workgroups then still cover
+    // 7/8 of the CUs.  Each unit pays its own bookkeeping (the next unit from the LDS
+    // counter, its expert and tokens, the row sums), so one-sweep units lose:
+    // at 7168 x 2048 experts (4 tokens x top-8 of 256) 76.3 us with 64 lanes,
+    // 57.2 us with 32, 54.4 us with 16.  At 768 x 2048, 16 lanes would leave
+    // 96 workgroups: 19.1 us against 15.4 us with 32 (18.1 us with 64).  At
+    // 4096 x 1536 three-sweep units stay: 25.5 us against 26.1 us with six.
+    const int NU = I / 32 > 0 ? I / 32 : 1;
+    int lpr = pick_lpr(NU);
+    while (lpr > 8 && NU / lpr < 2) lpr /= 2;
+    if (lpr > 8 && NU / lpr <= 2) {
+        int RT2, NB2;
+        moe_blocks(O, (WAVE / (lpr / 2)) * QG_MOE_R, RT2, NB2);
+        if (8L * NB2 >= 7L * cu_count()) lpr /= 2;
+    }
     const int rpw = (WAVE / lpr) * QG_MOE_R;
     int RT, NB;
     moe_blocks(O, rpw, RT, NB);

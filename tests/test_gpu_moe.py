@@ -61,6 +61,8 @@ def moe_magnitude(qref, d):
 @pytest.mark.parametrize("E,O,I,gs,T,K", [
     (16, 256, 512, 64, 4, 8), (32, 300, 1024, 64, 2, 4), (8, 77, 7168, 64, 4, 2),
     (12, 40, 256, 128, 1, 1), (64, 512, 2048, 32, 8, 8), (6, 100, 2048, 64, 3, 6),
+    # short rows: 16 and 32 lanes per row instead of 64 (two- and four-sweep units)
+    (8, 7168, 2048, 64, 4, 8), (12, 768, 2048, 64, 4, 8),
 ])
 def test_matches_oracle(q, qref, E, O, I, gs, T, K):
     d = W.gen_moe(E, O, I, gs, T, K, seed=E + O)
