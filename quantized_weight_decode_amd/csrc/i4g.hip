@@ -413,6 +413,19 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
         // against 25.9 us (R = 2); and on a tie R = 3 wins: 18432 x 7168
         // 15.96 us against 17.52 us (R = 2).
         const long ncu = cu_count();
+        // Few rows -- at most one workgroup per CU with 32-lane one-row
+        // tiles -- on rows of at least 64 lane chunks: 64 lanes per row (twice
+        // the waves) and a ring of four sweeps (twice the bytes in flight per
+        // wave), one row per lane group where that leaves at most one
+        // workgroup per CU, else two.  2048 x 14336 8.9 -> 6.6 us, 1024 x
+        // 28672 15.2 -> 9.8 us, 1536 x 16384 9.8 -> 6.8 us, 4096 x 6144 5.39
+        // -> 5.24 us, 4096 x 14336 9.43 -> 9.21 us.  With more rows the
+        // 32-lane tiles stay ahead (12288 x 6144: 10.9 us this way).
+        if (pick_lpr(I / 32) == 64 && (O + 2L * QG_I4G_WPB - 1) / (2L * QG_I4G_WPB) <= ncu) {
+            if ((O + QG_I4G_WPB - 1) / QG_I4G_WPB <= ncu)
+                return launch_stream_t<S, 64, 1, 4>(w, s, x, y, I, O, gs, st);
+            return launch_stream_t<S, 64, 2, 4>(w, s, x, y, I, O, gs, st);
+        }
         auto rows_wg = [&](int r) { return (long)QG_I4G_WPB * (64 / i4g_lanes_per_row(I)) * r; };
         auto wgs = [&](int r) { return (O + rows_wg(r) - 1) / rows_wg(r); };
         auto busiest = [&](int r) { return (wgs(r) + ncu - 1) / ncu * rows_wg(r); };

@@ -47,6 +47,8 @@ def test_dequant_bit_exact(q, qref, O, I, gs):
     # tiles the launcher picks by rows on the busiest CU: two rows per lane
     # group (16384 x 512), one row (20000 x 1024, ragged)
     (16384, 512, 64, 1), (20000, 1024, 64, 1),
+    # few rows of long rows: 64 lanes per row, a ring of four sweeps
+    (2048, 14336, 64, 1), (1000, 8192, 128, 1), (4096, 6144, 64, 1),
     # several vectors: 16-wave workgroups; S > 4 runs as groups of streaming launches
     (12288, 6144, 64, 2), (4000, 6144, 64, 4), (300, 1024, 64, 6), (65, 6144, 64, 7),
     # four vectors, scale groups of one, two and three 64-column blocks, ragged
