@@ -45,6 +45,8 @@ def test_dequant_bit_exact(q, qref, O, I):
     # one vector on eight-wave tiles: two rows per lane group (4096, ragged
     # 4001 rows) and one (2048 x 6144 above, ragged 2047 rows)
     (4096, 7168, 1), (4001, 4096, 1), (2047, 16384, 1),
+    # short rows: lanes per row narrowed to 16 and 8 (three or more sweeps)
+    (3000, 1024, 1), (1000, 512, 1), (5000, 2048, 1),
     # several vectors whose activations do not all fit the LDS: column phases
     (300, 16384, 4), (7168, 16384, 2),
 ])

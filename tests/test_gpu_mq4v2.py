@@ -50,6 +50,8 @@ def test_dequant_bit_exact(q, qref, O, I):
     (5, 768, 8), (1, 256, 1),
     # one vector on 14-, 12- and 8-wave tiles (ragged row counts included)
     (7000, 8192, 1), (5000, 5120, 1), (4096, 8192, 1), (2000, 7168, 1),
+    # short rows: lanes per row narrowed so that a row takes two sweeps
+    (3000, 1024, 1), (5000, 2048, 1), (700, 512, 1),
 ])
 def test_gemv_matches_oracle(q, qref, O, I, S):
     d = W.gen_mq4v2(O, I, S=S, seed=O + 7)
@@ -245,7 +247,7 @@ def _two_launch(q, w, x, signs):
 
 @pytest.mark.parametrize("O,I,S", [(8192, 8192, 1), (256, 512, 1), (300, 1024, 2),
                                    (77, 256, 3), (1000, 4096, 4), (33, 2304, 1), (5, 768, 6),
-                                   (7000, 8192, 1), (5000, 5120, 1)])
+                                   (7000, 8192, 1), (5000, 5120, 1), (3000, 1024, 1)])
 def test_fused_rotation_matches_two_launches_bitwise(q, qref, O, I, S):
     # one launch == qgemv_fwht256 then qgemv_mq4v2, to the bit; and the oracle
     d = W.gen_mq4v2(O, I, S=S, seed=O + 11)
