@@ -289,10 +289,12 @@ __device__ __forceinline__ float lane_xor(float v)
 {
     const int iv = __builtin_bit_cast(int, v);
     int r;
-    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);
-    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);
+    // every source lane of these patterns exists, so bound_ctrl changes no
+    // value; it lets the move go without first clearing its destination
+    if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);
+    else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);
     // M == 8: row_ror:8
-    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);
+    else if constexpr (M == 8) r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);
     else r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (M << 10));   // xor M within 32 lanes
     return __builtin_bit_cast(float, r);
 }
@@ -360,14 +362,29 @@ struct XStageQ {
 #pragma unroll
         for (int j = 0; j < NPRE; j++) {
             const int f = (int)threadIdx.x + j * NT;
+            if constexpr (ROT) {
+                // unconditional (clamped past the end) and, as a relaxed atomic,
+                // kept in place: a sign load behind the branch below ends in a
+                // register copy that waits for it before the weight loads
+                // behind it are issued
+                const uint32_t g = (uint32_t)stage_index(f, items, rot);
+                const uint64_t sv = __hip_atomic_load(
+                    reinterpret_cast<const uint64_t *>(signs + 8u * sign_item(g, ipv)),
+                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                sg[j] = u32x2{(uint32_t)sv, (uint32_t)(sv >> 32)};
+            }
             if (f < items) {
                 const uint32_t g = (uint32_t)stage_index(f, items, rot);
                 a[j] = ldx4(x, 2u * g);
                 b[j] = ldx4(x, 2u * g + 1u);
-                if constexpr (ROT)
-                    sg[j] = *reinterpret_cast<const u32x2 *>(signs + 8u * (g % (uint32_t)ipv));
             }
         }
+    }
+
+    // item g's position within its vector (one vector: g itself)
+    __device__ __forceinline__ static uint32_t sign_item(uint32_t g, int ipv)
+    {
+        return S == 1 ? g : g % (uint32_t)ipv;
     }
 
     __device__ __forceinline__ void load_all(const float *__restrict__ x, int items)
@@ -428,8 +445,7 @@ struct XStageQ {
             const int g = stage_index(f, items, rot);
             u32x2 sv = {0, 0};
             if constexpr (ROT)
-                sv = *reinterpret_cast<const u32x2 *>(signs +
-                                                      8u * ((uint32_t)g % (uint32_t)(NU * 4)));
+                sv = *reinterpret_cast<const u32x2 *>(signs + 8u * sign_item((uint32_t)g, NU * 4));
             bad |= put(ldx4(x, 2u * (uint32_t)g), ldx4(x, 2u * (uint32_t)g + 1u), sv, g, NU, xq,
                        xc, xsum);
         }
