@@ -247,7 +247,9 @@ def _two_launch(q, w, x, signs):
 
 @pytest.mark.parametrize("O,I,S", [(8192, 8192, 1), (256, 512, 1), (300, 1024, 2),
                                    (77, 256, 3), (1000, 4096, 4), (33, 2304, 1), (5, 768, 6),
-                                   (7000, 8192, 1), (5000, 5120, 1), (3000, 1024, 1)])
+                                   (7000, 8192, 1), (5000, 5120, 1), (3000, 1024, 1),
+                                   # two staged items per thread
+                                   (1500, 16384, 1), (2000, 7168, 1), (600, 12288, 2)])
 def test_fused_rotation_matches_two_launches_bitwise(q, qref, O, I, S):
     # one launch == qgemv_fwht256 then qgemv_mq4v2, to the bit; and the oracle
     d = W.gen_mq4v2(O, I, S=S, seed=O + 11)
