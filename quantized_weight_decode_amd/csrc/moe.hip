@@ -283,7 +283,13 @@ __global__ __launch_bounds__(64 * QG_MOE_WPB) void moe_i4g_stream(
             const int row = live ? min(fu.row0 + r, O - 1) : 0;
             wb[j][r] = ld_stream(reinterpret_cast<const u32x4 *>(we + (size_t)row * rb +
                                                                  (uint32_t)u * 16u));
-            sb[j][r] = ld_stream(se + (size_t)row * ng + g);
+            // the scales as ordinary cached loads: one 128-byte line of them
+            // serves several sweeps, and with the streaming hint it was often
+            // gone before the next one.  4 tokens x top-8 of 256 experts of
+            // 2048 x 7168: 1.037 -> 1.004 of the algorithmic bytes fetched,
+            // time within +-2 % (mean of four interleaved runs +0.6 %); one
+            // token x top-32: 2-4 % faster
+            sb[j][r] = se[(size_t)row * ng + g];
         }
         if (fi < nunits) {
             if (fc + 1 < nit) {
