@@ -537,11 +537,15 @@ def warm(torch, fn, seconds, start=0):
 # ---------------------------------------------------------------------------
 class Ceiling:
     """Best plain streaming read of `nbytes` (pattern 0: contiguous 16-byte
-    chunks; 1: the MQ4 136-byte group pattern) over a sweep of tile shapes,
-    rotating through copies totalling over 1 GiB."""
-    # (waves per workgroup, loads in flight per lane, workgroups per CU; 0: one-shot)
-    VARIANTS = [(wpb, u, wpc) for wpb in (4, 8, 16) for u in (2, 4, 8) for wpc in (1, 2)
-                if wpb * wpc <= 16] + [(wpb, u, 0) for wpb in (4, 8, 16) for u in (1, 2, 4)]
+    chunks; 1: the MQ4 136-byte group pattern) over a sweep of tile shapes and
+    of the load policy (non-temporal hint or cached), rotating through copies
+    totalling over 1 GiB."""
+    # (waves per workgroup, loads in flight per lane, workgroups per CU; 0: one-shot,
+    #  cached loads)
+    VARIANTS = [(wpb, u, wpc, ca) for ca in (False, True)
+                for wpb, u, wpc in
+                [(wpb, u, wpc) for wpb in (4, 8, 16) for u in (2, 4, 8) for wpc in (1, 2)
+                 if wpb * wpc <= 16] + [(wpb, u, 0) for wpb in (4, 8, 16) for u in (1, 2, 4)]]
     OUT_LEN = 1 << 20
 
     def __init__(self, torch, lib, nbytes, pattern, cus):
@@ -560,8 +564,9 @@ class Ceiling:
         self.name = f"read_{self.nbytes}" + ("_mq4" if pattern else "")
 
     def step(self, i):
-        wpb, u, wpc = self.v
-        st = self.lib.qgemv_ceiling_read(self.ptrs[i % self.n], self.nbytes, self.pattern, wpb,
+        wpb, u, wpc, ca = self.v
+        st = self.lib.qgemv_ceiling_read(self.ptrs[i % self.n], self.nbytes,
+                                         self.pattern | (2 if ca else 0), wpb,
                                          u, self.cus * wpc, self.out.data_ptr(), self.OUT_LEN,
                                          self.sp)
         if st:
@@ -815,7 +820,8 @@ def main():
                                                4),
                                  "tile": {"waves_per_wg": v[0], "loads_in_flight": v[1],
                                           "mapping": "slab" if v[2] else "one-shot",
-                                          "wgs_per_cu": v[2] or None}}
+                                          "wgs_per_cu": v[2] or None,
+                                          "loads": "cached" if v[3] else "non-temporal"}}
                 del cl
                 torch.cuda.empty_cache()
 

@@ -11,6 +11,8 @@
 //     bytes); chunk c is the 16 payload bytes at 136 (c / 8) + 8 + 16 (c % 8),
 //     an 8-byte-aligned 16-byte load, plus the header dword at
 //     136 (c / 8) + 4 (c % 8 >= 4) -- the reads an MQ4-v2 GEMV makes.
+// Each pattern reads with the non-temporal hint or as ordinary cached loads
+// (pattern | 2): the faster of the two is the reference.
 // Slab mapping: workgroup b reads the b-th contiguous slab of chunks; wave w of it reads
 // the 64-chunk pieces w, w + WPB, ... of the slab, U pieces in flight per
 // lane (a ring: the oldest is consumed, then refilled U pieces ahead).  The
@@ -26,20 +28,26 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 
-enum : int { CONTIG = 0, MQ4 = 1 };
+enum : int { CONTIG = 0, MQ4 = 1, CACHED = 2 };
+
+template <bool NT, typename T>
+__device__ __forceinline__ T rd(const T *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
 
 template <int PAT>
 __device__ __forceinline__ u32x4 load_chunk(const uint8_t *__restrict__ p, size_t c)
 {
-    if constexpr (PAT == CONTIG) {
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + c);
+    constexpr bool NT = !(PAT & CACHED);
+    if constexpr ((PAT & MQ4) == 0) {
+        return rd<NT>(reinterpret_cast<const u32x4 *>(p) + c);
     } else {
         const uint8_t *g = p + (c >> 3) * 136;
         const uint32_t q = (uint32_t)c & 7u;
-        const u32x4_a8 v =
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4_a8 *>(g + 8 + 16 * q));
-        const uint32_t h =
-            __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(g + (q >= 4 ? 4 : 0)));
+        const u32x4_a8 v = rd<NT>(reinterpret_cast<const u32x4_a8 *>(g + 8 + 16 * q));
+        const uint32_t h = rd<NT>(reinterpret_cast<const uint32_t *>(g + (q >= 4 ? 4 : 0)));
         return u32x4{v.x ^ h, v.y, v.z, v.w};
     }
 }
@@ -162,7 +170,9 @@ extern "C" {
 
 // Reads `bytes` bytes of device memory at `buf` once.
 //   pattern 0: contiguous 16-byte chunks (bytes % 16 == 0, buf 16-byte aligned);
-//   pattern 1: MQ4 136-byte groups (bytes % 136 == 0, buf 8-byte aligned).
+//   pattern 1: MQ4 136-byte groups (bytes % 136 == 0, buf 8-byte aligned);
+//   pattern | 2: the same reads as ordinary cached loads instead of with the
+//   non-temporal hint.
 //   wpb in {4, 8, 16} waves per workgroup, u in {1, 2, 4, 8} loads in flight
 //   per lane; wgs >= 1 workgroups of the slab mapping (u >= 2), or 0 for the
 //   one-shot mapping.  out: device u32, one per wave of the grid, at most
@@ -175,20 +185,22 @@ int qgemv_ceiling_read(const void *buf, size_t bytes, int pattern, int wpb, int 
     if (wpb != 4 && wpb != 8 && wpb != 16) return 1;
     if (u != 1 && u != 2 && u != 4 && u != 8) return 1;
     if (wgs > 0 && u == 1) return 1;
-    const size_t nch = pattern == MQ4 ? bytes / 136 * 8 : bytes / 16;
+    if (pattern < 0 || pattern > 3) return 1;
+    const bool mq4 = (pattern & MQ4) != 0;
+    const size_t nch = mq4 ? bytes / 136 * 8 : bytes / 16;
     const size_t waves = wgs > 0 ? (size_t)wgs * wpb
                                  : ((nch + 64 * (size_t)u - 1) / (64 * u) + wpb - 1) / wpb * wpb;
     if (waves > out_len) return 1;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (pattern == CONTIG) {
+    if (!mq4) {
         if (bytes == 0 || bytes % 16 || ((uintptr_t)buf & 15)) return 1;
-        e = launch_wpb<CONTIG>(wpb, u, buf, bytes / 16, wgs, out, st);
-    } else if (pattern == MQ4) {
-        if (bytes == 0 || bytes % 136 || ((uintptr_t)buf & 7)) return 1;
-        e = launch_wpb<MQ4>(wpb, u, buf, bytes / 136 * 8, wgs, out, st);
+        e = pattern & CACHED ? launch_wpb<CONTIG | CACHED>(wpb, u, buf, nch, wgs, out, st)
+                             : launch_wpb<CONTIG>(wpb, u, buf, nch, wgs, out, st);
     } else {
-        return 1;
+        if (bytes == 0 || bytes % 136 || ((uintptr_t)buf & 7)) return 1;
+        e = pattern & CACHED ? launch_wpb<MQ4 | CACHED>(wpb, u, buf, nch, wgs, out, st)
+                             : launch_wpb<MQ4>(wpb, u, buf, nch, wgs, out, st);
     }
     return e == hipSuccess ? 0 : 2;
 }

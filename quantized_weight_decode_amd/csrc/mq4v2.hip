@@ -58,9 +58,16 @@ constexpr int MQ4_GROUP_BYTES = 136;
 // 16 bytes at an 8-byte-aligned address.
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 
+// Unlike the other formats, MQ4 weights are read as ordinary cached loads,
+// not with the streaming hint: each group's header dword is a second load
+// from the lines its payload loads just fetched, and with the payload cached
+// that second touch is served close to the CU.  8192 x 8192, interleaved,
+// three boxes: 8.89-8.94 -> 8.54-8.57 us pre-rotated, 9.69-9.71 -> 9.55 us
+// with the fused rotation; the same bytes fetched.  (Cached headers alone
+// gained nothing; cached weights made i4g and fp8 5-8 % slower.)
 __device__ __forceinline__ u32x4 load16_a8(const uint8_t *p)
 {
-    const u32x4_a8 v = ld_stream(reinterpret_cast<const u32x4_a8 *>(p));
+    const u32x4_a8 v = *reinterpret_cast<const u32x4_a8 *>(p);
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
@@ -100,7 +107,7 @@ struct Mq4Hdr {
     // header of payload chunk p (16 bytes at +8 + 16p) of group gp
     __device__ __forceinline__ static T load(const uint8_t *gp, int p)
     {
-        return ld_stream(reinterpret_cast<const uint32_t *>(gp + (HF == MQ4_V2 && p >= 4 ? 4 : 0)));
+        return *reinterpret_cast<const uint32_t *>(gp + (HF == MQ4_V2 && p >= 4 ? 4 : 0));
     }
     __device__ __forceinline__ static void decode(T h, float &sc, float &zp)
     {
@@ -113,7 +120,7 @@ struct Mq4Hdr<MQ4_V1> {
     typedef u32x2 T;
     __device__ __forceinline__ static T load(const uint8_t *gp, int)
     {
-        return ld_stream(reinterpret_cast<const u32x2 *>(gp));
+        return *reinterpret_cast<const u32x2 *>(gp);
     }
     __device__ __forceinline__ static void decode(T h, float &sc, float &zp)
     {
