@@ -598,13 +598,14 @@ hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y
         default: return launch_r<HF, S, 1, ROT, 8>(w, x, sg, y, I, O, st);
         }
     } else {
-        // several vectors: R keeps every workgroup resident at once.  With the
-        // rotation every workgroup rotates all S vectors, so ties go to the
-        // larger R (fewer workgroups)
-        static const int cand[] = {1, 2, 3};
-        static const int cand_rot[] = {3, 2, 1};
+        // several vectors: R keeps every workgroup resident at once.  Every
+        // workgroup converts all S vectors, so ties go to the larger R (fewer
+        // workgroups).  Pre-rotated 8192 x 8192, two vectors: 15.0 -> 11.1-11.2
+        // us against ties to the smaller R (two workgroups per CU, each
+        // converting the vectors); eleven other shapes and counts within 1 %
+        static const int cand[] = {3, 2, 1};
         switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_MQ4_WPB_MULTI,
-                                    mq4_lds_bytes(S, I, ROT), ROT ? cand_rot : cand, 3)) {
+                                    mq4_lds_bytes(S, I, ROT), cand, 3)) {
         case 1: return launch_r<HF, S, 1, ROT>(w, x, sg, y, I, O, st);
         case 2: return launch_r<HF, S, 2, ROT>(w, x, sg, y, I, O, st);
         default: return launch_r<HF, S, 3, ROT>(w, x, sg, y, I, O, st);
