@@ -42,10 +42,15 @@
 #define QG_FP8_WPB_MULTI 16
 #endif
 // sweeps issued before the activations are staged (at most PF).  Unlike the
-// nibble formats, the fp8 stream is faster with its first round of weight
-// loads in flight while the (larger) activation vector is staged.
+// nibble formats, the fp8 stream is faster with most of its first round of
+// weight loads in flight while the (larger) activation vector is staged.
+// Three of a ring of four, against all four (interleaved, three runs, one
+// vector): 7168 x 16384 unchanged, 4096 x 7168 -2.3 %, 2048 x 16384 -1.3 %,
+// 18432 x 7168 -1.3 %, 12288 x 7168 -1.2 %, 3072 x 7168 -3.1 %, 2048 x 7168
+// +1.8 %, 4096 x 16384 +1.1 %; several vectors within 0.5 %.  One or two
+// were slower.
 #ifndef QG_FP8_PF0
-#define QG_FP8_PF0 4
+#define QG_FP8_PF0 3
 #endif
 
 // activation float4s each thread loads up front (the rest follow one round
