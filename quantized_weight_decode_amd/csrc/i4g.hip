@@ -347,9 +347,24 @@ namespace {
 
 // lanes per row: the fullest sweep, at most QG_I4G_LPR (one vector) or
 // QG_I4G_LPR_MULTI (several)
+// Lanes per row: of 64 and 32 the one that leaves fewer lanes idle (ties to
+// 64); narrower only for rows of fewer than 32 chunks.  The fewest idle lanes
+// over all widths took 4 to 16 lanes for rows of e.g. 2176, 4352, 11008 or
+// 18944 columns, and such short segments per row stream far slower.
+// Interleaved: 4096 x 11008 18.8 -> 8.8 us, 3584 x 18944 17.9 -> 11.4 us,
+// 5120 x 13824 14.1 -> 11.1 us, 1024 x 4352 8.8 -> 4.0 us; 18944 x 3584 3 %
+// slower (where 16 lanes fit exactly); 12288 x 6144 and other shapes of whole
+// 64-chunk rows unchanged.
+inline int i4g_wide_lpr(int n)
+{
+    if (n < 32) return pick_lpr(n);
+    const int s64 = (n + 63) / 64, s32 = (n + 31) / 32;
+    return (long)n * s64 * 64 > (long)n * s32 * 32 ? 32 : 64;   // fewer idle lanes; ties to 64
+}
+
 inline int i4g_lanes_per_row(int I, int S = 1)
 {
-    const int lpr = pick_lpr(I / 32);
+    const int lpr = i4g_wide_lpr(I / 32);
     const int cap = S == 1 ? QG_I4G_LPR : QG_I4G_LPR_MULTI;
     return lpr > cap ? cap : lpr;
 }
@@ -419,9 +434,12 @@ hipError_t launch_stream_s(const uint8_t *w, const float *s, const float *x, flo
         // wave), one row per lane group where that leaves at most one
         // workgroup per CU, else two.  2048 x 14336 8.9 -> 6.6 us, 1024 x
         // 28672 15.2 -> 9.8 us, 1536 x 16384 9.8 -> 6.8 us, 4096 x 6144 5.39
-        // -> 5.24 us, 4096 x 14336 9.43 -> 9.21 us.  With more rows the
-        // 32-lane tiles stay ahead (12288 x 6144: 10.9 us this way).
-        if (pick_lpr(I / 32) == 64 && (O + 2L * QG_I4G_WPB - 1) / (2L * QG_I4G_WPB) <= ncu) {
+        // -> 5.24 us, 4096 x 14336 9.43 -> 9.21 us; and for any row of at
+        // least 64 chunks, whatever width the rule above gives it: 2048 x 7168
+        // 5.7 -> 4.7 us, 1536 x 7168 5.7 -> 4.6 us, 2048 x 2176 11.5 -> 4.0 us.
+        // With more rows the 32-lane tiles stay ahead (12288 x 6144: 10.9 us
+        // this way).
+        if (I / 32 >= 64 && (O + 2L * QG_I4G_WPB - 1) / (2L * QG_I4G_WPB) <= ncu) {
             if ((O + QG_I4G_WPB - 1) / QG_I4G_WPB <= ncu)
                 return launch_stream_t<S, 64, 1, 4>(w, s, x, y, I, O, gs, st);
             return launch_stream_t<S, 64, 2, 4>(w, s, x, y, I, O, gs, st);

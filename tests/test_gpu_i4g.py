@@ -205,3 +205,19 @@ def test_output_rows_outside_o_untouched(q):
     assert st == 0
     flat = host(y).reshape(-1)
     assert np.all(flat[2 * 37:] == 7.0)
+
+
+@pytest.mark.parametrize("O,I,S", [(2048, 2176, 1), (700, 4352, 1), (4096, 11008, 1),
+                                   (300, 18944, 1), (5000, 3584, 1), (1000, 2560, 2),
+                                   (513, 11008, 4)])
+def test_odd_row_widths(q, qref, O, I, S):
+    # rows whose chunk count no wide lane width divides (64 or 32 lanes per
+    # row with idle lanes in the last sweep)
+    d = W.gen_i4g(O, I, 64, S=S, seed=O + I)
+    y = host(q.i4g(dev(d["w"]), dev(d["scales"]), dev(d["x"]), 64))
+    rows = np.arange(0, O, 7) if O * I > (1 << 22) else np.arange(O)
+    wr = np.ascontiguousarray(d["w"].reshape(O, -1)[rows])
+    sr = np.ascontiguousarray(d["scales"].reshape(O, -1)[rows])
+    ref = qref.i4g_gemv(wr, sr, d["x"], len(rows), I, 64)
+    mag = magnitude(qref.i4g_dequant(wr, sr, len(rows), I, 64), d["x"])
+    assert_y_close(y[:, rows], ref, mag=mag)
