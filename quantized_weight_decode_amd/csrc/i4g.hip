@@ -347,24 +347,12 @@ namespace {
 
 // lanes per row: the fullest sweep, at most QG_I4G_LPR (one vector) or
 // QG_I4G_LPR_MULTI (several)
-// Lanes per row: of 64 and 32 the one that leaves fewer lanes idle (ties to
-// 64); narrower only for rows of fewer than 32 chunks.  The fewest idle lanes
-// over all widths took 4 to 16 lanes for rows of e.g. 2176, 4352, 11008 or
-// 18944 columns, and such short segments per row stream far slower.
-// Interleaved: 4096 x 11008 18.8 -> 8.8 us, 3584 x 18944 17.9 -> 11.4 us,
-// 5120 x 13824 14.1 -> 11.1 us, 1024 x 4352 8.8 -> 4.0 us; 18944 x 3584 3 %
-// slower (where 16 lanes fit exactly); 12288 x 6144 and other shapes of whole
-// 64-chunk rows unchanged.
-inline int i4g_wide_lpr(int n)
-{
-    if (n < 32) return pick_lpr(n);
-    const int s64 = (n + 63) / 64, s32 = (n + 31) / 32;
-    return (long)n * s64 * 64 > (long)n * s32 * 32 ? 32 : 64;   // fewer idle lanes; ties to 64
-}
-
+// Lanes per row (pick_lpr_wide).  i4g: 3584 x 18944 17.9 -> 11.4 us, 5120 x
+// 13824 14.1 -> 11.1 us, 1024 x 4352 8.8 -> 4.0 us; 18944 x 3584 3 % slower;
+// 12288 x 6144 and other rows of whole 64-chunk sweeps unchanged.
 inline int i4g_lanes_per_row(int I, int S = 1)
 {
-    const int lpr = i4g_wide_lpr(I / 32);
+    const int lpr = pick_lpr_wide(I / 32);
     const int cap = S == 1 ? QG_I4G_LPR : QG_I4G_LPR_MULTI;
     return lpr > cap ? cap : lpr;
 }

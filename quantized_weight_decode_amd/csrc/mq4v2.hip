@@ -523,13 +523,16 @@ __global__ __launch_bounds__(256) void fwht256_kernel(const float *__restrict__ 
 
 namespace {
 
-// Lanes per row for one vector: the widest with the fewest idle lanes (at
-// most QG_MQ4_LPR), narrowed (not below 8) until a row takes at least two
-// sweeps.  28672 x 1024 8.3 -> 5.8 us, 14336 x 2048 8.4 -> 5.4 us, 7168 x
-// 2048 5.2 -> 4.3 us; four sweeps instead of two measured 3-10 % slower.
+// Lanes per row for one vector: pick_lpr_wide (at most QG_MQ4_LPR), narrowed
+// (not below 8) until a row takes at least two sweeps.  pick_lpr_wide against
+// the fewest idle lanes: 4096 x 11008 8.7 against 19.3 us (fused 10.2 against
+// 20.7), 3584 x 18944 13.1 against 18.8, 2048 x 2560 4.1 against 4.6; 18944 x
+// 3584 4 % slower (fused 18-21 %).  The narrowing: 28672 x 1024 8.3 -> 5.8
+// us, 14336 x 2048 8.4 -> 5.4 us, 7168 x 2048 5.2 -> 4.3 us; four sweeps
+// instead of two measured 3-10 % slower.
 int mq4_lpr1(int I)
 {
-    int lpr = pick_lpr(I / 32);
+    int lpr = pick_lpr_wide(I / 32);
     if (lpr > QG_MQ4_LPR) lpr = QG_MQ4_LPR;
     while (lpr > 8 && (I / 32) / lpr < 2) lpr /= 2;
     return lpr;
@@ -565,7 +568,7 @@ hipError_t launch_r(const uint8_t *w, const float *x, const int8_t *sg, float *y
     // several vectors: 16-wave workgroups leave 128 registers per lane, so
     // two sweeps in flight
     constexpr int PF = S == 1 ? QG_MQ4_PF : 2;
-    const int lpr = S == 1 ? mq4_lpr1(I) : pick_lpr(I / 32);
+    const int lpr = S == 1 ? mq4_lpr1(I) : pick_lpr_wide(I / 32);
     switch (lpr) {
     case 64: return launch_t<HF, S, 64, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
     case 32: return launch_t<HF, S, 32, R, PF, WPB, ROT>(w, x, sg, y, I, O, st);
@@ -604,7 +607,7 @@ hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y
         // us against ties to the smaller R (two workgroups per CU, each
         // converting the vectors); eleven other shapes and counts within 1 %
         static const int cand[] = {3, 2, 1};
-        switch (pick_rows_per_group(O, pick_lpr(I / 32), QG_MQ4_WPB_MULTI,
+        switch (pick_rows_per_group(O, pick_lpr_wide(I / 32), QG_MQ4_WPB_MULTI,
                                     mq4_lds_bytes(S, I, ROT), cand, 3)) {
         case 1: return launch_r<HF, S, 1, ROT>(w, x, sg, y, I, O, st);
         case 2: return launch_r<HF, S, 2, ROT>(w, x, sg, y, I, O, st);

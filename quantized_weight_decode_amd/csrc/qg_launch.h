@@ -27,6 +27,21 @@ inline int pick_lpr(int nchunks)
     return best;
 }
 
+// Lanes per row for the 4-bit streams: for rows of at least 32 chunks, 64 or
+// 32, whichever leaves fewer lanes idle (ties to 64); shorter rows as
+// pick_lpr.  pick_lpr alone gives rows such as 1408, 2176, 4352, 11008 or
+// 18944 columns 4 to 16 lanes, and such short segments per row stream far
+// slower (e.g. 4096 x 11008: i4g 18.8 -> 8.8 us, MQ4 19.3 -> 8.7 us; routed
+// experts of 2048 x 1408: 41.5 -> 17.6 us).  The cost: many rows of 112
+// chunks (3584 columns), which 16 lanes fit exactly, run 3-5 % slower (MQ4
+// with the fused rotation about 20 % at 18944 rows).
+inline int pick_lpr_wide(int nchunks)
+{
+    if (nchunks < 32) return pick_lpr(nchunks);
+    const long s64 = (nchunks + 63) / 64, s32 = (nchunks + 31) / 32;
+    return s64 * 64 > s32 * 32 ? 32 : 64;
+}
+
 // Raises a kernel's dynamic-LDS limit to `bytes` once (cached per kernel).
 hipError_t set_max_lds(const void *kernel, size_t bytes);
 // Compute units of the current device.

@@ -63,6 +63,8 @@ def moe_magnitude(qref, d):
     (12, 40, 256, 128, 1, 1), (64, 512, 2048, 32, 8, 8), (6, 100, 2048, 64, 3, 6),
     # short rows: 16 and 32 lanes per row instead of 64 (two- and four-sweep units)
     (8, 7168, 2048, 64, 4, 8), (12, 768, 2048, 64, 4, 8),
+    # expert rows no wide lane count divides (1408, 2560 and 11008 columns)
+    (16, 500, 1408, 64, 4, 8), (10, 300, 2560, 64, 2, 4), (6, 200, 11008, 64, 2, 2),
 ])
 def test_matches_oracle(q, qref, E, O, I, gs, T, K):
     d = W.gen_moe(E, O, I, gs, T, K, seed=E + O)

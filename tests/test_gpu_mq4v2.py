@@ -52,6 +52,8 @@ def test_dequant_bit_exact(q, qref, O, I):
     (7000, 8192, 1), (5000, 5120, 1), (4096, 8192, 1), (2000, 7168, 1),
     # short rows: lanes per row narrowed so that a row takes two sweeps
     (3000, 1024, 1), (5000, 2048, 1), (700, 512, 1),
+    # row widths no wide lane count divides: 64 or 32 lanes with idle lanes
+    (500, 11008, 1), (300, 18944, 1), (1000, 3584, 2), (600, 2560, 1), (200, 4352, 4),
 ])
 def test_gemv_matches_oracle(q, qref, O, I, S):
     d = W.gen_mq4v2(O, I, S=S, seed=O + 7)
@@ -249,7 +251,9 @@ def _two_launch(q, w, x, signs):
                                    (77, 256, 3), (1000, 4096, 4), (33, 2304, 1), (5, 768, 6),
                                    (7000, 8192, 1), (5000, 5120, 1), (3000, 1024, 1),
                                    # two staged items per thread
-                                   (1500, 16384, 1), (2000, 7168, 1), (600, 12288, 2)])
+                                   (1500, 16384, 1), (2000, 7168, 1), (600, 12288, 2),
+                                   # odd row widths (64 or 32 lanes, idle lanes)
+                                   (500, 11008, 1), (900, 3584, 1), (300, 4352, 2)])
 def test_fused_rotation_matches_two_launches_bitwise(q, qref, O, I, S):
     # one launch == qgemv_fwht256 then qgemv_mq4v2, to the bit; and the oracle
     d = W.gen_mq4v2(O, I, S=S, seed=O + 11)
