@@ -369,15 +369,19 @@ hipError_t launch_t(const uint8_t *w, const ST *sc, const float *x, float *y, in
     return hipGetLastError();
 }
 
-// Lanes per row: the widest with the fewest idle lanes; for one vector
+// Lanes per row: pick_lpr_wide's width; for one vector
 // narrowed (not below 8) until a row takes at least three sweeps, so that
 // short rows give each wave more than one or two loads per row to keep in
 // flight.  28672 x 1024 13.8 -> 7.9 us, 14336 x 2048 9.8 -> 7.8 us, 7168 x
 // 2048 6.0 -> 5.1 us, 28672 x 512 8.0 -> 5.0 us; three-sweep rows stay
 // (16384 x 1536: six sweeps 8.85 against 8.60 us).
+// The starting width is pick_lpr_wide's (64 or 32 lanes for rows of at
+// least 32 chunks): 4096 x 11008 12.7 -> 11.3 us, 1024 x 4352 5.8 -> 5.1 us,
+// 2048 x 2176 5.8 -> 4.4 us; other shapes unchanged.  (18944 x 3584 runs
+// 9.8 or 13.6 us from one build to another of the same fp8 code, either way.)
 inline int fp8_lpr(int I, int S)
 {
-    int l = pick_lpr(I / 16);
+    int l = pick_lpr_wide(I / 16);
     if (S == 1)
         while (l > 8 && (I / 16) / l < 3) l /= 2;
     return l;
@@ -432,7 +436,7 @@ hipError_t launch_s(const uint8_t *w, const ST *sc, const float *x, float *y, in
         // several vectors: R keeps every workgroup resident at once (the rows
         // of a lane group must share a 128-row band, so R divides 128)
         static const int cand[] = {1, 2};
-        switch (pick_rows_per_group(O, pick_lpr(I / 16), QG_FP8_WPB_MULTI,
+        switch (pick_rows_per_group(O, pick_lpr_wide(I / 16), QG_FP8_WPB_MULTI,
                                     fp8_lds_bytes(S, fp8_phase_chunks(S, I) * 16), cand, 2)) {
         case 1: return launch_r<ST, S, 1>(w, sc, x, y, I, O, st);
         default: return launch_r<ST, S, 2>(w, sc, x, y, I, O, st);

@@ -81,3 +81,13 @@ def test_every_column_of_a_chunk(q, qref):
         x[0, j] = 1.0
         got = host(q.fp8b128(wt, st, x))[0]
         assert np.array_equal(got, Wd[:, j]), f"column {j}"
+
+
+@pytest.mark.parametrize("O,I,S", [(700, 11008, 1), (300, 4352, 1), (1000, 2176, 1),
+                                   (257, 11008, 3)])
+def test_odd_row_widths(q, qref, O, I, S):
+    # row widths whose chunk counts no wide lane count divides
+    d = W.gen_fp8b128(O, I, S=S, seed=O + I)
+    y = host(q.fp8b128(dev(d["w"]), dev(d["scale_inv"]), dev(d["x"])))
+    mag = magnitude(qref.fp8b128_dequant(d["w"], d["scale_inv"], O, I), d["x"])
+    assert_y_close(y, qref.fp8b128_gemv(d["w"], d["scale_inv"], d["x"], O, I), mag=mag)
