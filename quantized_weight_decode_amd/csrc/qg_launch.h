@@ -13,7 +13,8 @@ namespace qg {
 constexpr size_t LDS_BUDGET = 160 * 1024;
 
 // Lanes per row for a row of `nchunks` 16-byte lane chunks: the widest of
-// 64/32/16/8/4 lanes whose sweeps leave the fewest lanes idle.
+// 64/32/16/8/4 lanes whose sweeps leave the fewest lanes idle (the launchers
+// use it through pick_lpr_wide, for short rows only).
 inline int pick_lpr(int nchunks)
 {
     const int opts[] = {64, 32, 16, 8, 4};
@@ -27,14 +28,15 @@ inline int pick_lpr(int nchunks)
     return best;
 }
 
-// Lanes per row for the 4-bit streams: for rows of at least 32 chunks, 64 or
-// 32, whichever leaves fewer lanes idle (ties to 64); shorter rows as
-// pick_lpr.  pick_lpr alone gives rows such as 1408, 2176, 4352, 11008 or
-// 18944 columns 4 to 16 lanes, and such short segments per row stream far
-// slower (e.g. 4096 x 11008: i4g 18.8 -> 8.8 us, MQ4 19.3 -> 8.7 us; routed
-// experts of 2048 x 1408: 41.5 -> 17.6 us).  The cost: many rows of 112
-// chunks (3584 columns), which 16 lanes fit exactly, run 3-5 % slower (MQ4
-// with the fused rotation about 20 % at 18944 rows).
+// Lanes per row for the streaming GEMVs (all four formats): for rows of at
+// least 32 chunks, 64 or 32, whichever leaves fewer lanes idle (ties to 64);
+// shorter rows as pick_lpr.  pick_lpr alone gives rows such as 1408, 2176,
+// 4352, 11008 or 18944 columns 4 to 16 lanes, and such short segments per row
+// stream far slower (e.g. 4096 x 11008: i4g 18.8 -> 8.8 us, MQ4 19.3 -> 8.7
+// us, fp8 12.7 -> 11.3 us; routed experts of 2048 x 1408: 41.5 -> 17.6 us).
+// The cost: many 4-bit rows of 112 chunks (3584 columns), which 16 lanes fit
+// exactly, run 3-5 % slower (MQ4 with the fused rotation about 20 % at 18944
+// rows: fewer rows per wave make more workgroups, each rotating x).
 inline int pick_lpr_wide(int nchunks)
 {
     if (nchunks < 32) return pick_lpr(nchunks);
