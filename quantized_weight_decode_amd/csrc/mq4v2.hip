@@ -588,9 +588,12 @@ hipError_t launch_s(const uint8_t *w, const float *x, const int8_t *sg, float *y
         // Against 16 waves with R by the busiest CU, in us: 2048 x 7168 8.2
         // -> 5.9 (8 waves), 5120 x 5120 7.1 -> 6.2 and 17408 x 5120 17.4 ->
         // 13.8 (12), 7168 x 8192 8.8 -> 8.6 and 14336 x 4096 9.2 -> 8.9 (14).
+        // With the fused rotation every workgroup rotates x, so one-row tiles
+        // count only where they leave at most one workgroup per CU (18944 x
+        // 3584: 12.3 -> 10.9 us; eleven other shapes within 1 %).
         static const WaveTile cand[] = {{16, 2}, {16, 1}, {14, 2}, {14, 1},
                                         {12, 2}, {12, 1}, {8, 2},  {8, 1}};
-        switch (pick_fill_tile(O, 64 / mq4_lpr1(I), cand, 8, cu_count())) {
+        switch (pick_fill_tile(O, 64 / mq4_lpr1(I), cand, 8, cu_count(), ROT)) {
         case 0: return launch_r<HF, S, 2, ROT, 16>(w, x, sg, y, I, O, st);
         case 1: return launch_r<HF, S, 1, ROT, 16>(w, x, sg, y, I, O, st);
         case 2: return launch_r<HF, S, 2, ROT, 14>(w, x, sg, y, I, O, st);

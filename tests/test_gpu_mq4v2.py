@@ -253,7 +253,10 @@ def _two_launch(q, w, x, signs):
                                    # two staged items per thread
                                    (1500, 16384, 1), (2000, 7168, 1), (600, 12288, 2),
                                    # odd row widths (64 or 32 lanes, idle lanes)
-                                   (500, 11008, 1), (900, 3584, 1), (300, 4352, 2)])
+                                   (500, 11008, 1), (900, 3584, 1), (300, 4352, 2),
+                                   # many rows: one-row tiles kept to one
+                                   # workgroup per CU
+                                   (18944, 3584, 1)])
 def test_fused_rotation_matches_two_launches_bitwise(q, qref, O, I, S):
     # one launch == qgemv_fwht256 then qgemv_mq4v2, to the bit; and the oracle
     d = W.gen_mq4v2(O, I, S=S, seed=O + 11)
