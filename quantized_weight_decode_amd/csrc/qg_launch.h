@@ -34,9 +34,9 @@ inline int pick_lpr(int nchunks)
 // 4352, 11008 or 18944 columns 4 to 16 lanes, and such short segments per row
 // stream far slower (e.g. 4096 x 11008: i4g 18.8 -> 8.8 us, MQ4 19.3 -> 8.7
 // us, fp8 12.7 -> 11.3 us; routed experts of 2048 x 1408: 41.5 -> 17.6 us).
-// The cost: many 4-bit rows of 112 chunks (3584 columns), which 16 lanes fit
-// exactly, run 3-5 % slower (MQ4 with the fused rotation about 20 % at 18944
-// rows: fewer rows per wave make more workgroups, each rotating x).
+// Rows of 48, 80 or 112 chunks, which 16 lanes fit exactly, keep this rule
+// too: 16 lanes there gain up to 6 % on some row counts (4-bit 18944 x 3584
+// 4-5 %) and lose up to 15 % on others (i4g 37888 x 3584, 12288 x 3584).
 inline int pick_lpr_wide(int nchunks)
 {
     if (nchunks < 32) return pick_lpr(nchunks);
