@@ -826,7 +826,7 @@ def main():
                 torch.cuda.empty_cache()
 
     threads = host_threads()
-    configs = {}
+    others = {}
     for n in names:
         c = cases[n]
         rr = sorted(runs[n])
@@ -853,7 +853,7 @@ def main():
             budget = 2.5
             ent["cpu_baseline"] = {"all_threads": cpu_rate(c, threads, budget),
                                    "one_thread": cpu_rate(c, 1, budget)}
-        configs[n] = ent
+        others[n] = ent
         print(f"bench: {n}: {us_med:.3f} us/launch, "
               f"{ent['roofline']['frac']:.3f} of peak", file=sys.stderr, flush=True)
 
@@ -873,7 +873,7 @@ def main():
     if not args.no_cpu and not isinstance(hc, ReadCeiling):
         # the headline workload's oracle on all host threads over a longer sample
         out["cpu_baseline"] = cpu_rate(hc, threads, 10.0)
-    out["configs"] = configs
+    out["configs"] = others
     out["host"] = host_record(torch)
     print(json.dumps(out), flush=True)
 
